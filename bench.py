@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""µs per decode MoE block and achieved HBM GB/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp16_b1]
+
+A step is one pass of the whole decode MoE block (router scoring, top-k and
+plan, routed and shared expert gate/up + SwiGLU + down, weighted combine)
+over one batch of synthetic bf16 input, through the C ABI (moe_block).
+Default workload: one TP16 weight shard at batch 1 (d=7168, E=384, top-8,
+I=Is=128).  Other workloads: tp16_b8, tp8_b64, tiny, dense (the attention
+input projection, --batch B).
+
+Weights are random (seeded torch generator on the GPU) in R rotating full
+sets so that the bytes touched between two uses of a set exceed twice the
+256 MB Infinity Cache plus L2: each timed step reads HBM, not cache.
+Inputs are resident in HBM before the timed region.  W warm-up steps, then
+exactly K timed steps between two synchronised HIP events.
+
+Prints ONE JSON line.  Besides the headline, it carries
+  roofline:     the dominant kernel (expert gate/up) timed alone with HIP
+                events on its launch stream, algorithmic bytes / duration
+                against the 8 TB/s HBM peak;
+  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the
+                same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs per decode MoE block and achieved HBM GB/s (% of peak), batch 1–64"
+MALL_L2_BYTES = 256e6 + 32e6
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="tp16_b1",
+                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense"])
+    ap.add_argument("--batch", type=int, default=1, help="dense workload batch")
+    ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: enough to defeat caches)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kernel-steps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def rotations(bytes_per_step: float, cap_sets: int) -> int:
+    r = int(2 * MALL_L2_BYTES // max(bytes_per_step, 1.0)) + 1
+    return max(2, min(r, cap_sets))
+
+
+# ---------------------------------------------------------------- MoE block
+
+def moe_sets(cfg, R, seed, torch):
+    """R full weight sets + per-set activations, bf16 (fp32 for tiny)."""
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    sets = []
+    for r in range(R):
+        g = torch.Generator(device="cuda").manual_seed(seed * 1000003 + r)
+        rn = lambda shape, std: (torch.randn(shape, generator=g, device="cuda", dtype=dt) * std).to(dt)
+        s = dict(
+            X=rn((cfg.B, cfg.d), 1.0),
+            Wr=rn((cfg.E, cfg.d), cfg.d ** -0.5),
+            W13=rn((cfg.E, 2 * cfg.I, cfg.d), cfg.d ** -0.5),
+            W2=rn((cfg.E, cfg.d, cfg.I), cfg.I ** -0.5),
+            Ws13=rn((2 * cfg.Is, cfg.d), cfg.d ** -0.5) if cfg.Is else None,
+            Ws2=rn((cfg.d, cfg.Is), cfg.Is ** -0.5) if cfg.Is else None,
+            bias=None, bias_ld=0,
+            ids=torch.empty((cfg.B, cfg.k), dtype=torch.int32, device="cuda"),
+            out=torch.empty((cfg.B, cfg.d), dtype=dt, device="cuda"),
+        )
+        if cfg.routing == "gumbel":
+            u = torch.rand((cfg.B, cfg.E), generator=g, device="cuda").clamp_(min=1e-30)
+            s["bias"], s["bias_ld"] = (-torch.log(-torch.log(u))).float().contiguous(), cfg.E
+        elif cfg.routing == "zipf":
+            rank = torch.randperm(cfg.E, generator=g, device="cuda").float() + 1
+            s["bias"], s["bias_ld"] = (-cfg.zipf_s * torch.log(rank)).contiguous(), 0
+        sets.append(s)
+    return sets
+
+
+def run_moe(args, torch, mb, synth):
+    cfg = synth.CONFIGS[args.workload]
+    esz = 2 if cfg.dtype == "bf16" else 4
+    expert_bytes = 3 * cfg.I * cfg.d * esz
+    shared_bytes = 3 * cfg.Is * cfg.d * esz
+    est = cfg.E * cfg.d * esz + min(cfg.B * cfg.k, cfg.E) * 0.9 * expert_bytes + shared_bytes
+    full_set = (cfg.E * cfg.d + 3 * cfg.E * cfg.I * cfg.d + 3 * cfg.Is * cfg.d) * esz
+    R = args.rotate or rotations(est, cap_sets=max(2, int(60e9 // full_set)))
+    sets = moe_sets(cfg, R, args.seed, torch)
+    dt = mb.DT_BF16 if cfg.dtype == "bf16" else mb.DT_F32
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, dt, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                         I=cfg.I, Is=cfg.Is))
+
+    def step(i):
+        s = sets[i % R]
+        mb.moe_block(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, s["Ws13"], s["Ws2"],
+                     s["bias"], s["bias_ld"], topk_ids=s["ids"])
+
+    ms = timed_loop(step, args, torch)
+    # algorithmic bytes per set: every selected expert's weights once, the
+    # router and shared expert, x (and bias) read once, out written once
+    per_set = []
+    up_bytes = []
+    for s in sets:
+        n = int(torch.unique(s["ids"]).numel())
+        bias_b = 0 if s["bias"] is None else s["bias"].numel() * 4
+        b = cfg.E * cfg.d * esz + n * expert_bytes + shared_bytes + 2 * cfg.B * cfg.d * esz + bias_b
+        per_set.append((n, b))
+        up_bytes.append((n * 2 * cfg.I + 2 * cfg.Is) * cfg.d * esz + cfg.B * cfg.d * esz
+                        + (cfg.B * cfg.k * cfg.I + cfg.B * cfg.Is) * 4)
+    avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
+    avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
+    kern = {}
+    for name, kid in (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
+                      ("expert_down", mb.KERNEL_EXPERT_DOWN), ("combine", mb.KERNEL_COMBINE)):
+        kern[name] = kernel_times(step, kid, args, torch, mb)
+    durs = kern["expert_up"]
+    K2 = len(durs)
+    up_total = sum(up_bytes[i % R] for i in range(K2))
+    achieved = up_total / (sum(durs) * 1e-3)  / 1e9            # GB/s
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                kernel="expert_up_kernel", bytes_per_launch=round(up_total / K2),
+                avg_us=round(sum(durs) / K2 * 1e3, 3))
+    us = ms * 1e3
+    gbs = avg_bytes / (us * 1e-6) / 1e9
+    config = dict(workload="%s: decode MoE block, one TP weight shard, B=%d, d=%d, E=%d, top-%d, "
+                           "I=%d, Is=%d, %s routing" % (cfg.name, cfg.B, cfg.d, cfg.E, cfg.k, cfg.I,
+                                                         cfg.Is, cfg.routing),
+                  B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is, rotate=R,
+                  distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
+                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                  kernels_us={k: round(sum(v) / len(v) * 1e3, 3) for k, v in kern.items()},
+                  variant=mb.last_variant())
+    cpu = None if args.no_cpu_baseline else cpu_baseline_moe(cfg, args)
+    return us, ms, cfg.dtype, config, roof, cpu
+
+
+# ---------------------------------------------------------------- dense
+
+def run_dense(args, torch, mb, synth):
+    B, N, K = args.batch, synth.DENSE_N, synth.DENSE_K
+    wbytes = N * K * 2
+    R = args.rotate or rotations(wbytes, cap_sets=64)
+    sets = []
+    for r in range(R):
+        g = torch.Generator(device="cuda").manual_seed(args.seed * 1000003 + r)
+        sets.append(dict(X=torch.randn((B, K), generator=g, device="cuda", dtype=torch.bfloat16),
+                         W=(torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * K ** -0.5).to(torch.bfloat16),
+                         Y=torch.empty((B, N), device="cuda", dtype=torch.bfloat16)))
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K))
+
+    def step(i):
+        s = sets[i % R]
+        mb.skinny_gemm(s["X"], s["W"], s["Y"], ws)
+
+    ms = timed_loop(step, args, torch)
+    nbytes = wbytes + B * K * 2 + B * N * 2
+    durs = kernel_times(step, mb.KERNEL_SKINNY, args, torch, mb)
+    achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="skinny_kernel",
+                bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
+    us = ms * 1e3
+    config = dict(workload="dense skinny GEMM (attention input projection): Y[%d x %d] = "
+                           "X[%d x %d] . W[%d x %d]^T, bf16" % (B, N, B, K, N, K),
+                  B=B, N=N, K=K, rotate=R, algorithmic_bytes=nbytes,
+                  gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                  hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  variant=mb.last_variant())
+    cpu = None if args.no_cpu_baseline else cpu_baseline_dense(B, N, K, args)
+    return us, ms, "bf16", config, roof, cpu
+
+
+# ---------------------------------------------------------------- timing
+
+def timed_loop(step, args, torch):
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
+def kernel_times(step, kernel_id, args, torch, mb):
+    """Duration (ms) of each launch of one kernel over kernel-steps steps,
+    from HIP events the library records around that launch on its stream."""
+    n = max(1, args.kernel_steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    try:
+        for i in range(n):
+            mb.profile_events(kernel_id, evs[i][0], evs[i][1])
+            step(args.warmup + args.steps + i)
+    finally:
+        mb.profile_events(kernel_id)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline_moe(cfg, args):
+    import numpy as np
+    from moe_block_skinny_amd import synth
+    from oracle import oracle as orc
+
+    X, Wr = synth.x(cfg, args.seed), synth.router_w(cfg, args.seed)
+    bias, ld = synth.bias(cfg, args.seed)
+    _, ids, _, _ = orc.route(X, Wr, cfg.k, bias, ld)
+    touched = set(ids.reshape(-1).tolist())
+    W13 = [synth.expert_w13(cfg, args.seed, e) if e in touched else None for e in range(cfg.E)]
+    W2 = [synth.expert_w2(cfg, args.seed, e) if e in touched else None for e in range(cfg.E)]
+    Ws13, Ws2 = synth.shared_w13(cfg, args.seed), synth.shared_w2(cfg, args.seed)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.moe_block(X, Wr, cfg.k, W13, W2, Ws13, Ws2, bias, ld)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
+                sample="%d blocks of the %s workload (seed %d, %d distinct experts), fp64 C oracle, "
+                       "one thread, %.1f s" % (n, cfg.name, args.seed, len(touched), el),
+                cpu=platform.processor() or platform.machine(), host_cpus=os.cpu_count())
+
+
+def cpu_baseline_dense(B, N, K, args):
+    from moe_block_skinny_amd import synth
+    from oracle import oracle as orc
+
+    X, W = synth.dense_x(B), synth.dense_w()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.skinny_gemm(X, W)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
+                sample="%d skinny GEMMs at B=%d, fp64 C oracle, one thread, %.1f s" % (n, B, el),
+                host_cpus=os.cpu_count())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the decode MoE block here is one GPU's "
+              "tensor-parallel weight shard and this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from moe_block_skinny_amd import binding as mb
+    from moe_block_skinny_amd import synth
+
+    torch.cuda.set_device(0)
+    if args.workload == "dense":
+        us, ms, dtype, config, roof, cpu = run_dense(args, torch, mb, synth)
+    else:
+        us, ms, dtype, config, roof, cpu = run_moe(args, torch, mb, synth)
+    line = dict(metric=METRIC, value=round(us, 3), unit="µs", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(ms, 6), higher_is_better=False,
+                scaling="weak", vs_baseline=None, dtype=dtype, data="synthetic", config=config,
+                roofline=roof, cpu_baseline=cpu)
+    print(json.dumps(line, ensure_ascii=False), flush=True)
+
+
+if __name__ == "__main__":
+    main()

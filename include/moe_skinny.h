@@ -1,0 +1,220 @@
+/*
+ * moe_skinny.h -- C ABI of the MI355X (gfx950) decode-step MoE block.
+ *
+ * The block is the mixture-of-experts layer of a large MoE transformer at
+ * decode time (batch 1-64), on one GPU's tensor-parallel weight shard:
+ * router scoring and top-k selection, the token->expert plan, skinny
+ * gate/up/down expert products with SwiGLU, a shared expert and the weighted
+ * combine; plus the dense skinny product used for the attention input
+ * projection.
+ *
+ * Sources (web pages on the Kimi K3 specialised decode path):
+ *   [WRITEUP] "vLLM 如何用智能体辅助优化 Kimi K3 解码性能" (Chinese translation
+ *     of the vLLM write-up): part 1 §1 (batch-shaped kernels: a small-matrix
+ *     kernel at batch 1-2, split-K above), part 1 §3 (router scores and the
+ *     latent projection per rank, routed experts, a shared expert on its own
+ *     stream), part 1 §4 (small-batch decode is bound by weight reads),
+ *     part 2 §1 (the switch into and out of the specialised path must be
+ *     traceable at run time), part 2 §2 (scope: decode batch up to 64 on the
+ *     tested parallel settings; other work stays on the standard path),
+ *     part 2 §3 (tests must exercise the changed path).
+ *   [AREX] "vLLM 宣布 Kimi K3 在 GB300 NVL72 上实现 batch 1 解码 842
+ *     tokens/s": sections "每层从 23 个内核减到 13 个" (the same four changes)
+ *     and "DeepSeek-V4.1-Flash 跟进同一模式" (opt-in path, prefill and mixed
+ *     batches fall back to the default implementation).
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, contiguous, row-major.  The library never allocates, frees or
+ *     synchronises; it enqueues on `stream` (a hipStream_t, NULL = default
+ *     stream) and returns.  Buffers must stay alive until the stream has run
+ *     the work.
+ *   - dtype: MOE_DT_BF16 (bf16 storage) or MOE_DT_F32.  Activations and
+ *     weights share the dtype; all accumulation is fp32.
+ *   - Weight layouts ([out][in], the in-dimension contiguous):
+ *       Wr   [E][d]          router
+ *       W13  [E][2I][d]      per expert: gate rows 0..I-1, then up rows I..2I-1
+ *       W2   [E][d][I]       per expert down projection
+ *       Ws13 [2Is][d], Ws2 [d][Is]   shared expert (same split)
+ *       W    [N][K]          dense skinny product
+ *   - Workspace: `ws` is caller-owned device memory of at least
+ *     moe_workspace_bytes(...) bytes.  It holds split-K partial sums,
+ *     router logits, the SwiGLU intermediate and completion counters.  It must
+ *     be zero-filled once before its first use (moe_workspace_init); every
+ *     call leaves its counter words at zero again.  Two calls that run
+ *     concurrently must not share a workspace.
+ *   - Errors: every call validates all arguments on the host BEFORE any HIP
+ *     call and returns MOE_EINVAL (null or misaligned pointer, bad dimension,
+ *     k > E, unknown dtype), MOE_EUNSUPPORTED (outside the specialised
+ *     path's scope: B outside 1..64, E > 512, k > 16, sizes not multiples of
+ *     the vector width, ...; the caller should use its standard path),
+ *     MOE_EWORKSPACE (ws too small) or MOE_EHIP (a launch failed).  Nothing
+ *     is enqueued unless MOE_OK is returned; no call ever silently switches
+ *     to another path.  moe_last_error() gives the detail.
+ *   - Kernel shape follows the batch (WRITEUP part 1 §1): "gemv" at B <= 2,
+ *     "splitk" at B <= 8, "mfma" above.  moe_set_variant() (or the
+ *     MOE_FORCE_VARIANT environment variable: gemv, splitk, mfma) forces one
+ *     shape wherever it supports the sizes, and fails the call with
+ *     MOE_EUNSUPPORTED where it does not.  MOE_TRACE=1 prints the chosen
+ *     shape of every call to stderr; moe_last_variant() returns it
+ *     (thread-local).
+ */
+#ifndef MOE_SKINNY_H
+#define MOE_SKINNY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status_t;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_VARIANT_AUTO = 0,
+  MOE_VARIANT_GEMV = 1,
+  MOE_VARIANT_SPLITK = 2,
+  MOE_VARIANT_MFMA = 3
+} moe_variant_t;
+
+typedef enum {
+  MOE_OP_SKINNY_GEMM = 0,
+  MOE_OP_ROUTE = 1,
+  MOE_OP_EXPERT_FFN = 2,
+  MOE_OP_BLOCK = 3
+} moe_op_t;
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status_t s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Kernel shape chosen by the last successful call on this thread. */
+const char* moe_last_variant(void);
+
+/* Force a kernel shape for every later call in the process
+ * (MOE_VARIANT_AUTO restores the batch-based choice).  Returns the previous
+ * setting. */
+int moe_set_variant(int variant);
+
+/* int32 words of a routing plan for B tokens, top-k of E experts:
+ * 2 + 2*min(E, B*k) + B*k.  Layout, with maxa = min(E, B*k):
+ *   plan[0]                    n, the number of distinct experts selected
+ *   plan[1 .. 1+maxa)          those experts in ascending id (unused: -1)
+ *   plan[1+maxa .. 2+2*maxa)   slot offsets per listed expert, n+1 used
+ *                              (unused entries: B*k)
+ *   plan[2+2*maxa .. +B*k)     slots s = t*k + j (token t's j-th choice),
+ *                              grouped by expert, tokens ascending. */
+int moe_plan_words(int B, int k, int E);
+
+/* Bytes of workspace a call needs.  op: moe_op_t.  Unused sizes may be 0:
+ *   MOE_OP_SKINNY_GEMM: dtype, B, N, K
+ *   MOE_OP_ROUTE:       dtype, B, d, E, k
+ *   MOE_OP_EXPERT_FFN:  dtype, B, d, E, k, I, Is
+ *   MOE_OP_BLOCK:       dtype, B, d, E, k, I, Is */
+size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I, int Is, int N,
+                           int K);
+
+/* Kernels, for moe_profile_events. */
+typedef enum {
+  MOE_KERNEL_ROUTE = 0,        /* router logits + top-k + plan */
+  MOE_KERNEL_EXPERT_UP = 1,    /* expert gate/up + SwiGLU */
+  MOE_KERNEL_EXPERT_DOWN = 2,  /* expert down projection */
+  MOE_KERNEL_COMBINE = 3,      /* weighted combine */
+  MOE_KERNEL_SKINNY = 4        /* dense skinny product */
+} moe_kernel_t;
+
+/* Profiling hook (for timing one kernel with HIP events on the stream it is
+ * launched on): while armed, every launch of `kernel` is bracketed by
+ * hipEventRecord(start_event) and hipEventRecord(stop_event) on the launch
+ * stream.  Both NULL disarms.  Process-wide; not for concurrent use.
+ * start_event / stop_event are hipEvent_t handles owned by the caller.
+ * Returns MOE_EINVAL for an unknown kernel or only one NULL event. */
+moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event);
+
+/* Zero-fill a workspace (with a kernel, so it may be captured in a graph). */
+moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Dense skinny product Y[b][n] = sum_c X[b][c] * W[n][c]   (WRITEUP part 1
+ * §1, the attention input projection at decode batch: small-matrix kernel at
+ * batch 1-2, split-K at larger batch).
+ *   X [B][K] dtype, W [N][K] dtype, Y [B][N] of y_dtype (dtype or
+ *   MOE_DT_F32).  1 <= B <= 64; K a multiple of 8 (bf16) or 4 (fp32), and of
+ *   32 for the mfma shape (bf16 only).  Output rounded to nearest-even when
+ *   y_dtype is bf16. */
+moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
+                         int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Router (WRITEUP part 1 §3; selection and weights are the standard top-k
+ * softmax the block's workload definitions name):
+ *   logits[t][e] = sum_c X[t][c] * Wr[e][c] + bias(t, e), accumulated in fp32;
+ *   the k experts with the largest fp32 logits (on an exact tie the lower
+ *   expert index wins), in ascending expert id, with weights
+ *   w_j = exp(l_j - max) / sum_{i in top-k} exp(l_i - max)
+ *   (= softmax over all E renormalised over the top-k; no extra scale);
+ *   and the routing plan (moe_plan_words layout).
+ *   X [B][d], Wr [E][d]; bias: NULL, [E] (bias_ld = 0, added to every token)
+ *   or [B][E] (bias_ld = E), fp32.  Outputs: topk_ids int32 [B][k],
+ *   topk_w fp32 [B][k], plan int32 [moe_plan_words(B, k, E)], and, when
+ *   logits_out is not NULL, the fp32 logits [B][E].
+ *   Scope: 1 <= B <= 64, 1 <= k <= min(E, 16), E <= 512, d a multiple of 32
+ *   (bf16) or 4 (fp32, B <= 8).  Inputs must be finite. */
+moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, const void* Wr,
+                       const float* bias, int bias_ld, int32_t* topk_ids, float* topk_w,
+                       int32_t* plan, float* logits_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed and shared experts (WRITEUP part 1 §3; SwiGLU expert FFN):
+ *   for every slot s = t*k + j of the plan, with e its expert:
+ *     h = silu(X[t] . W13[e][0:I]^T) * (X[t] . W13[e][I:2I]^T),
+ *     silu(z) = z / (1 + exp(-z)),  h kept in fp32,
+ *     Yslot[t][j] = h . W2[e]^T                          (fp32 [d])
+ *   and, when Ws13 is not NULL, the shared expert for every token t:
+ *     Yslot[t][k] = the same FFN with Ws13 / Ws2 (Is).   Without a shared
+ *   expert Yslot[t][k] is left untouched.
+ *   Each selected expert's weights are read once however many tokens chose
+ *   it; unselected experts are never read.  plan comes from moe_route (it
+ *   must be complete before this call runs: same stream or synchronised).
+ *   Yslot fp32 [B][k+1][d].  Scope as moe_route, plus I (and Is) multiples
+ *   of 32 up to 512 (bf16; fp32: multiples of 4 up to 256, B <= 8). */
+moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const void* X,
+                            const int32_t* plan, const void* W13, const void* W2, int Is,
+                            const void* Ws13, const void* Ws2, float* Yslot, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Weighted combine:
+ *   out[t] = sum_{j ascending} topk_w[t][j] * Yslot[t][j] + (has_shared ?
+ *   Yslot[t][k] : 0), accumulated in fp32 in that order, stored as dtype
+ *   (bf16: round to nearest-even).  Yslot fp32 [B][k+1][d], topk_w fp32
+ *   [B][k], out [B][d].  No workspace. */
+moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
+                         int has_shared, void* out, void* stream);
+
+/* The whole block: moe_route, then moe_expert_ffn, then moe_combine, with
+ * every intermediate in ws.  Same scope and results as the three calls;
+ * topk_ids / topk_w / plan outputs are optional (NULL: kept in ws). */
+moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                       const void* Wr, const float* bias, int bias_ld, const void* W13,
+                       const void* W2, const void* Ws13, const void* Ws2, void* out,
+                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_SKINNY_H */

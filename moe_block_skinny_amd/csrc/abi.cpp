@@ -1,0 +1,544 @@
+// abi.cpp -- the C ABI declared in include/moe_skinny.h: host-side argument
+// validation (complete before any HIP call), batch-shaped kernel choice,
+// workspace layout, tracing of the chosen path, and the launches.
+//
+// Sources: [WRITEUP] "vLLM 如何用智能体辅助优化 Kimi K3 解码性能", part 1 §1
+// (kernel shape by batch size), part 2 §1 (the choice of path must be
+// traceable at run time), part 2 §2 (a stated scope, outside which the
+// standard path is used), part 2 §3 (tests must reach the changed path:
+// hence the forced-shape switch and the per-call trace).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.hpp"
+#include "moe_skinny.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local char g_variant[256] = "";
+std::atomic<int> g_force{-1};  // -1: not yet read from the environment
+
+constexpr int kMaxB = 64, kMaxE = 512, kMaxK = 16, kMaxI = 512;
+constexpr size_t kAlign = 256;
+
+// Profiling hook: events bracketing every launch of one kernel.
+struct ProfileHook {
+  int kernel = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+} g_prof;
+
+struct ProfileScope {
+  bool on;
+  hipStream_t st;
+  ProfileScope(int kernel, hipStream_t s) : on(g_prof.kernel == kernel), st(s) {
+    if (on) (void)hipEventRecord(g_prof.start, st);
+  }
+  ~ProfileScope() {
+    if (on) (void)hipEventRecord(g_prof.stop, st);
+  }
+};
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int forced() {
+  int f = g_force.load();
+  if (f < 0) {
+    f = MOE_VARIANT_AUTO;
+    const char* e = getenv("MOE_FORCE_VARIANT");
+    if (e) {
+      if (!strcmp(e, "gemv")) f = MOE_VARIANT_GEMV;
+      else if (!strcmp(e, "splitk")) f = MOE_VARIANT_SPLITK;
+      else if (!strcmp(e, "mfma")) f = MOE_VARIANT_MFMA;
+    }
+    int expect = -1;
+    g_force.compare_exchange_strong(expect, f);
+    f = g_force.load();
+  }
+  return f;
+}
+
+bool trace_on() {
+  static const int on = [] {
+    const char* e = getenv("MOE_TRACE");
+    return (e && *e && strcmp(e, "0")) ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+void record(const char* op, int B, const char* desc) {
+  snprintf(g_variant, sizeof g_variant, "%s B=%d %s", op, B, desc);
+  if (trace_on()) fprintf(stderr, "[moe_skinny] %s\n", g_variant);
+}
+
+bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ---- kernel shape of the skinny product --------------------------------------
+
+moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
+  const int f = forced();
+  int v = f;
+  if (f == MOE_VARIANT_AUTO) v = B <= 2 ? VAR_GEMV : (B <= 8 ? VAR_SPLITK : VAR_MFMA);
+  if (v == VAR_GEMV && B > 2) return fail(MOE_EUNSUPPORTED, "gemv shape supports B <= 2 (B=%d)", B);
+  if (v == VAR_SPLITK && B > 8) return fail(MOE_EUNSUPPORTED, "splitk shape supports B <= 8 (B=%d)", B);
+  if (v == VAR_MFMA && !bf16) return fail(MOE_EUNSUPPORTED, "mfma shape needs bf16 (fp32 supports B <= 8)");
+  if (v == VAR_MFMA && K % 32) return fail(MOE_EUNSUPPORTED, "mfma shape needs K %% 32 == 0 (K=%d)", K);
+  *variant = v;
+  return MOE_OK;
+}
+
+// Largest split count / row-block count any feasible shape can use.
+void skinny_ws_dims(int bf16, int B, int N, int K, int* smax, int* nrbmax) {
+  *smax = 1;
+  *nrbmax = 1;
+  for (int v = VAR_GEMV; v <= VAR_MFMA; ++v) {
+    if (v == VAR_MFMA && (!bf16 || K % 32)) continue;
+    const int s = skinny_default_splits(v, bf16, B, N, K);
+    const int rows = skinny_rows_per_block(v, bf16, B);
+    const int nrb = (N + rows - 1) / rows;
+    if (s > *smax) *smax = s;
+    if (nrb > *nrbmax) *nrbmax = nrb;
+  }
+}
+
+struct SkinnyWs {
+  size_t partial, rb_counter, logits, done, total;
+};
+
+SkinnyWs skinny_ws(int bf16, int B, int N, int K, bool router) {
+  int smax, nrbmax;
+  skinny_ws_dims(bf16, B, N, K, &smax, &nrbmax);
+  SkinnyWs w;
+  size_t o = 0;
+  w.partial = o;
+  o = up(o + (size_t)smax * B * N * 4);
+  w.rb_counter = o;
+  o = up(o + (size_t)nrbmax * 4);
+  w.logits = o;
+  if (router) o = up(o + (size_t)B * N * 4);
+  w.done = o;
+  if (router) o = up(o + 4);
+  w.total = o;
+  return w;
+}
+
+struct ExpertWs {
+  size_t h, total;
+  int hld;
+};
+
+ExpertWs expert_ws(int B, int k, int I, int Is) {
+  ExpertWs w;
+  w.hld = I > Is ? I : Is;
+  w.h = 0;
+  w.total = up((size_t)(B * k + B) * w.hld * 4);
+  return w;
+}
+
+struct BlockWs {
+  SkinnyWs route;
+  ExpertWs ffn;
+  size_t route_off, ffn_off, yslot, ids, w, plan, total;
+};
+
+BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
+  BlockWs b;
+  b.route = skinny_ws(bf16, B, E, d, true);
+  b.ffn = expert_ws(B, k, I, Is);
+  size_t o = 0;
+  b.route_off = o;
+  o = up(o + b.route.total);
+  b.ffn_off = o;
+  o = up(o + b.ffn.total);
+  b.yslot = o;
+  o = up(o + (size_t)B * (k + 1) * d * 4);
+  b.ids = o;
+  o = up(o + (size_t)B * k * 4);
+  b.w = o;
+  o = up(o + (size_t)B * k * 4);
+  b.plan = o;
+  o = up(o + (size_t)moe_plan_words(B, k, E) * 4);
+  b.total = o;
+  return b;
+}
+
+// ---- validation -----------------------------------------------------------
+
+moe_status_t check_dtype(int dt) {
+  if (dt != MOE_DT_F32 && dt != MOE_DT_BF16) return fail(MOE_EINVAL, "unknown dtype %d", dt);
+  return MOE_OK;
+}
+
+moe_status_t check_route_dims(int dt, int B, int d, int E, int k) {
+  moe_status_t s = check_dtype(dt);
+  if (s) return s;
+  if (B <= 0 || d <= 0 || E <= 0 || k <= 0) return fail(MOE_EINVAL, "non-positive size");
+  if (k > E) return fail(MOE_EINVAL, "k=%d > E=%d", k, E);
+  if (B > kMaxB) return fail(MOE_EUNSUPPORTED, "B=%d outside the decode range 1..%d", B, kMaxB);
+  if (E > kMaxE) return fail(MOE_EUNSUPPORTED, "E=%d > %d", E, kMaxE);
+  if (k > kMaxK) return fail(MOE_EUNSUPPORTED, "k=%d > %d", k, kMaxK);
+  if (dt == MOE_DT_BF16 && d % 32) return fail(MOE_EUNSUPPORTED, "d=%d not a multiple of 32", d);
+  if (dt == MOE_DT_F32 && d % 4) return fail(MOE_EUNSUPPORTED, "d=%d not a multiple of 4", d);
+  if (dt == MOE_DT_F32 && B > 8) return fail(MOE_EUNSUPPORTED, "fp32 supports B <= 8 (B=%d)", B);
+  return MOE_OK;
+}
+
+moe_status_t check_inter(int dt, int I, const char* name) {
+  if (I <= 0) return fail(MOE_EINVAL, "%s=%d", name, I);
+  if (dt == MOE_DT_BF16 && (I % 32 || I > kMaxI))
+    return fail(MOE_EUNSUPPORTED, "%s=%d must be a multiple of 32 up to %d", name, I, kMaxI);
+  if (dt == MOE_DT_F32 && (I % 4 || I > 256))
+    return fail(MOE_EUNSUPPORTED, "%s=%d must be a multiple of 4 up to 256 (fp32)", name, I);
+  return MOE_OK;
+}
+
+moe_status_t expert_force(int dt, int B, int* force) {
+  const int f = forced();
+  if (f == MOE_VARIANT_MFMA && dt != MOE_DT_BF16)
+    return fail(MOE_EUNSUPPORTED, "mfma shape needs bf16");
+  if ((f == MOE_VARIANT_GEMV || f == MOE_VARIANT_SPLITK) && B > 8)
+    return fail(MOE_EUNSUPPORTED, "vector expert shape supports up to 8 tokens per expert (B=%d)", B);
+  *force = f == MOE_VARIANT_MFMA ? VAR_MFMA : (f == MOE_VARIANT_AUTO ? VAR_AUTO : VAR_GEMV);
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---- launch helpers (arguments already validated) ---------------------------
+
+moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
+                       const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
+                       float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl) {
+  const int bf16 = dt == MOE_DT_BF16;
+  int v;
+  moe_status_t s = resolve_skinny(bf16, B, d, &v);
+  if (s) return s;
+  const SkinnyWs L = skinny_ws(bf16, B, E, d, true);
+  SkinnyLaunch a = {};
+  a.bf16 = bf16;
+  a.X = X;
+  a.W = Wr;
+  a.M = B;
+  a.N = E;
+  a.K = d;
+  a.variant = v;
+  a.S = skinny_default_splits(v, bf16, B, E, d);
+  a.partial = reinterpret_cast<float*>(ws + L.partial);
+  a.rb_counter = reinterpret_cast<uint32_t*>(ws + L.rb_counter);
+  a.router = 1;
+  a.bias = bias;
+  a.bias_ld = bias_ld;
+  a.logits = reinterpret_cast<float*>(ws + L.logits);
+  a.logits_out = logits_out;
+  a.done_counter = reinterpret_cast<uint32_t*>(ws + L.done);
+  a.k = k;
+  a.topk_ids = ids;
+  a.topk_w = w;
+  a.plan = plan;
+  ProfileScope prof(MOE_KERNEL_ROUTE, st);
+  return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
+}
+
+moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, const int32_t* plan,
+                     const void* W13, const void* W2, int Is, const void* Ws13, const void* Ws2,
+                     float* Yslot, char* ws, int force, hipStream_t st, char* desc, size_t dl) {
+  const ExpertWs L = expert_ws(B, k, I, Ws13 ? Is : 0);
+  ExpertLaunch a = {};
+  a.bf16 = dt == MOE_DT_BF16;
+  a.B = B;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.I = I;
+  a.Is = Ws13 ? Is : 0;
+  a.X = X;
+  a.plan = plan;
+  a.W13 = W13;
+  a.W2 = W2;
+  a.Ws13 = Ws13;
+  a.Ws2 = Ws2;
+  a.h = reinterpret_cast<float*>(ws + L.h);
+  a.hld = L.hld;
+  a.Yslot = Yslot;
+  a.force = force;
+  char d1[128] = "", d2[128] = "";
+  moe_status_t s;
+  {
+    ProfileScope prof(MOE_KERNEL_EXPERT_UP, st);
+    s = hip_status(launch_expert_up(a, st, d1, sizeof d1), "expert gate/up launch");
+  }
+  if (s) return s;
+  {
+    ProfileScope prof(MOE_KERNEL_EXPERT_DOWN, st);
+    s = hip_status(launch_expert_down(a, st, d2, sizeof d2), "expert down launch");
+  }
+  if (desc) snprintf(desc, dl, "%s; %s", d1, d2);
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported by the specialised decode path";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event) {
+  g_err[0] = 0;
+  if (!start_event && !stop_event) {
+    g_prof.kernel = -1;
+    g_prof.start = g_prof.stop = nullptr;
+    return MOE_OK;
+  }
+  if (kernel < MOE_KERNEL_ROUTE || kernel > MOE_KERNEL_SKINNY) return fail(MOE_EINVAL, "unknown kernel %d", kernel);
+  if (!start_event || !stop_event) return fail(MOE_EINVAL, "both events or neither");
+  g_prof.kernel = kernel;
+  g_prof.start = reinterpret_cast<hipEvent_t>(start_event);
+  g_prof.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
+const char* moe_last_variant(void) { return g_variant; }
+
+int moe_set_variant(int variant) {
+  const int prev = forced();
+  if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_MFMA) return prev;
+  g_force.store(variant);
+  return prev;
+}
+
+int moe_plan_words(int B, int k, int E) {
+  const int maxa = B * k < E ? B * k : E;
+  return 2 + 2 * maxa + B * k;
+}
+
+size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I, int Is, int N, int K) {
+  const int bf16 = dtype == MOE_DT_BF16;
+  if (B <= 0) return 0;
+  switch (op) {
+    case MOE_OP_SKINNY_GEMM:
+      if (N <= 0 || K <= 0) return 0;
+      return skinny_ws(bf16, B, N, K, false).total;
+    case MOE_OP_ROUTE:
+      if (E <= 0 || d <= 0) return 0;
+      return skinny_ws(bf16, B, E, d, true).total;
+    case MOE_OP_EXPERT_FFN:
+      if (k <= 0) return 0;
+      return expert_ws(B, k, I, Is).total;
+    case MOE_OP_BLOCK:
+      if (E <= 0 || d <= 0 || k <= 0) return 0;
+      return block_ws(bf16, B, d, E, k, I, Is).total;
+  }
+  return 0;
+}
+
+moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  return hip_status(launch_fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream)),
+                    "workspace fill");
+}
+
+moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
+                         int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_dtype(dtype);
+  if (s) return s;
+  if (y_dtype != dtype && y_dtype != MOE_DT_F32) return fail(MOE_EINVAL, "y_dtype %d", y_dtype);
+  if (B <= 0 || N <= 0 || K <= 0) return fail(MOE_EINVAL, "non-positive size");
+  if (!aligned(X) || !aligned(W) || !aligned(Y)) return fail(MOE_EINVAL, "X, W or Y null or not 16-byte aligned");
+  if (B > kMaxB) return fail(MOE_EUNSUPPORTED, "B=%d outside 1..%d", B, kMaxB);
+  if (K % (dtype == MOE_DT_BF16 ? 8 : 4)) return fail(MOE_EUNSUPPORTED, "K=%d not a multiple of the vector width", K);
+  const int bf16 = dtype == MOE_DT_BF16;
+  int v;
+  s = resolve_skinny(bf16, B, K, &v);
+  if (s) return s;
+  const SkinnyWs L = skinny_ws(bf16, B, N, K, false);
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  SkinnyLaunch a = {};
+  a.bf16 = bf16;
+  a.X = X;
+  a.W = W;
+  a.M = B;
+  a.N = N;
+  a.K = K;
+  a.variant = v;
+  a.S = skinny_default_splits(v, bf16, B, N, K);
+  char* w = static_cast<char*>(ws);
+  a.partial = reinterpret_cast<float*>(w + L.partial);
+  a.rb_counter = reinterpret_cast<uint32_t*>(w + L.rb_counter);
+  a.Y = Y;
+  a.y_bf16 = y_dtype == MOE_DT_BF16;
+  char desc[160];
+  {
+    ProfileScope prof(MOE_KERNEL_SKINNY, reinterpret_cast<hipStream_t>(stream));
+    s = hip_status(launch_skinny(a, reinterpret_cast<hipStream_t>(stream), desc, sizeof desc),
+                   "skinny_gemm launch");
+  }
+  if (!s) record("skinny_gemm", B, desc);
+  return s;
+}
+
+moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, const void* Wr,
+                       const float* bias, int bias_ld, int32_t* topk_ids, float* topk_w,
+                       int32_t* plan, float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_route_dims(dtype, B, d, E, k);
+  if (s) return s;
+  if (!aligned(X) || !aligned(Wr)) return fail(MOE_EINVAL, "X or Wr null or misaligned");
+  if (!aligned(topk_ids) || !aligned(topk_w) || !aligned(plan))
+    return fail(MOE_EINVAL, "topk_ids, topk_w or plan null or misaligned");
+  if (bias && !aligned(bias)) return fail(MOE_EINVAL, "bias misaligned");
+  if (bias && bias_ld != 0 && bias_ld != E) return fail(MOE_EINVAL, "bias_ld must be 0 or E");
+  if (logits_out && !aligned(logits_out)) return fail(MOE_EINVAL, "logits_out misaligned");
+  const int bf16 = dtype == MOE_DT_BF16;
+  int v;
+  s = resolve_skinny(bf16, B, d, &v);
+  if (s) return s;
+  const size_t need = skinny_ws(bf16, B, E, d, true).total;
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  char desc[160];
+  s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, topk_ids, topk_w, plan, logits_out,
+                static_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream), desc, sizeof desc);
+  if (!s) record("moe_route", B, desc);
+  return s;
+}
+
+moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const void* X,
+                            const int32_t* plan, const void* W13, const void* W2, int Is,
+                            const void* Ws13, const void* Ws2, float* Yslot, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_route_dims(dtype, B, d, E, k);
+  if (s) return s;
+  if ((s = check_inter(dtype, I, "I"))) return s;
+  if (Ws13 && (s = check_inter(dtype, Is, "Is"))) return s;
+  if (!aligned(X) || !aligned(plan) || !aligned(W13) || !aligned(W2) || !aligned(Yslot))
+    return fail(MOE_EINVAL, "X, plan, W13, W2 or Yslot null or misaligned");
+  if (Ws13 && (!aligned(Ws13) || !aligned(Ws2))) return fail(MOE_EINVAL, "Ws13 or Ws2 null or misaligned");
+  int force;
+  if ((s = expert_force(dtype, B, &force))) return s;
+  const size_t need = expert_ws(B, k, I, Ws13 ? Is : 0).total;
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  char desc[300];
+  s = run_ffn(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, Yslot, static_cast<char*>(ws),
+              force, reinterpret_cast<hipStream_t>(stream), desc, sizeof desc);
+  if (!s) record("moe_expert_ffn", B, desc);
+  return s;
+}
+
+moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
+                         int has_shared, void* out, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_dtype(dtype);
+  if (s) return s;
+  if (B <= 0 || d <= 0 || k <= 0) return fail(MOE_EINVAL, "non-positive size");
+  if (B > kMaxB) return fail(MOE_EUNSUPPORTED, "B=%d outside 1..%d", B, kMaxB);
+  if (k > kMaxK) return fail(MOE_EUNSUPPORTED, "k=%d > %d", k, kMaxK);
+  if (!aligned(Yslot) || !aligned(topk_w) || !aligned(out)) return fail(MOE_EINVAL, "Yslot, topk_w or out null or misaligned");
+  CombineLaunch a = {};
+  a.out_bf16 = dtype == MOE_DT_BF16;
+  a.B = B;
+  a.d = d;
+  a.k = k;
+  a.has_shared = has_shared ? 1 : 0;
+  a.Yslot = Yslot;
+  a.topk_w = topk_w;
+  a.out = out;
+  {
+    ProfileScope prof(MOE_KERNEL_COMBINE, reinterpret_cast<hipStream_t>(stream));
+    s = hip_status(launch_combine(a, reinterpret_cast<hipStream_t>(stream)), "moe_combine launch");
+  }
+  if (!s) record("moe_combine", B, "elementwise");
+  return s;
+}
+
+moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                       const void* Wr, const float* bias, int bias_ld, const void* W13,
+                       const void* W2, const void* Ws13, const void* Ws2, void* out,
+                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_route_dims(dtype, B, d, E, k);
+  if (s) return s;
+  if ((s = check_inter(dtype, I, "I"))) return s;
+  if (Ws13 && (s = check_inter(dtype, Is, "Is"))) return s;
+  if (!aligned(X) || !aligned(Wr) || !aligned(W13) || !aligned(W2) || !aligned(out))
+    return fail(MOE_EINVAL, "X, Wr, W13, W2 or out null or misaligned");
+  if (Ws13 && (!aligned(Ws13) || !aligned(Ws2))) return fail(MOE_EINVAL, "Ws13 or Ws2 null or misaligned");
+  if (bias && !aligned(bias)) return fail(MOE_EINVAL, "bias misaligned");
+  if (bias && bias_ld != 0 && bias_ld != E) return fail(MOE_EINVAL, "bias_ld must be 0 or E");
+  if ((topk_ids && !aligned(topk_ids)) || (topk_w && !aligned(topk_w)))
+    return fail(MOE_EINVAL, "topk_ids or topk_w misaligned");
+  const int bf16 = dtype == MOE_DT_BF16;
+  int v, force;
+  if ((s = resolve_skinny(bf16, B, d, &v))) return s;
+  if ((s = expert_force(dtype, B, &force))) return s;
+  const BlockWs L = block_ws(bf16, B, d, E, k, I, Ws13 ? Is : 0);
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(w + L.ids);
+  float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.w);
+  int32_t* plan = reinterpret_cast<int32_t*>(w + L.plan);
+  float* yslot = reinterpret_cast<float*>(w + L.yslot);
+  char d1[160] = "", d2[300] = "";
+  if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
+                     st, d1, sizeof d1)))
+    return s;
+  if ((s = run_ffn(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, yslot, w + L.ffn_off, force,
+                   st, d2, sizeof d2)))
+    return s;
+  CombineLaunch c = {};
+  c.out_bf16 = bf16;
+  c.B = B;
+  c.d = d;
+  c.k = k;
+  c.has_shared = Ws13 ? 1 : 0;
+  c.Yslot = yslot;
+  c.topk_w = tw;
+  c.out = out;
+  {
+    ProfileScope prof(MOE_KERNEL_COMBINE, st);
+    s = hip_status(launch_combine(c, st), "combine launch");
+  }
+  if (s) return s;
+  char desc[480];
+  snprintf(desc, sizeof desc, "route[%s] ffn[%s] combine", d1, d2);
+  record("moe_block", B, desc);
+  return MOE_OK;
+}
+
+}  // extern "C"

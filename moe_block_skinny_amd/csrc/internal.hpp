@@ -1,0 +1,77 @@
+// internal.hpp -- host-side launch interface between the C-ABI layer
+// (abi.cpp) and the kernel translation units.  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Variant { VAR_AUTO = 0, VAR_GEMV = 1, VAR_SPLITK = 2, VAR_MFMA = 3 };
+
+// Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
+// (Y, y_bf16) or, in router mode, turned into logits + bias and then top-k
+// weights and the routing plan by the last workgroup to finish.
+struct SkinnyLaunch {
+  int bf16;                 // element type of X and W
+  const void* X;
+  const void* W;
+  int M, N, K;
+  int variant;              // VAR_GEMV / VAR_SPLITK / VAR_MFMA (resolved)
+  int S;                    // K splits (1 = none)
+  float* partial;           // [S][M][N] fp32 when S > 1
+  uint32_t* rb_counter;     // one per row block when S > 1 (zero on entry)
+  // store mode
+  void* Y;
+  int y_bf16;
+  // router mode (router != 0)
+  int router;
+  const float* bias;
+  int bias_ld;
+  float* logits;            // [M][N] workspace
+  float* logits_out;        // optional copy [M][N]
+  uint32_t* done_counter;   // zero on entry
+  int k;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* plan;
+};
+
+// Expert FFN stage over the routing plan.  h is fp32 [B*k + B][Imax]:
+// routed slot s = t*k + j at row s, shared-expert token t at row B*k + t.
+struct ExpertLaunch {
+  int bf16;
+  int B, d, E, k, I, Is;
+  const void* X;            // [B][d]
+  const int32_t* plan;
+  const void* W13;          // [E][2I][d]
+  const void* W2;           // [E][d][I]
+  const void* Ws13;         // [2Is][d] or null
+  const void* Ws2;          // [d][Is]
+  float* h;                 // workspace
+  int hld;                  // row stride of h (max(I, Is))
+  float* Yslot;             // [B][k+1][d]
+  int force;                // VAR_AUTO, VAR_GEMV (vector path for all),
+                            // VAR_MFMA (matrix path for all bf16 experts)
+};
+
+struct CombineLaunch {
+  int out_bf16;
+  int B, d, k, has_shared;
+  const float* Yslot;
+  const float* topk_w;
+  void* out;
+};
+
+hipError_t launch_skinny(const SkinnyLaunch& a, hipStream_t st, char* desc, size_t desc_len);
+hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
+hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
+hipError_t launch_combine(const CombineLaunch& a, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Row blocks of the skinny kernel for a given variant (host-side geometry).
+int skinny_rows_per_block(int variant, int bf16, int M);
+int skinny_default_splits(int variant, int bf16, int M, int N, int K);
+
+}  // namespace moe
