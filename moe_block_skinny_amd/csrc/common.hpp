@@ -56,12 +56,18 @@ __device__ __forceinline__ u32x4 ld128_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// A 32-bit word as two bf16.  Takes the word by value: bit-casting an
+// ext-vector element subscript directly is miscompiled (always element 0).
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
 // sum_e w[e] * x[e] over one 128-bit chunk, accumulated into acc.
 __device__ __forceinline__ float dot_chunk(u32x4 w, u32x4 x, float acc, bf16_t) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
-                                          __builtin_bit_cast(bf16x2, x[i]), acc, false);
+  const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  const uint32_t x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), as_bf16x2(x0), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), as_bf16x2(x1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), as_bf16x2(x2), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
   return acc;
 }
 __device__ __forceinline__ float dot_chunk(u32x4 w, u32x4 x, float acc, float) {
