@@ -38,8 +38,9 @@
  *       Ws13 [2Is][d], Ws2 [d][Is]   shared expert (same split)
  *       W    [N][K]          dense skinny product
  *   - Workspace: `ws` is caller-owned device memory of at least
- *     moe_workspace_bytes(...) bytes.  It holds split-K partial sums,
- *     router logits, the SwiGLU intermediate and completion counters.  It must
+ *     moe_workspace_bytes(...) bytes.  It holds the router logits, the
+ *     SwiGLU intermediate, per-slot expert outputs and a completion counter.
+ *     It must
  *     be zero-filled once before its first use (moe_workspace_init); every
  *     call leaves its counter words at zero again.  Two calls that run
  *     concurrently must not share a workspace.
@@ -156,7 +157,7 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   X [B][K] dtype, W [N][K] dtype, Y [B][N] of y_dtype (dtype or
  *   MOE_DT_F32).  1 <= B <= 64; K a multiple of 8 (bf16) or 4 (fp32), and of
  *   32 for the mfma shape (bf16 only).  Output rounded to nearest-even when
- *   y_dtype is bf16. */
+ *   y_dtype is bf16.  Needs no workspace (ws may be NULL, ws_bytes 0). */
 moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
                          int y_dtype, void* ws, size_t ws_bytes, void* stream);
 
@@ -190,7 +191,7 @@ moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, con
  *   it; unselected experts are never read.  plan comes from moe_route (it
  *   must be complete before this call runs: same stream or synchronised).
  *   Yslot fp32 [B][k+1][d].  Scope as moe_route, plus I (and Is) multiples
- *   of 32 up to 512 (bf16; fp32: multiples of 4 up to 256, B <= 8). */
+ *   of 32 up to 256 (bf16; fp32: multiples of 4 up to 256, B <= 8). */
 moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const void* X,
                             const int32_t* plan, const void* W13, const void* W2, int Is,
                             const void* Ws13, const void* Ws2, float* Yslot, void* ws,
@@ -204,9 +205,16 @@ moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const 
 moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
                          int has_shared, void* out, void* stream);
 
-/* The whole block: moe_route, then moe_expert_ffn, then moe_combine, with
- * every intermediate in ws.  Same scope and results as the three calls;
- * topk_ids / topk_w / plan outputs are optional (NULL: kept in ws). */
+/* The whole block in three launches, every intermediate in ws:
+ *   1. router scoring + top-k + plan, with the shared expert's gate/up
+ *      (which needs no routing) in the same launch;
+ *   2. routed experts' gate/up + SwiGLU;
+ *   3. down projection of every expert fused with the weighted combine: the
+ *      per-slot outputs never leave the chip.
+ * Same scope and results as moe_route, moe_expert_ffn and moe_combine in
+ * sequence (bit for bit with the vector-ALU shapes; with the MFMA shape the
+ * shared expert's K split differs, within fp32 rounding).  topk_ids /
+ * topk_w are optional outputs (NULL: kept in ws). */
 moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
                        const void* Wr, const float* bias, int bias_ld, const void* W13,
                        const void* W2, const void* Ws13, const void* Ws2, void* out,

@@ -128,11 +128,11 @@ def profile_events(kernel: int, start=None, stop=None):
     _check(lib.moe_profile_events(kernel, h(start), h(stop)))
 
 
-def skinny_gemm(X, W, Y, ws, stream=None):
+def skinny_gemm(X, W, Y, ws=None, stream=None):
     B, K = X.shape
     N = W.shape[0]
     _check(lib.skinny_gemm(_dt(X), B, N, K, _ptr(X), _ptr(W), _ptr(Y), _dt(Y), _ptr(ws),
-                           ws.numel(), _stream(stream)))
+                           0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def moe_route(X, Wr, k, topk_ids, topk_w, plan, ws, bias=None, bias_ld=0, logits_out=None,

@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "expert_core.hpp"
 #include "internal.hpp"
 #include "moe_skinny.h"
 
@@ -27,7 +28,7 @@ thread_local char g_err[512] = "";
 thread_local char g_variant[256] = "";
 std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 
-constexpr int kMaxB = 64, kMaxE = 512, kMaxK = 16, kMaxI = 512;
+constexpr int kMaxB = 64, kMaxE = 512, kMaxK = 16, kMaxI = 256;
 constexpr size_t kAlign = 256;
 
 // Profiling hook: events bracketing every launch of one kernel.
@@ -102,33 +103,15 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
   return MOE_OK;
 }
 
-// Largest split count / row-block count any feasible shape can use.
-void skinny_ws_dims(int bf16, int B, int N, int K, int* smax, int* nrbmax) {
-  *smax = 1;
-  *nrbmax = 1;
-  for (int v = VAR_GEMV; v <= VAR_MFMA; ++v) {
-    if (v == VAR_MFMA && (!bf16 || K % 32)) continue;
-    const int s = skinny_default_splits(v, bf16, B, N, K);
-    const int rows = skinny_rows_per_block(v, bf16, B);
-    const int nrb = (N + rows - 1) / rows;
-    if (s > *smax) *smax = s;
-    if (nrb > *nrbmax) *nrbmax = nrb;
-  }
-}
-
+// Router workspace: fp32 logits [B][E] and the completion counter.  The
+// dense product needs none.
 struct SkinnyWs {
-  size_t partial, rb_counter, logits, done, total;
+  size_t logits, done, total;
 };
 
-SkinnyWs skinny_ws(int bf16, int B, int N, int K, bool router) {
-  int smax, nrbmax;
-  skinny_ws_dims(bf16, B, N, K, &smax, &nrbmax);
+SkinnyWs skinny_ws(int B, int N, bool router) {
   SkinnyWs w;
   size_t o = 0;
-  w.partial = o;
-  o = up(o + (size_t)smax * B * N * 4);
-  w.rb_counter = o;
-  o = up(o + (size_t)nrbmax * 4);
   w.logits = o;
   if (router) o = up(o + (size_t)B * N * 4);
   w.done = o;
@@ -153,20 +136,18 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 struct BlockWs {
   SkinnyWs route;
   ExpertWs ffn;
-  size_t route_off, ffn_off, yslot, ids, w, plan, total;
+  size_t route_off, ffn_off, ids, w, plan, total;
 };
 
 BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   BlockWs b;
-  b.route = skinny_ws(bf16, B, E, d, true);
+  b.route = skinny_ws(B, E, true);
   b.ffn = expert_ws(B, k, I, Is);
   size_t o = 0;
   b.route_off = o;
   o = up(o + b.route.total);
   b.ffn_off = o;
   o = up(o + b.ffn.total);
-  b.yslot = o;
-  o = up(o + (size_t)B * (k + 1) * d * 4);
   b.ids = o;
   o = up(o + (size_t)B * k * 4);
   b.w = o;
@@ -226,12 +207,13 @@ moe_status_t hip_status(hipError_t e, const char* what) {
 
 moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
                        const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
-                       float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl) {
+                       float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
+                       const ExpertLaunch* shared = nullptr) {
   const int bf16 = dt == MOE_DT_BF16;
   int v;
   moe_status_t s = resolve_skinny(bf16, B, d, &v);
   if (s) return s;
-  const SkinnyWs L = skinny_ws(bf16, B, E, d, true);
+  const SkinnyWs L = skinny_ws(B, E, true);
   SkinnyLaunch a = {};
   a.bf16 = bf16;
   a.X = X;
@@ -240,10 +222,9 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.N = E;
   a.K = d;
   a.variant = v;
-  a.S = skinny_default_splits(v, bf16, B, E, d);
-  a.partial = reinterpret_cast<float*>(ws + L.partial);
-  a.rb_counter = reinterpret_cast<uint32_t*>(ws + L.rb_counter);
+  a.S = skinny_default_splits(v, bf16, B, E, d, 1);
   a.router = 1;
+  if (shared) a.ex = *shared;
   a.bias = bias;
   a.bias_ld = bias_ld;
   a.logits = reinterpret_cast<float*>(ws + L.logits);
@@ -257,9 +238,9 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
 }
 
-moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, const int32_t* plan,
-                     const void* W13, const void* W2, int Is, const void* Ws13, const void* Ws2,
-                     float* Yslot, char* ws, int force, hipStream_t st, char* desc, size_t dl) {
+ExpertLaunch expert_launch(int dt, int B, int d, int E, int k, int I, const void* X, const int32_t* plan,
+                           const void* W13, const void* W2, int Is, const void* Ws13, const void* Ws2,
+                           char* ws, int force) {
   const ExpertWs L = expert_ws(B, k, I, Ws13 ? Is : 0);
   ExpertLaunch a = {};
   a.bf16 = dt == MOE_DT_BF16;
@@ -277,8 +258,15 @@ moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, c
   a.Ws2 = Ws2;
   a.h = reinterpret_cast<float*>(ws + L.h);
   a.hld = L.hld;
-  a.Yslot = Yslot;
   a.force = force;
+  return a;
+}
+
+moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, const int32_t* plan,
+                     const void* W13, const void* W2, int Is, const void* Ws13, const void* Ws2,
+                     float* Yslot, char* ws, int force, hipStream_t st, char* desc, size_t dl) {
+  ExpertLaunch a = expert_launch(dt, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, ws, force);
+  a.Yslot = Yslot;
   char d1[128] = "", d2[128] = "";
   moe_status_t s;
   {
@@ -347,10 +335,10 @@ size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I,
   switch (op) {
     case MOE_OP_SKINNY_GEMM:
       if (N <= 0 || K <= 0) return 0;
-      return skinny_ws(bf16, B, N, K, false).total;
+      return skinny_ws(B, N, false).total;
     case MOE_OP_ROUTE:
       if (E <= 0 || d <= 0) return 0;
-      return skinny_ws(bf16, B, E, d, true).total;
+      return skinny_ws(B, E, true).total;
     case MOE_OP_EXPERT_FFN:
       if (k <= 0) return 0;
       return expert_ws(B, k, I, Is).total;
@@ -382,9 +370,8 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   int v;
   s = resolve_skinny(bf16, B, K, &v);
   if (s) return s;
-  const SkinnyWs L = skinny_ws(bf16, B, N, K, false);
-  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
-  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  (void)ws;
+  (void)ws_bytes;
   SkinnyLaunch a = {};
   a.bf16 = bf16;
   a.X = X;
@@ -393,10 +380,7 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   a.N = N;
   a.K = K;
   a.variant = v;
-  a.S = skinny_default_splits(v, bf16, B, N, K);
-  char* w = static_cast<char*>(ws);
-  a.partial = reinterpret_cast<float*>(w + L.partial);
-  a.rb_counter = reinterpret_cast<uint32_t*>(w + L.rb_counter);
+  a.S = skinny_default_splits(v, bf16, B, N, K, 0);
   a.Y = Y;
   a.y_bf16 = y_dtype == MOE_DT_BF16;
   char desc[160];
@@ -425,7 +409,7 @@ moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, con
   int v;
   s = resolve_skinny(bf16, B, d, &v);
   if (s) return s;
-  const size_t need = skinny_ws(bf16, B, E, d, true).total;
+  const size_t need = skinny_ws(B, E, true).total;
   if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   char desc[160];
@@ -513,30 +497,32 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(w + L.ids);
   float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.w);
   int32_t* plan = reinterpret_cast<int32_t*>(w + L.plan);
-  float* yslot = reinterpret_cast<float*>(w + L.yslot);
-  char d1[160] = "", d2[300] = "";
+  ExpertLaunch ex = expert_launch(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, w + L.ffn_off, force);
+  ex.topk_w = tw;
+  ex.out = out;
+  ex.out_bf16 = bf16;
+  // The shared expert's gate/up needs no routing, so it runs inside the
+  // router launch when both take the same kernel family (vector or MFMA).
+  // The router kernel's shape family must match the shared expert's: the
+  // vector router kernel carries only the vector gate/up, the MFMA one only
+  // the MFMA gate/up.
+  const int paths = expert_paths(bf16, force, B);
+  ex.skip_shared = Ws13 && (paths == kPathValu ? v != VAR_MFMA : v == VAR_MFMA);
+  char d1[200] = "", d2[128] = "", d3[128] = "";
   if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
-                     st, d1, sizeof d1)))
+                     st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
     return s;
-  if ((s = run_ffn(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, yslot, w + L.ffn_off, force,
-                   st, d2, sizeof d2)))
-    return s;
-  CombineLaunch c = {};
-  c.out_bf16 = bf16;
-  c.B = B;
-  c.d = d;
-  c.k = k;
-  c.has_shared = Ws13 ? 1 : 0;
-  c.Yslot = yslot;
-  c.topk_w = tw;
-  c.out = out;
   {
-    ProfileScope prof(MOE_KERNEL_COMBINE, st);
-    s = hip_status(launch_combine(c, st), "combine launch");
+    ProfileScope prof(MOE_KERNEL_EXPERT_UP, st);
+    if ((s = hip_status(launch_expert_up(ex, st, d2, sizeof d2), "expert gate/up launch"))) return s;
   }
-  if (s) return s;
+  {
+    ProfileScope prof(MOE_KERNEL_EXPERT_DOWN, st);
+    if ((s = hip_status(launch_expert_down_combine(ex, st, d3, sizeof d3), "expert down+combine launch")))
+      return s;
+  }
   char desc[480];
-  snprintf(desc, sizeof desc, "route[%s] ffn[%s] combine", d1, d2);
+  snprintf(desc, sizeof desc, "route[%s] %s; %s", d1, d2, d3);
   record("moe_block", B, desc);
   return MOE_OK;
 }

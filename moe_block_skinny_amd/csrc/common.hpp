@@ -104,13 +104,30 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// 64-bit DPP move of both halves (CTRL: a DPP lane-permutation control).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wave-wide max of a 64-bit key, returned uniformly to every lane: DPP
+// exchanges within each 16-lane row (xor 1, xor 2, half-mirror, mirror),
+// then the four row results are read out and compared.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint64_t o2 = __shfl_xor(v, o, kWave);
-    v = o2 > v ? o2 : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
 // ---- vector-ALU streaming core ---------------------------------------------
@@ -154,6 +171,64 @@ __device__ __forceinline__ void valu_dot(const T* const (&wr)[R], const T* const
     for (int t = 0; t < MB; ++t) acc[r][t] = group_sum<64>(acc[r][t]);
 }
 
+// ---- MFMA streaming core -----------------------------------------------------
+
+// One wave: a 16-row A tile (this lane's row pointer wr, real when wok;
+// lane l holds row l%16 and K elements 8*(l/16) .. +7 of every 32-wide step)
+// against NT 16-token B tiles (xr[nt], real when xok[nt]) with
+// v_mfma_f32_16x16x32_bf16.  The wave takes the SB-step blocks b0, b0 +
+// bstride, ... of the J steps.  Two register stages: the loads of the next
+// block are issued before the current one is multiplied, so a wave always has
+// a block of loads in flight.  Addresses are clamped into range and invalid
+// operands are zeroed at use, so no load sits behind a branch.
+template <int NT, int SB>
+__device__ __forceinline__ void mfma_kloop(const uint16_t* wr, bool wok, const uint16_t* const (&xr)[NT],
+                                           const bool (&xok)[NT], int kq, int J, int b0, int bstride,
+                                           f32x4 (&acc)[NT]) {
+  u32x4 a0[SB], x0[SB][NT], a1[SB], x1[SB][NT];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load = [&](int blk, u32x4 (&av)[SB], u32x4 (&xv)[SB][NT]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int j = blk * SB + u;
+      const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+      av[u] = ld128_stream(wr + off);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) xv[u][nt] = ld128(xr[nt] + off);
+    }
+  };
+  auto mul = [&](int blk, const u32x4 (&av)[SB], const u32x4 (&xv)[SB][NT]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const bool ok = blk * SB + u < J;
+      const u32x4 a = (ok && wok) ? av[u] : zero;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const u32x4 b = (ok && xok[nt]) ? xv[u][nt] : zero;
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, b), acc[nt], 0, 0, 0);
+      }
+    }
+  };
+  int blk = b0;
+  if (blk * SB >= J) return;
+  load(blk, a0, x0);
+  while (true) {
+    int nb = blk + bstride;
+    bool more = nb * SB < J;
+    if (more) load(nb, a1, x1);
+    mul(blk, a0, x0);
+    if (!more) break;
+    blk = nb;
+    nb = blk + bstride;
+    more = nb * SB < J;
+    if (more) load(nb, a0, x0);
+    mul(blk, a1, x1);
+    if (!more) break;
+    blk = nb;
+  }
+}
+
 // Lane `lane` picks acc[t == lane]: spreads MB results over the first lanes.
 template <int MB>
 __device__ __forceinline__ float pick_lane(const float (&v)[MB], int lane) {
@@ -168,15 +243,17 @@ __device__ __forceinline__ float pick_lane(const float (&v)[MB], int lane) {
 
 // Called by every thread of a workgroup after it stored its results.  Returns
 // true in the workgroup that arrives last of `expected` on `counter`, which
-// also resets the counter to zero for the next launch.  Every thread's
-// release fence publishes its own stores at device scope before the barrier;
-// the acquire fence in the last workgroup makes every other workgroup's
-// stores visible to it.
+// also resets the counter to zero for the next launch.  Each wave first waits
+// until its own stores are acknowledged (they are in this XCD's L2); then one
+// release atomic per workgroup writes the L2 back and counts the arrival, and
+// only the last workgroup pays the acquire (L2 invalidate) before it reads
+// what the others wrote.  A device-scope fence costs tens of nanoseconds and
+// is serialised across the device, so there is exactly one per workgroup.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     int last = (old == expected - 1u);
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;

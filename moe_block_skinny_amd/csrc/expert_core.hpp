@@ -1,0 +1,384 @@
+// expert_core.hpp -- device code of one expert task: gate/up + SwiGLU over a
+// tile of (gate row i, up row I+i) pairs, and the down projection of a tile
+// of 16 output rows.  Used by the expert kernels and, for the shared expert,
+// by the router kernel of the fused block.
+//
+// Expert e computes h = silu(x . Wg^T) * (x . Wu^T), y = h . W2^T, with
+// silu(z) = z / (1 + exp(-z)); W13[e] is [2I][d] (gate rows, then up rows),
+// W2[e] is [d][I] (see expert.hip for the page citations).
+//
+// Shape by the expert's token count m:
+//   m <= 8 : vector ALU.  Gate/up: one wave per pair over the whole of d, so
+//            SwiGLU happens in registers.  Down: L lanes per W2 row (L*VEC >=
+//            I), 64/L rows per load instruction.
+//   m > 8  : MFMA 16x16x32 bf16.  Gate/up: a 16-row A tile holding 4 gate +
+//            4 up rows; the waves of the workgroup split d and meet in LDS.
+//            Down: 16 W2 rows per wave over all of I; h (fp32) enters as a
+//            bf16 hi/lo pair so it keeps ~16 mantissa bits.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int kMaxPlanWords = 2 + 2 * 512 + 64 * 16;
+constexpr int kUpPairsMfma = 4;   // gate/up pairs per MFMA up task
+
+// Routing plan staged in LDS (see moe_plan_words for the layout).
+struct PlanView {
+  int n, maxa;
+  const int32_t* active;
+  const int32_t* offs;
+  const int32_t* slots;
+};
+
+// Copy the plan into LDS with the whole workgroup (one coalesced pass) and
+// return a view of it.  Ends with a barrier.
+__device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s_plan) {
+  const int nslot = a.B * a.k;
+  const int maxa = nslot < a.E ? nslot : a.E;
+  const int words = 2 + 2 * maxa + nslot;
+  for (int i = threadIdx.x; i < words; i += blockDim.x) s_plan[i] = a.plan[i];
+  __syncthreads();
+  PlanView p;
+  p.maxa = maxa;
+  p.n = s_plan[0];
+  p.active = s_plan + 1;
+  p.offs = s_plan + 1 + maxa;
+  p.slots = s_plan + 2 + 2 * maxa;
+  return p;
+}
+
+// Entry e_idx of the plan: a routed expert (e_idx < n) or the shared one.
+struct ExpertView {
+  int m;              // tokens
+  int I;              // intermediate size
+  const void* W13;    // [2I][d]
+  const void* W2;     // [d][I]
+  int slot0;          // first plan slot (routed) or -1 (shared)
+};
+
+template <typename T>
+__device__ __forceinline__ ExpertView expert_view(const ExpertLaunch& a, const PlanView& p, int e_idx) {
+  ExpertView v;
+  if (e_idx < p.n) {
+    const int e = p.active[e_idx];
+    v.m = p.offs[e_idx + 1] - p.offs[e_idx];
+    v.I = a.I;
+    v.W13 = reinterpret_cast<const T*>(a.W13) + (size_t)e * 2 * a.I * a.d;
+    v.W2 = reinterpret_cast<const T*>(a.W2) + (size_t)e * a.d * a.I;
+    v.slot0 = p.offs[e_idx];
+  } else {
+    v.m = a.B;
+    v.I = a.Is;
+    v.W13 = a.Ws13;
+    v.W2 = a.Ws2;
+    v.slot0 = -1;
+  }
+  return v;
+}
+
+// The shared expert alone (no plan needed).
+__device__ __forceinline__ ExpertView shared_view(const ExpertLaunch& a) {
+  ExpertView v;
+  v.m = a.B;
+  v.I = a.Is;
+  v.W13 = a.Ws13;
+  v.W2 = a.Ws2;
+  v.slot0 = -1;
+  return v;
+}
+
+// Token index and slot row (row of h / of the per-slot outputs) of the i-th
+// token of an entry: routed slot s = t*k + j sits at row s, shared token t
+// at row B*k + t.
+__device__ __forceinline__ void token_of(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                         int i, int& tok, int& srow) {
+  if (v.slot0 >= 0) {
+    const int s = slots[v.slot0 + i];
+    tok = s / a.k;
+    srow = s;
+  } else {
+    tok = i;
+    srow = a.B * a.k + i;
+  }
+}
+
+// Kernel shape per entry.  PATHS is fixed per kernel instantiation: 1 = the
+// vector shape only (fp32, B <= 8 or forced), 2 = MFMA only (forced), 3 =
+// either, by token count (m > 8: MFMA).  Keeping unused shapes out of an
+// instantiation keeps its register count, hence its occupancy, down.
+constexpr int kPathValu = 1, kPathMfma = 2, kPathBoth = 3;
+
+template <int PATHS>
+__device__ __forceinline__ bool use_mfma(int m) {
+  if constexpr (PATHS == kPathValu) return false;
+  else if constexpr (PATHS == kPathMfma) return true;
+  else return m > 8;
+}
+
+// Host and device agree on the path set of a launch.
+__host__ __device__ __forceinline__ int expert_paths(int bf16, int force, int B) {
+  if (!bf16) return kPathValu;
+  if (force == VAR_MFMA) return kPathMfma;
+  if (force == VAR_GEMV || B <= 8) return kPathValu;
+  return kPathBoth;
+}
+
+// ---- gate/up + SwiGLU ------------------------------------------------------
+
+// Wave `wave` takes pair i (gate row i, up row I+i) over all of d and writes
+// h[srow][i] for the entry's tokens.
+template <typename T, int MB>
+__device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i) {
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int U = MB <= 1 ? 8 : (MB <= 2 ? 4 : 2);
+  const int lane = threadIdx.x & 63;
+  if (i >= v.I) return;
+  const T* W13 = reinterpret_cast<const T*>(v.W13);
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const T* wr[2] = {W13 + (size_t)i * a.d, W13 + (size_t)(v.I + i) * a.d};
+  const T* xr[MB];
+  int srow[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) {
+    int tok = 0, sr = 0;
+    if (t < v.m) token_of(a, slots, v, t, tok, sr);
+    xr[t] = X + (size_t)tok * a.d;
+    srow[t] = sr;
+  }
+  float acc[2][MB];
+  valu_dot<T, 2, MB, U>(wr, xr, v.m, 0, a.d / VEC, acc);
+  if (lane < v.m) {
+    const float g = pick_lane<MB>(acc[0], lane), u = pick_lane<MB>(acc[1], lane);
+    int sr = 0;
+#pragma unroll
+    for (int t = 0; t < MB; ++t)
+      if (t == lane) sr = srow[t];
+    a.h[(size_t)sr * a.hld + i] = silu(g) * u;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void up_valu_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                                 int i) {
+  if (v.m <= 1) up_valu<T, 1>(a, slots, v, i);
+  else if (v.m <= 2) up_valu<T, 2>(a, slots, v, i);
+  else if (v.m <= 4) up_valu<T, 4>(a, slots, v, i);
+  else up_valu<T, 8>(a, slots, v, i);
+}
+
+// Pairs i0..i0+3 with the whole workgroup: lanes with row%16 in 0..3 load
+// gate rows, 4..7 up rows, 8..15 stay zero; wave w covers the w-th of nw
+// slices of the K steps.  s_red holds nw * NT * 1 KB.
+template <int NT>
+__device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i0, float* s_red) {
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const bf16_t* W13 = reinterpret_cast<const bf16_t*>(v.W13);
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
+  int wrow = -1;
+  if (row < 4 && i0 + row < v.I) wrow = i0 + row;
+  else if (row >= 4 && row < 8 && i0 + row - 4 < v.I) wrow = v.I + i0 + row - 4;
+  const bf16_t* wr = W13 + (size_t)(wrow >= 0 ? wrow : 0) * a.d;
+  const bf16_t* xr[NT];
+  bool xok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int ti = nt * 16 + row;
+    int tok = 0, sr = 0;
+    xok[nt] = ti < v.m;
+    if (xok[nt]) token_of(a, slots, v, ti, tok, sr);
+    xr[nt] = X + (size_t)tok * a.d;
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mfma_kloop<NT, NT <= 2 ? 4 : 2>(wr, wrow >= 0, xr, xok, kq, a.d / 32, wave, nw, acc);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_red[((wave * NT + nt) * 64 + lane) * 4 + q] = acc[nt][q];
+  __syncthreads();
+  // thread (q, t): pair i0+q, token t.  Gate sums sit in lanes 0..15 (rows
+  // 0..3) and up sums in lanes 16..31 (rows 4..7) of each wave's tile.
+  for (int idx = threadIdx.x; idx < 4 * 64; idx += blockDim.x) {
+    const int q = idx >> 6, t = idx & 63;
+    if (t < v.m && i0 + q < v.I) {
+      const int nt = t >> 4, l = t & 15;
+      float g = 0.f, u = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        g += s_red[((w * NT + nt) * 64 + l) * 4 + q];
+        u += s_red[((w * NT + nt) * 64 + 16 + l) * 4 + q];
+      }
+      int tok, sr;
+      token_of(a, slots, v, t, tok, sr);
+      a.h[(size_t)sr * a.hld + i0 + q] = silu(g) * u;
+    }
+  }
+  __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ void up_mfma_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                                 int i0, float* s_red) {
+  if constexpr (sizeof(T) == 2) {
+    const int nt = (v.m + 15) / 16;
+    if (nt <= 1) up_mfma<1>(a, slots, v, i0, s_red);
+    else if (nt == 2) up_mfma<2>(a, slots, v, i0, s_red);
+    else if (nt == 3) up_mfma<3>(a, slots, v, i0, s_red);
+    else up_mfma<4>(a, slots, v, i0, s_red);
+  }
+}
+
+// Shared-expert gate/up tile `tile` with the whole workgroup (nw waves):
+// the vector shape takes nw pairs (one per wave), the MFMA shape 4 pairs.
+template <typename T, int PATHS>
+__device__ __forceinline__ void shared_up_task(const ExpertLaunch& a, int tile, float* s_red) {
+  const ExpertView v = shared_view(a);
+  const int nw = blockDim.x >> 6;
+  if (use_mfma<PATHS>(v.m)) up_mfma_dispatch<T>(a, nullptr, v, tile * kUpPairsMfma, s_red);
+  else up_valu_dispatch<T>(a, nullptr, v, tile * nw + (threadIdx.x >> 6));
+}
+
+// ---- down projection ---------------------------------------------------------
+
+// Destination of the per-slot outputs of one 16-row tile: either the global
+// Yslot [B][k+1][d] or an LDS tile [B*k + B][16].
+struct YSink {
+  float* base;
+  int lds;       // 1: LDS tile rows of 16, else global Yslot
+  int r0;        // first row of the tile (LDS)
+  __device__ __forceinline__ float* at(const ExpertLaunch& a, int srow, int row) const {
+    if (lds) return base + srow * 16 + (row - r0);
+    int t, j;
+    if (srow < a.B * a.k) { t = srow / a.k; j = srow % a.k; }
+    else { t = srow - a.B * a.k; j = a.k; }
+    return base + ((size_t)t * (a.k + 1) + j) * a.d + row;
+  }
+};
+
+// Rows r0..r0+15 of entry v with one wave: L lanes per W2 row (L*VEC >= I),
+// P = 64/L rows per load instruction, R = 16/P rows per lane.
+template <typename T, int L>
+__device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
+                          const YSink& sink) {
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int P = 64 / L;
+  constexpr int R = 16 / P;
+  const int lane = threadIdx.x & 63;
+  const int c = lane % L, g = lane / L;
+  const bool cok = c * VEC < v.I;
+  const int rbase = r0 + g;
+  const T* W2 = reinterpret_cast<const T*>(v.W2);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 wv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = rbase + P * r;
+    wv[r] = (cok && row < a.d) ? ld128_stream(W2 + (size_t)row * v.I + (size_t)c * VEC) : zero;
+  }
+  for (int t = 0; t < v.m; ++t) {
+    int tok, sr;
+    token_of(a, slots, v, t, tok, sr);
+    float xs[VEC];
+    const float* hp = a.h + (size_t)sr * a.hld + (size_t)(cok ? c * VEC : 0);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) xs[e] = cok ? hp[e] : 0.f;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_f32x(wv[r], xs, 0.f, T()));
+    if (c == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = rbase + P * r;
+        if (row < a.d) *sink.at(a, sr, row) = acc[r];
+      }
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
+                          const YSink& sink) {
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
+  const bf16_t* wr = W2 + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
+  const float* hr[NT];
+  bool ok[NT];
+  int srow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int ti = nt * 16 + row;
+    int tok = 0, sr = 0;
+    ok[nt] = ti < v.m;
+    if (ok[nt]) token_of(a, slots, v, ti, tok, sr);
+    hr[nt] = a.h + (size_t)sr * a.hld;
+    srow[nt] = sr;
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int J = v.I / 32;
+  for (int j = 0; j < J; ++j) {
+    const size_t off = (size_t)(j * 4 + kq) * 8;
+    const u32x4 av = ld128_stream(wr + off);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+      if (ok[nt]) {
+        const f32x4 h0 = *reinterpret_cast<const f32x4*>(hr[nt] + off);
+        const f32x4 h1 = *reinterpret_cast<const f32x4*>(hr[nt] + off + 4);
+        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16_t a0 = f32_to_bf16(hv[2 * e]), a1 = f32_to_bf16(hv[2 * e + 1]);
+          const bf16_t b0 = f32_to_bf16(hv[2 * e] - bf16_to_f32(a0));
+          const bf16_t b1 = f32_to_bf16(hv[2 * e + 1] - bf16_to_f32(a1));
+          hi[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+          lo[e] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        }
+      }
+      const u32x4 hv4 = {hi[0], hi[1], hi[2], hi[3]}, lv4 = {lo[0], lo[1], lo[2], lo[3]};
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, hv4), acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, lv4), acc[nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (ok[nt]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * kq + i;
+        if (r < a.d) *sink.at(a, srow[nt], r) = acc[nt][i];
+      }
+    }
+  }
+}
+
+template <typename T, int PATHS>
+__device__ __forceinline__ void down_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                              int r0, const YSink& sink) {
+  if (use_mfma<PATHS>(v.m)) {
+    if constexpr (sizeof(T) == 2) {
+      const int nt = (v.m + 15) / 16;
+      if (nt <= 1) down_mfma<1>(a, slots, v, r0, sink);
+      else if (nt == 2) down_mfma<2>(a, slots, v, r0, sink);
+      else if (nt == 3) down_mfma<3>(a, slots, v, r0, sink);
+      else down_mfma<4>(a, slots, v, r0, sink);
+    }
+  } else {
+    constexpr int VEC = Elem<T>::VEC;
+    const int chunks = v.I / VEC;
+    if (chunks <= 16) down_valu<T, 16>(a, slots, v, r0, sink);
+    else if (chunks <= 32 || sizeof(T) == 2) down_valu<T, 32>(a, slots, v, r0, sink);
+    else if constexpr (sizeof(T) == 4) down_valu<T, 64>(a, slots, v, r0, sink);
+  }
+}
+
+}  // namespace moe

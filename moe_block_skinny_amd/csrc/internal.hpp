@@ -10,34 +10,6 @@ namespace moe {
 
 enum Variant { VAR_AUTO = 0, VAR_GEMV = 1, VAR_SPLITK = 2, VAR_MFMA = 3 };
 
-// Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
-// (Y, y_bf16) or, in router mode, turned into logits + bias and then top-k
-// weights and the routing plan by the last workgroup to finish.
-struct SkinnyLaunch {
-  int bf16;                 // element type of X and W
-  const void* X;
-  const void* W;
-  int M, N, K;
-  int variant;              // VAR_GEMV / VAR_SPLITK / VAR_MFMA (resolved)
-  int S;                    // K splits (1 = none)
-  float* partial;           // [S][M][N] fp32 when S > 1
-  uint32_t* rb_counter;     // one per row block when S > 1 (zero on entry)
-  // store mode
-  void* Y;
-  int y_bf16;
-  // router mode (router != 0)
-  int router;
-  const float* bias;
-  int bias_ld;
-  float* logits;            // [M][N] workspace
-  float* logits_out;        // optional copy [M][N]
-  uint32_t* done_counter;   // zero on entry
-  int k;
-  int32_t* topk_ids;
-  float* topk_w;
-  int32_t* plan;
-};
-
 // Expert FFN stage over the routing plan.  h is fp32 [B*k + B][Imax]:
 // routed slot s = t*k + j at row s, shared-expert token t at row B*k + t.
 struct ExpertLaunch {
@@ -54,6 +26,43 @@ struct ExpertLaunch {
   float* Yslot;             // [B][k+1][d]
   int force;                // VAR_AUTO, VAR_GEMV (vector path for all),
                             // VAR_MFMA (matrix path for all bf16 experts)
+  int skip_shared;          // gate/up kernel: the shared expert is done elsewhere
+  // fused down + combine
+  const float* topk_w;      // [B][k]
+  void* out;                // [B][d]
+  int out_bf16;
+};
+
+// Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
+// (Y, y_bf16) or, in router mode, turned into logits + bias and then top-k
+// weights and the routing plan by the last workgroup to finish.  S is the
+// number of waves per workgroup, which split K among themselves.
+struct SkinnyLaunch {
+  int bf16;                 // element type of X and W
+  const void* X;
+  const void* W;
+  int M, N, K;
+  int variant;              // VAR_GEMV / VAR_SPLITK / VAR_MFMA (resolved)
+  int S;                    // waves per workgroup (in-workgroup K split)
+  // store mode
+  void* Y;
+  int y_bf16;
+  // router mode (router != 0)
+  int router;
+  const float* bias;
+  int bias_ld;
+  float* logits;            // [M][N] workspace
+  float* logits_out;        // optional copy [M][N]
+  uint32_t* done_counter;   // zero on entry
+  int k;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* plan;
+  // router workgroups are blockIdx < router_wgs; in the fused block the
+  // remaining shared_tiles workgroups run the shared expert's gate/up (ex)
+  int router_wgs;
+  int shared_tiles;
+  ExpertLaunch ex;
 };
 
 struct CombineLaunch {
@@ -67,11 +76,13 @@ struct CombineLaunch {
 hipError_t launch_skinny(const SkinnyLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
+hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 // Row blocks of the skinny kernel for a given variant (host-side geometry).
-int skinny_rows_per_block(int variant, int bf16, int M);
-int skinny_default_splits(int variant, int bf16, int M, int N, int K);
+int skinny_rows_per_block(int variant, int router);
+int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router);
+int shared_up_tiles_host(const ExpertLaunch& ex, int nw);
 
 }  // namespace moe

@@ -14,26 +14,29 @@
 //
 // Three kernel shapes, all streaming every weight byte exactly once with
 // 128-bit loads (one 1 KB row segment per wave instruction):
-//   gemv   : M <= 2 activation rows; a wave owns 2 weight rows over a K range,
-//            the 64 lanes split K, v_dot2_f32_bf16 (or fp32 FMA) accumulates,
-//            one butterfly reduction at the end.
-//   splitk : M <= 8; a wave owns 4 weight rows so each activation chunk it
-//            loads is reused 4 times.
+//   gemv   : M <= 2 activation rows; a workgroup owns 2 weight rows, its
+//            waves split K, v_dot2_f32_bf16 (or fp32 FMA) accumulates.
+//   splitk : M <= 8; a workgroup owns 4 weight rows, so each activation chunk
+//            a lane loads is reused 4 times; its waves split K.
 //   mfma   : M <= 64 (bf16); v_mfma_f32_16x16x32_bf16 with 16 weight rows as
 //            the A operand and up to four 16-token tiles as B, used once
-//            batch x rows is a dense contraction.
-// Every shape may split K over S workgroups.  Split partials go to an fp32
-// workspace and the last workgroup of each row block (completion counter)
-// sums them in fixed split order, so results are deterministic.
-// In router mode the last row block to finish also selects the top-k
-// experts per token, computes their softmax weights and builds the plan.
+//            batch x rows is a dense contraction; its waves split K.
+// Split-K stays inside the workgroup: each wave reduces its lanes, the waves
+// meet in LDS and are summed in fixed wave order, so results are
+// deterministic and no partial sum ever goes through global memory (a
+// device-wide fence on this GPU writes back and invalidates the L2 of every
+// XCD, far dearer than an LDS exchange).  The number of waves per workgroup
+// is chosen on the host so that a launch has ~1.5k waves in flight.
+// In router mode every workgroup arrives once on a completion counter; the
+// last one selects the top-k experts per token, computes their softmax
+// weights and builds the plan.
 
 #include "common.hpp"
+#include "expert_core.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
-constexpr int kNW = 4;  // waves per workgroup
 
 // ---- epilogue ---------------------------------------------------------------
 
@@ -49,29 +52,24 @@ __device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n
   }
 }
 
-__device__ __forceinline__ void emit(const SkinnyLaunch& a, int s, int t, int n, float v) {
-  if (a.S > 1)
-    a.partial[((size_t)s * a.M + t) * a.N + n] = v;
-  else
-    finish_value(a, t, n, v);
-}
-
 // ---- router finish: top-k, weights, plan (one workgroup) ------------------
 
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 16;
 constexpr int kMaxB = 64;
 
-// One wave selects token t's top-k.  Keys order by fp32 logit, then by lower
-// expert index; k rounds of a wave-wide max each remove one winner.
-__device__ void topk_token(const SkinnyLaunch& a, int t, int* s_ids) {
+// One wave selects the top-k of one token from its logits lv (lane l holds
+// experts l, l+64, ...).  Keys order by fp32 logit, then by lower expert
+// index; k rounds of a wave-wide max each remove one winner.
+__device__ __forceinline__ void topk_select(const SkinnyLaunch& a, int t, const float (&lv)[kMaxE / 64],
+                                            int* s_ids) {
   const int lane = threadIdx.x & 63;
   const int E = a.N, k = a.k;
   uint64_t key[kMaxE / 64];
 #pragma unroll
   for (int i = 0; i < kMaxE / 64; ++i) {
-    int e = lane + 64 * i;
-    key[i] = e < E ? topk_key(ld_shared_f32(&a.logits[(size_t)t * E + e]), e) : 0ull;
+    const int e = lane + 64 * i;
+    key[i] = e < E ? topk_key(lv[i], e) : 0ull;
   }
   int sel_e[kMaxK];
   float sel_v[kMaxK];
@@ -84,7 +82,7 @@ __device__ void topk_token(const SkinnyLaunch& a, int t, int* s_ids) {
 #pragma unroll
       for (int i = 0; i < kMaxE / 64; ++i) best = key[i] > best ? key[i] : best;
       best = wave_max_u64(best);
-      int e = key_index(best);
+      const int e = key_index(best);
       sel_e[j] = e;
       sel_v[j] = key_value(best);
 #pragma unroll
@@ -114,7 +112,32 @@ __device__ void topk_token(const SkinnyLaunch& a, int t, int* s_ids) {
   }
 }
 
-__device__ void route_finish(const SkinnyLaunch& a) {
+// The wave's tokens t = wave, wave + nw, ... in batches of four: all logit
+// loads of a batch are issued (clamped addresses, no branches) before any is
+// used, so a batch costs one memory round trip.
+__device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, int* s_ids) {
+  constexpr int QB = 4;
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.N, M = a.M;
+  for (int t0 = wave; t0 < M; t0 += nw * QB) {
+    float lv[QB][kMaxE / 64];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int t = t0 + nw * q;
+      const int tc = t < M ? t : M - 1;
+#pragma unroll
+      for (int i = 0; i < kMaxE / 64; ++i) {
+        const int e = lane + 64 * i;
+        lv[q][i] = ld_shared_f32(&a.logits[(size_t)tc * E + (e < E ? e : E - 1)]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      if (t0 + nw * q < M) topk_select(a, t0 + nw * q, lv[q], s_ids);
+  }
+}
+
+__device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   __shared__ int s_ids[kMaxB * kMaxK];
   __shared__ unsigned long long s_mask[kMaxE];
   __shared__ int s_cnt[kMaxE];
@@ -123,7 +146,7 @@ __device__ void route_finish(const SkinnyLaunch& a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int M = a.M, E = a.N, k = a.k, nslot = M * k;
 
-  for (int t = wave; t < M; t += kNW) topk_token(a, t, s_ids);
+  topk_tokens(a, s_ids);
   for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
   __syncthreads();
   // bit t of s_mask[e] is set when token t selected expert e (B <= 64)
@@ -174,77 +197,101 @@ __device__ void route_finish(const SkinnyLaunch& a) {
   }
 }
 
-// Shared tail of every skinny kernel: split-K reduction by the last
-// workgroup of the row block, then (router) the route finish by the last row
-// block.  rows_pb = rows per row block, nrb = row blocks.
-__device__ __forceinline__ void skinny_tail(const SkinnyLaunch& a, int rb, int rows_pb, int nrb) {
+// Router tail: every router workgroup arrives once; the last runs the finish.
+__device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   __shared__ int s_flag;
-  if (a.S > 1) {
-    if (!arrive_last(&a.rb_counter[rb], (uint32_t)a.S, &s_flag)) return;
-    const int n_lo = rb * rows_pb;
-    for (int idx = threadIdx.x; idx < rows_pb * a.M; idx += blockDim.x) {
-      int t = idx / rows_pb, n = n_lo + idx % rows_pb;
-      if (n >= a.N) continue;
-      float v = 0.f;
-      for (int s = 0; s < a.S; ++s) v += ld_shared_f32(&a.partial[((size_t)s * a.M + t) * a.N + n]);
-      finish_value(a, t, n, v);
-    }
-  }
-  if (a.router) {
-    if (!arrive_last(a.done_counter, (uint32_t)nrb, &s_flag)) return;
-    route_finish(a);
-  }
+  if (!a.router) return;
+  if (!arrive_last(a.done_counter, (uint32_t)a.router_wgs, &s_flag)) return;
+  route_finish(a);
 }
 
 // ---- vector-ALU kernels (gemv / splitk) ----------------------------------
 
-template <typename T, int R, int MB>
-__global__ __launch_bounds__(256) void skinny_valu_kernel(SkinnyLaunch a) {
+// Workgroup: RB weight rows starting at blockIdx.x * RB, all K.  Wave w
+// takes the 64-chunk blocks w, w + NW, w + 2 NW, ... of every row (one 1 KB
+// segment per row per load instruction); U blocks per lane are in flight.
+template <typename T, int RB, int MB, int U>
+__global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int U = MB <= 2 ? 4 : 2;
-  const int rows_pb = kNW * R;
-  const int nrb = (a.N + rows_pb - 1) / rows_pb;
-  const int rb = blockIdx.x % nrb, s = blockIdx.x / nrb;
+  __shared__ float s_red[16 * RB * MB];
+  if (a.router && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
+    shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, nullptr);
+    return;
+  }
+  const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = rb * rows_pb + wave * R;
-  const int C = a.K / VEC;
-  const int c0 = (int)((long long)s * C / a.S), c1 = (int)((long long)(s + 1) * C / a.S);
+  const int n0 = blockIdx.x * RB;
   const T* W = reinterpret_cast<const T*>(a.W);
   const T* X = reinterpret_cast<const T*>(a.X);
-  const T* wr[R];
+  const T* wr[RB];
   const T* xr[MB];
 #pragma unroll
-  for (int r = 0; r < R; ++r) wr[r] = W + (size_t)(n0 + r < a.N ? n0 + r : a.N - 1) * a.K;
+  for (int r = 0; r < RB; ++r) wr[r] = W + (size_t)(n0 + r < a.N ? n0 + r : a.N - 1) * a.K;
 #pragma unroll
   for (int t = 0; t < MB; ++t) xr[t] = X + (size_t)(t < a.M ? t : 0) * a.K;
-  float acc[R][MB];
-  valu_dot<T, R, MB, U>(wr, xr, a.M, c0, c1, acc);
+  const int C = a.K / VEC;
+  float acc[RB][MB];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = n0 + r;
-    const float v = pick_lane<MB>(acc[r], lane);
-    if (n < a.N && lane < a.M && lane < MB) emit(a, s, lane, n, v);
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[r][t] = 0.f;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int blk = wave; blk * 64 < C; blk += nw * U) {
+    u32x4 wv[U][RB], xv[U][MB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (blk + u * nw) * 64 + lane;
+      const bool ok = c < C;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) wv[u][r] = ok ? ld128_stream(wr[r] + (size_t)c * VEC) : zero;
+#pragma unroll
+      for (int t = 0; t < MB; ++t) xv[u][t] = (ok && t < a.M) ? ld128(xr[t] + (size_t)c * VEC) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MB; ++t) acc[r][t] = dot_chunk(wv[u][r], xv[u][t], acc[r][t], T());
   }
-  skinny_tail(a, rb, rows_pb, nrb);
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      const float v = group_sum<64>(acc[r][t]);
+      if (lane == 0) s_red[(wave * RB + r) * MB + t] = v;
+    }
+  __syncthreads();
+  if (threadIdx.x < RB * MB) {
+    const int r = threadIdx.x / MB, t = threadIdx.x % MB, n = n0 + r;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += s_red[(w * RB + r) * MB + t];
+    if (n < a.N && t < a.M) finish_value(a, t, n, v);
+  }
+  router_tail(a);
 }
 
 // ---- MFMA kernel (bf16) --------------------------------------------------
 
-// A wave: 16 weight rows (A operand: lane l holds row l%16, K elements
+// Workgroup: 16 weight rows (A operand: lane l holds row l%16, K elements
 // 8*(l/16) .. +7 of each 32-wide step) against NT tiles of 16 activation
 // rows (B operand: lane l holds token l%16 of the tile, same K elements).
-// The accumulator of tile nt holds, in lane l, rows 4*(l/16)+i, token l%16.
+// Wave w takes the 4-step blocks w, w + NW, ... (128 K elements per row, 256
+// contiguous bytes, over four back-to-back loads).  The accumulator of tile
+// nt holds, in lane l, rows 4*(l/16)+i, token l%16.
 template <int NT>
-__global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyLaunch a) {
-  constexpr int U = NT <= 2 ? 4 : 2;
-  const int rows_pb = kNW * 16;
-  const int nrb = (a.N + rows_pb - 1) / rows_pb;
-  const int rb = blockIdx.x % nrb, s = blockIdx.x / nrb;
+__global__ __launch_bounds__(512) void skinny_mfma_kernel(SkinnyLaunch a) {
+  constexpr int SB = 4;  // K steps per block
+  extern __shared__ float s_dyn[];  // [NW][NT][64][4]
+  if (a.router && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
+    shared_up_task<bf16_t, kPathMfma>(a.ex, blockIdx.x - a.router_wgs, s_dyn);
+    return;
+  }
+  const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
-  const int n0 = rb * rows_pb + wave * 16;
+  const int n0 = blockIdx.x * 16;
   const int J = a.K / 32;
-  const int j0 = (int)((long long)s * J / a.S), j1 = (int)((long long)(s + 1) * J / a.S);
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
   const bf16_t* wr = W + (size_t)(n0 + row < a.N ? n0 + row : a.N - 1) * a.K;
@@ -252,104 +299,120 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyLaunch a) {
   bool xok[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    int tok = nt * 16 + row;
+    const int tok = nt * 16 + row;
     xok[nt] = tok < a.M;
     xr[nt] = X + (size_t)(xok[nt] ? tok : 0) * a.K;
   }
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int j = j0; j < j1; j += U) {
-    u32x4 av[U], bv[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jj = j + u;
-      const bool ok = jj < j1;
-      const size_t off = (size_t)(jj * 4 + kq) * 8;
-      av[u] = ok ? ld128_stream(wr + off) : zero;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bv[u][nt] = (ok && xok[nt]) ? ld128(xr[nt] + off) : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                          __builtin_bit_cast(bf16x8, bv[u][nt]),
-                                                          acc[nt], 0, 0, 0);
-  }
+  mfma_kloop<NT, SB>(wr, n0 + row < a.N, xr, xok, kq, J, wave, nw, acc);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 4 * kq + i, t = nt * 16 + row;
-      if (n < a.N && t < a.M) emit(a, s, t, n, acc[nt][i]);
-    }
-  skinny_tail(a, rb, rows_pb, nrb);
+    for (int i = 0; i < 4; ++i) s_dyn[((wave * NT + nt) * 64 + lane) * 4 + i] = acc[nt][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NT * 256; idx += blockDim.x) {
+    const int nt = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += s_dyn[((w * NT + nt) * 64 + l) * 4 + i];
+    const int n = n0 + 4 * (l >> 4) + i, t = nt * 16 + (l & 15);
+    if (n < a.N && t < a.M) finish_value(a, t, n, v);
+  }
+  router_tail(a);
 }
 
 // ---- host side -----------------------------------------------------------
 
-int skinny_rows_per_block(int variant, int bf16, int M) {
-  (void)bf16;
-  (void)M;
-  if (variant == VAR_MFMA) return kNW * 16;
-  if (variant == VAR_SPLITK) return kNW * 4;
-  return kNW * 2;
+int skinny_rows_per_block(int variant, int router) {
+  if (variant == VAR_MFMA) return 16;
+  if (router || variant == VAR_SPLITK) return 4;
+  return 2;
 }
 
-// Enough workgroups to keep every CU streaming (about 4 per CU), but no
-// split thinner than two 1 KB loads per lane.
-int skinny_default_splits(int variant, int bf16, int M, int N, int K) {
-  const int rows_pb = skinny_rows_per_block(variant, bf16, M);
-  const int nrb = (N + rows_pb - 1) / rows_pb;
-  const int target = 1024;
-  int S = (target + nrb - 1) / nrb;
-  const int vec = bf16 ? 8 : 4;
-  const int chunks = K / vec;
-  int smax = chunks / (64 * 2);
-  if (variant == VAR_MFMA) smax = (K / 32) / 8;
-  if (smax < 1) smax = 1;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  return S;
+// Waves per workgroup (the in-workgroup K split): enough for ~1536 waves per
+// launch, at most 16, and no wave with less than one 1 KB block per row.
+// The router takes 16 waves outright: it has few rows, and each of its
+// workgroups pays one device-scope release on the completion counter.
+int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router) {
+  const int rows = skinny_rows_per_block(variant, router);
+  const int nwg = (N + rows - 1) / rows;
+  int nw = router ? 16 : (1536 + nwg - 1) / nwg;
+  int maxw = variant == VAR_MFMA ? (K / 32) / 4 : (K / (bf16 ? 8 : 4)) / 64;
+  if (maxw > (variant == VAR_MFMA ? 8 : 16)) maxw = variant == VAR_MFMA ? 8 : 16;
+  if (variant == VAR_MFMA) {
+    // dynamic LDS nw * nt KB plus the router's static LDS within 64 KB
+    const int nt = (M + 15) / 16;
+    if (maxw > 40 / nt) maxw = 40 / nt;
+  }
+  if (maxw < 1) maxw = 1;
+  if (nw > maxw) nw = maxw;
+  if (nw < 1) nw = 1;
+  return nw;
 }
 
-hipError_t launch_skinny(const SkinnyLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
-  const int rows_pb = skinny_rows_per_block(a.variant, a.bf16, a.M);
-  const int nrb = (a.N + rows_pb - 1) / rows_pb;
-  dim3 grid((unsigned)(nrb * a.S)), block(256);
+// Shared-expert gate/up workgroups appended to the router grid: the vector
+// shape takes one pair per wave, the MFMA shape four pairs per workgroup.
+int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
+  const bool mfma = expert_paths(ex.bf16, ex.force, ex.B) != kPathValu;
+  return mfma ? (ex.Is + kUpPairsMfma - 1) / kUpPairsMfma : (ex.Is + nw - 1) / nw;
+}
+
+hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
+  SkinnyLaunch a = a0;
+  const int rows = skinny_rows_per_block(a.variant, a.router);
+  const int nwg = (a.N + rows - 1) / rows;
+  const int nw = a.S;
+  a.router_wgs = nwg;
+  const int extra = (a.router && a.ex.Ws13) ? shared_up_tiles_host(a.ex, nw) : 0;
+  a.shared_tiles = extra;
+  dim3 grid((unsigned)(nwg + extra)), block((unsigned)(64 * nw));
   const char* name = "?";
   if (a.variant == VAR_MFMA) {
     const int nt = (a.M + 15) / 16;
+    const size_t lds = (size_t)nw * nt * 256 * sizeof(float);
     switch (nt) {
-      case 1: hipLaunchKernelGGL(skinny_mfma_kernel<1>, grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL(skinny_mfma_kernel<2>, grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL(skinny_mfma_kernel<3>, grid, block, 0, st, a); break;
-      default: hipLaunchKernelGGL(skinny_mfma_kernel<4>, grid, block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL(skinny_mfma_kernel<1>, grid, block, lds, st, a); break;
+      case 2: hipLaunchKernelGGL(skinny_mfma_kernel<2>, grid, block, lds, st, a); break;
+      case 3: hipLaunchKernelGGL(skinny_mfma_kernel<3>, grid, block, lds, st, a); break;
+      default: hipLaunchKernelGGL(skinny_mfma_kernel<4>, grid, block, lds, st, a); break;
     }
     name = "mfma";
+  } else if (a.router) {
+    name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
+    if (a.bf16) {
+      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 1, 4>), grid, block, 0, st, a);
+      else if (a.M <= 2) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 2, 4>), grid, block, 0, st, a);
+      else if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
+    } else {
+      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 1, 4>), grid, block, 0, st, a);
+      else if (a.M <= 2) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 2, 4>), grid, block, 0, st, a);
+      else if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
+    }
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {
-      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 4>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 8>), grid, block, 0, st, a);
+      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 4>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 8>), grid, block, 0, st, a);
+      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
     }
     name = "splitk";
   } else {
     if (a.bf16) {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 1>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 2>), grid, block, 0, st, a);
+      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 1, 4>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 2, 4>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 1>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 2>), grid, block, 0, st, a);
+      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 1, 4>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 2, 4>), grid, block, 0, st, a);
     }
     name = "gemv";
   }
-  if (desc) snprintf(desc, desc_len, "%s M=%d N=%d K=%d S=%d grid=%d", name, a.M, a.N, a.K, a.S, nrb * a.S);
+  if (desc)
+    snprintf(desc, desc_len, "%s M=%d N=%d K=%d waves/wg=%d grid=%d%s", name, a.M, a.N, a.K, nw, nwg,
+             extra ? " +shared gate/up" : "");
   return hipGetLastError();
 }
 
