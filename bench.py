@@ -17,9 +17,12 @@ Inputs are resident in HBM before the timed region.  W warm-up steps, then
 exactly K timed steps between two synchronised HIP events.
 
 Prints ONE JSON line.  Besides the headline, it carries
-  roofline:     the dominant kernel (expert gate/up) timed alone with HIP
-                events on its launch stream, algorithmic bytes / duration
-                against the 8 TB/s HBM peak;
+  roofline:     the dominant kernel (expert gate/up) timed with HIP events
+                that its own dispatch records (hipExtLaunchKernel, on the
+                launch stream), algorithmic bytes / duration against the
+                8 TB/s HBM peak; traffic = counter-measured HBM bytes per
+                launch from profiles/traffic.json while the kernels are
+                unchanged since it was taken;
   cpu_baseline: the CPU oracle timed on this host on a bounded sample of the
                 same workload.
 """
@@ -46,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="tp16_b1",
-                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense"])
+                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "copy"])
     ap.add_argument("--batch", type=int, default=1, help="dense workload batch")
     ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: enough to defeat caches)")
     ap.add_argument("--seed", type=int, default=0)
@@ -119,8 +122,9 @@ def run_moe(args, torch, mb, synth):
         bias_b = 0 if s["bias"] is None else s["bias"].numel() * 4
         b = cfg.E * cfg.d * esz + n * expert_bytes + shared_bytes + 2 * cfg.B * cfg.d * esz + bias_b
         per_set.append((n, b))
-        up_bytes.append((n * 2 * cfg.I + 2 * cfg.Is) * cfg.d * esz + cfg.B * cfg.d * esz
-                        + (cfg.B * cfg.k * cfg.I + cfg.B * cfg.Is) * 4)
+        # the gate/up launch streams the routed experts' gate/up rows (the
+        # shared expert's run inside the router launch), reads x and writes h
+        up_bytes.append(n * 2 * cfg.I * cfg.d * esz + cfg.B * cfg.d * esz + cfg.B * cfg.k * cfg.I * 4)
     avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
     kern = {}
@@ -132,7 +136,8 @@ def run_moe(args, torch, mb, synth):
     up_total = sum(up_bytes[i % R] for i in range(K2))
     achieved = up_total / (sum(durs) * 1e-3)  / 1e9            # GB/s
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=stored_traffic(cfg.name, "expert_up_kernel"),
                 kernel="expert_up_kernel", bytes_per_launch=round(up_total / K2),
                 avg_us=round(sum(durs) / K2 * 1e3, 3))
     us = ms * 1e3
@@ -172,7 +177,8 @@ def run_dense(args, torch, mb, synth):
     durs = kernel_times(step, mb.KERNEL_SKINNY, args, torch, mb)
     achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="skinny_kernel",
+                frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=stored_traffic("dense_b%d" % B, "skinny_kernel"), kernel="skinny_kernel",
                 bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
     us = ms * 1e3
     config = dict(workload="dense skinny GEMM (attention input projection): Y[%d x %d] = "
@@ -183,6 +189,50 @@ def run_dense(args, torch, mb, synth):
                   variant=mb.last_variant())
     cpu = None if args.no_cpu_baseline else cpu_baseline_dense(B, N, K, args)
     return us, ms, "bf16", config, roof, cpu
+
+
+# ---------------------------------------------------------------- copy
+
+def run_copy(args, torch):
+    """A plain device copy of known size (256 MiB), as the yardstick for the
+    HBM byte counters (FETCH_SIZE / WRITE_SIZE) and for achievable
+    bandwidth on this GPU: 2 x 256 MiB of compulsory traffic per copy."""
+    n = 256 << 20
+    R = 4
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(r) for r in range(R)]
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        dst.copy_(src[i % R])
+
+    ms = timed_loop(step, args, torch)
+    us = ms * 1e3
+    gbs = 2 * n / (us * 1e-6) / 1e9
+    config = dict(workload="device copy of 256 MiB (read + write)", bytes=2 * n, rotate=R,
+                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="copy")
+    return us, ms, "u8", config, roof, None
+
+
+# ---------------------------------------------------------------- traffic
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` measured by rocprofv3 counters
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a 256 MiB copy)
+    and stored in profiles/traffic.json, or None when the library sources have
+    changed since the counters were taken."""
+    from moe_block_skinny_amd import build as hip_build
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != hip_build.source_digest():
+        return None
+    k = t.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------- timing
@@ -278,7 +328,9 @@ def main():
     from moe_block_skinny_amd import synth
 
     torch.cuda.set_device(0)
-    if args.workload == "dense":
+    if args.workload == "copy":
+        us, ms, dtype, config, roof, cpu = run_copy(args, torch)
+    elif args.workload == "dense":
         us, ms, dtype, config, roof, cpu = run_dense(args, torch, mb, synth)
     else:
         us, ms, dtype, config, roof, cpu = run_moe(args, torch, mb, synth)

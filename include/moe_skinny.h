@@ -141,9 +141,10 @@ typedef enum {
 } moe_kernel_t;
 
 /* Profiling hook (for timing one kernel with HIP events on the stream it is
- * launched on): while armed, every launch of `kernel` is bracketed by
- * hipEventRecord(start_event) and hipEventRecord(stop_event) on the launch
- * stream.  Both NULL disarms.  Process-wide; not for concurrent use.
+ * launched on): while armed, every launch of `kernel` is dispatched with
+ * hipExtLaunchKernel so that the dispatch itself records start_event when
+ * the kernel starts and stop_event when it ends.  Both NULL disarms.
+ * Process-wide; not for concurrent use.
  * start_event / stop_event are hipEvent_t handles owned by the caller.
  * Returns MOE_EINVAL for an unknown kernel or only one NULL event. */
 moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event);

@@ -31,22 +31,16 @@ std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 constexpr int kMaxB = 64, kMaxE = 512, kMaxK = 16, kMaxI = 256;
 constexpr size_t kAlign = 256;
 
-// Profiling hook: events bracketing every launch of one kernel.
+// Profiling hook: events recorded by the dispatch of one kernel.
 struct ProfileHook {
   int kernel = -1;
   hipEvent_t start = nullptr, stop = nullptr;
 } g_prof;
 
-struct ProfileScope {
-  bool on;
-  hipStream_t st;
-  ProfileScope(int kernel, hipStream_t s) : on(g_prof.kernel == kernel), st(s) {
-    if (on) (void)hipEventRecord(g_prof.start, st);
-  }
-  ~ProfileScope() {
-    if (on) (void)hipEventRecord(g_prof.stop, st);
-  }
-};
+static_assert(K_ROUTE == MOE_KERNEL_ROUTE && K_EXPERT_UP == MOE_KERNEL_EXPERT_UP &&
+                  K_EXPERT_DOWN == MOE_KERNEL_EXPERT_DOWN && K_COMBINE == MOE_KERNEL_COMBINE &&
+                  K_SKINNY == MOE_KERNEL_SKINNY,
+              "kernel ids");
 
 moe_status_t fail(moe_status_t s, const char* fmt, ...) {
   va_list ap;
@@ -234,7 +228,6 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.topk_ids = ids;
   a.topk_w = w;
   a.plan = plan;
-  ProfileScope prof(MOE_KERNEL_ROUTE, st);
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
 }
 
@@ -270,12 +263,10 @@ moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, c
   char d1[128] = "", d2[128] = "";
   moe_status_t s;
   {
-    ProfileScope prof(MOE_KERNEL_EXPERT_UP, st);
     s = hip_status(launch_expert_up(a, st, d1, sizeof d1), "expert gate/up launch");
   }
   if (s) return s;
   {
-    ProfileScope prof(MOE_KERNEL_EXPERT_DOWN, st);
     s = hip_status(launch_expert_down(a, st, d2, sizeof d2), "expert down launch");
   }
   if (desc) snprintf(desc, dl, "%s; %s", d1, d2);
@@ -283,6 +274,13 @@ moe_status_t run_ffn(int dt, int B, int d, int E, int k, int I, const void* X, c
 }
 
 }  // namespace
+
+bool moe::profile_events_for(int id, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_prof.kernel != id) return false;
+  *start = g_prof.start;
+  *stop = g_prof.stop;
+  return true;
+}
 
 extern "C" {
 
@@ -385,7 +383,6 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   a.y_bf16 = y_dtype == MOE_DT_BF16;
   char desc[160];
   {
-    ProfileScope prof(MOE_KERNEL_SKINNY, reinterpret_cast<hipStream_t>(stream));
     s = hip_status(launch_skinny(a, reinterpret_cast<hipStream_t>(stream), desc, sizeof desc),
                    "skinny_gemm launch");
   }
@@ -462,7 +459,6 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
   a.topk_w = topk_w;
   a.out = out;
   {
-    ProfileScope prof(MOE_KERNEL_COMBINE, reinterpret_cast<hipStream_t>(stream));
     s = hip_status(launch_combine(a, reinterpret_cast<hipStream_t>(stream)), "moe_combine launch");
   }
   if (!s) record("moe_combine", B, "elementwise");
@@ -513,11 +509,9 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
                      st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
     return s;
   {
-    ProfileScope prof(MOE_KERNEL_EXPERT_UP, st);
     if ((s = hip_status(launch_expert_up(ex, st, d2, sizeof d2), "expert gate/up launch"))) return s;
   }
   {
-    ProfileScope prof(MOE_KERNEL_EXPERT_DOWN, st);
     if ((s = hip_status(launch_expert_down_combine(ex, st, d3, sizeof d3), "expert down+combine launch")))
       return s;
   }

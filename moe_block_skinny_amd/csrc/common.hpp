@@ -7,10 +7,10 @@
 // wait; the fix confined that load type to static weights):
 //   * only weights, which no kernel of the library ever writes, are read with
 //     plain or non-temporal loads;
-//   * anything produced inside the same launch by another workgroup
-//     (split-K partials, router logits) is read after an acquire fence with
-//     relaxed agent-scope atomic loads, which the compiler can neither hoist
-//     above the fence nor serve from a non-coherent cache.
+//   * anything produced inside the same launch by another workgroup (the
+//     router logits) is read only after the acquire fence of a completion
+//     counter (arrive_last), which the compiler cannot hoist a load above and
+//     which invalidates the non-coherent caches first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -94,40 +94,44 @@ __device__ __forceinline__ float dot_chunk_f32x(u32x4 w, const float* xs, float 
 
 // ---- wavefront reductions -------------------------------------------------
 
-// Sum over aligned groups of L lanes (L a power of two <= 64); every lane of
-// the group ends with the group's sum.  Butterfly order is fixed, so the
-// result is deterministic.
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < L; o <<= 1) v += __shfl_xor(v, o, kWave);
+// DPP move of a float (CTRL: a DPP lane-permutation control).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over each 16-lane row, left in every lane of the row: xor 1, xor 2
+// (quad permutes), then half-mirror and mirror, which pair the quads and the
+// half-rows once every quad is uniform.  Fixed order, so deterministic.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
   return v;
 }
 
-// 64-bit DPP move of both halves (CTRL: a DPP lane-permutation control).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Wave-wide max of a 64-bit key, returned uniformly to every lane: DPP
-// exchanges within each 16-lane row (xor 1, xor 2, half-mirror, mirror),
-// then the four row results are read out and compared.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
-  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
-                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+// Sum over aligned groups of L lanes (L = 16, 32 or 64), valid in every lane
+// of its group: DPP within rows, then the row sums are read out (readlane)
+// and added in fixed order.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v = row_sum16(v);
+  if constexpr (L == 16) {
+    return v;
+  } else if constexpr (L == 32) {
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+  } else {
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+  }
 }
 
 // ---- vector-ALU streaming core ---------------------------------------------
@@ -264,29 +268,47 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   return last;
 }
 
-// Coherent read of a value another workgroup of this launch produced.
-__device__ __forceinline__ float ld_shared_f32(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Read of a value another workgroup of this launch produced, by the last
+// workgroup after arrive_last's acquire fence.  A plain load: the fence keeps
+// the compiler from moving it above the synchronisation and has invalidated
+// the caches it could be served stale from.  (Device-scope atomic loads would
+// also be coherent, but this GPU serialises them: ~150 ns each.)
+__device__ __forceinline__ float ld_after_acquire(const float* p) { return *p; }
+
+// Orderable 32-bit key of a logit: larger key <=> larger value (finite
+// inputs; -0 is folded into +0 first), so equal keys are equal logits.
+// Every finite value maps above 0, which marks "no candidate".
+__device__ __forceinline__ uint32_t ord_key(float v) {
+  v = v + 0.0f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ int32_t ld_shared_i32(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Orderable key of a logit: larger key <=> larger value (finite inputs;
-// -0 is folded into +0 first), low word breaks ties toward the lower index.
-__device__ __forceinline__ uint64_t topk_key(float v, int idx) {
-  v = v + 0.0f;
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
+// Wave-wide max of a 32-bit key, uniform result: DPP within rows, then the
+// four row maxima by readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+  return mx(mx((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+            mx((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  return __uint_as_float(u);
-}
-__device__ __forceinline__ int key_index(uint64_t key) {
-  return (int)(0xffffffffu - (uint32_t)key);
+
+// Inclusive prefix sum over the 64 lanes of a wave (classic DPP scan:
+// row_shr 1, 2, 4, 8, then row_bcast15 and row_bcast31 carry row totals).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
 }
 
 __device__ __forceinline__ float silu(float z) {

@@ -158,10 +158,10 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
   if (g > kMaxResidentWG) g = kMaxResidentWG;
   if (g < 1) g = 1;
   const int paths = expert_paths(a.bf16, a.force, a.B);
-  if (!a.bf16) hipLaunchKernelGGL((expert_up_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathValu) hipLaunchKernelGGL((expert_up_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathMfma) hipLaunchKernelGGL((expert_up_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((expert_up_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
+  if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
+  else launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
   if (desc) snprintf(desc, desc_len, "up grid=%d%s force=%d", g, a.skip_shared ? " routed-only" : "", a.force);
   return hipGetLastError();
 }
@@ -172,10 +172,10 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
   if (g > kMaxResidentWG) g = kMaxResidentWG;
   if (g < 1) g = 1;
   const int paths = expert_paths(a.bf16, a.force, a.B);
-  if (!a.bf16) hipLaunchKernelGGL((expert_down_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathValu) hipLaunchKernelGGL((expert_down_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathMfma) hipLaunchKernelGGL((expert_down_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((expert_down_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
+  if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
+  else launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
   if (desc) snprintf(desc, desc_len, "down grid=%d force=%d", g, a.force);
   return hipGetLastError();
 }
@@ -188,10 +188,10 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, cha
   const size_t lds = (size_t)(a.B * a.k + a.B) * 16 * sizeof(float);
   const int paths = expert_paths(a.bf16, a.force, a.B);
   const dim3 grid(g), block(64 * nw);
-  if (!a.bf16) hipLaunchKernelGGL((expert_down_combine_kernel<float, kPathValu>), grid, block, lds, st, a);
-  else if (paths == kPathValu) hipLaunchKernelGGL((expert_down_combine_kernel<bf16_t, kPathValu>), grid, block, lds, st, a);
-  else if (paths == kPathMfma) hipLaunchKernelGGL((expert_down_combine_kernel<bf16_t, kPathMfma>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((expert_down_combine_kernel<bf16_t, kPathBoth>), grid, block, lds, st, a);
+  if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu>), grid, block, lds, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu>), grid, block, lds, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma>), grid, block, lds, st, a);
+  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth>), grid, block, lds, st, a);
   if (desc) snprintf(desc, desc_len, "down+combine grid=%d waves/wg=%d force=%d", g, nw, a.force);
   return hipGetLastError();
 }
@@ -201,7 +201,7 @@ hipError_t launch_combine(const CombineLaunch& a, hipStream_t st) {
   int g = (int)((n + 255) / 256);
   if (g > 4096) g = 4096;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, st, a);
+  launch(K_COMBINE, combine_kernel, dim3(g), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -210,7 +210,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   int g = (int)((words + 255) / 256);
   if (g > 4096) g = 4096;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(g), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), words);
+  launch(K_NONE, fill_zero_kernel, dim3(g), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // (abi.cpp) and the kernel translation units.  Not part of the public API.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -72,6 +73,24 @@ struct CombineLaunch {
   const float* topk_w;
   void* out;
 };
+
+// Kernel ids of the profiling hook (same values as the public moe_kernel_t).
+enum KernelId { K_ROUTE = 0, K_EXPERT_UP = 1, K_EXPERT_DOWN = 2, K_COMBINE = 3, K_SKINNY = 4, K_NONE = -1 };
+
+// Events armed for kernel `id` by moe_profile_events (abi.cpp), if any.
+bool profile_events_for(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch; when the profiling hook is armed for `id`, the dispatch itself
+// records the start and stop events (hipExtLaunchKernel), so the measured
+// interval is the kernel's own execution, as a kernel trace reports it.
+template <typename F, typename... Args>
+inline void launch(int id, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (id != K_NONE && profile_events_for(id, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 hipError_t launch_skinny(const SkinnyLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);

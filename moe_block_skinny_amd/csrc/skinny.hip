@@ -59,55 +59,45 @@ constexpr int kMaxK = 16;
 constexpr int kMaxB = 64;
 
 // One wave selects the top-k of one token from its logits lv (lane l holds
-// experts l, l+64, ...).  Keys order by fp32 logit, then by lower expert
-// index; k rounds of a wave-wide max each remove one winner.
+// experts l, l+64, ...).  Each of the k rounds takes the largest remaining
+// key (DPP max + readlane) and, among equal keys, the lowest expert index
+// (first ballot hit: lowest slot i, then lowest lane), and removes it.  Lane
+// j keeps the j-th winner, computes its softmax term, and finds its place in
+// ascending-id order from the other winners.
 __device__ __forceinline__ void topk_select(const SkinnyLaunch& a, int t, const float (&lv)[kMaxE / 64],
                                             int* s_ids) {
   const int lane = threadIdx.x & 63;
   const int E = a.N, k = a.k;
-  uint64_t key[kMaxE / 64];
+  uint32_t key[kMaxE / 64];
 #pragma unroll
-  for (int i = 0; i < kMaxE / 64; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? topk_key(lv[i], e) : 0ull;
-  }
-  int sel_e[kMaxK];
-  float sel_v[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    sel_e[j] = 0x7fffffff;
-    sel_v[j] = 0.f;
-    if (j < k) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = key_index(best);
-      sel_e[j] = e;
-      sel_v[j] = key_value(best);
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i)
-        if (lane + 64 * i == e) key[i] = 0ull;
-    }
-  }
-  // softmax over the selection; sel_v[0] is the largest selected logit
-  const float m = sel_v[0];
-  float z = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k) z += expf(sel_v[j] - m);
+  for (int i = 0; i < kMaxE / 64; ++i) key[i] = lane + 64 * i < E ? ord_key(lv[i]) : 0u;
   int my_e = 0x7fffffff;
-  float my_v = 0.f;
+  uint32_t my_key = 0u;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = key[0];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j == lane) { my_e = sel_e[j]; my_v = sel_v[j]; }
+    for (int i = 1; i < kMaxE / 64; ++i) lm = key[i] > lm ? key[i] : lm;
+    const uint32_t best = wave_max_u32(lm);
+    int win = -1;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i) {
+      const uint64_t bal = __ballot(key[i] == best);
+      if (win < 0 && bal) win = 64 * i + __ffsll((long long)bal) - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i)
+      if (lane + 64 * i == win) key[i] = 0u;
+    if (lane == j) { my_e = win; my_key = best; }
+  }
+  // softmax over the selection; winner 0 holds the largest logit
+  const float m = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+  const float ex = lane < k ? expf(key_value(my_key) - m) : 0.f;
+  const float z = group_sum<64>(ex);
+  int pos = 0;
+  for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(my_e, i) < my_e ? 1 : 0;
   if (lane < k) {
-    int pos = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k && sel_e[j] < my_e) ++pos;
     a.topk_ids[(size_t)t * k + pos] = my_e;
-    a.topk_w[(size_t)t * k + pos] = expf(my_v - m) / z;
+    a.topk_w[(size_t)t * k + pos] = ex / z;
     s_ids[t * k + pos] = my_e;
   }
 }
@@ -128,7 +118,7 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, int* s_ids) {
 #pragma unroll
       for (int i = 0; i < kMaxE / 64; ++i) {
         const int e = lane + 64 * i;
-        lv[q][i] = ld_shared_f32(&a.logits[(size_t)tc * E + (e < E ? e : E - 1)]);
+        lv[q][i] = ld_after_acquire(&a.logits[(size_t)tc * E + (e < E ? e : E - 1)]);
       }
     }
 #pragma unroll
@@ -152,32 +142,30 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   // bit t of s_mask[e] is set when token t selected expert e (B <= 64)
   for (int s = tid; s < nslot; s += blockDim.x) atomicOr(&s_mask[s_ids[s]], 1ull << (s / k));
   __syncthreads();
-  if (wave == 0) {
-    // exclusive prefix sums over experts of slot counts and of "is active"
-    int c[kMaxE / 64], act[kMaxE / 64], cs = 0, as = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxE / 64; ++i) {
-      int e = lane * (kMaxE / 64) + i;
-      c[i] = e < E ? __popcll(s_mask[e]) : 0;
-      act[i] = c[i] > 0;
-      cs += c[i];
-      as += act[i];
-    }
-    int ci = cs, ai = as;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int yc = __shfl_up(ci, o, 64), ya = __shfl_up(ai, o, 64);
-      if (lane >= o) { ci += yc; ai += ya; }
-    }
-    int ce = ci - cs, ae = ai - as;
-#pragma unroll
-    for (int i = 0; i < kMaxE / 64; ++i) {
-      int e = lane * (kMaxE / 64) + i;
-      if (e < E) { s_cnt[e] = ce; s_act[e] = ae; }
-      ce += c[i];
-      ae += act[i];
-    }
-    if (lane == 63) s_n = ai;
+  // exclusive prefix sums over experts of slot counts and of "is active",
+  // packed in one int (counts <= 1024 in the low half, actives <= 512 in
+  // the high half): a DPP scan per wave, wave totals through LDS.
+  __shared__ int s_wtot[16];
+  const int nwv = (E + 63) >> 6;
+  int incl = 0, packed = 0;
+  if (tid < nwv * 64) {
+    const int c = tid < E ? __popcll(s_mask[tid]) : 0;
+    packed = c | ((c > 0 ? 1 : 0) << 16);
+    incl = wave_incl_scan(packed);
+    if (lane == 63) s_wtot[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wtot[w];
+    const int ex = base + incl - packed;
+    s_cnt[tid] = ex & 0xffff;
+    s_act[tid] = ex >> 16;
+  }
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < nwv; ++w) tot += s_wtot[w];
+    s_n = tot >> 16;
   }
   __syncthreads();
   const int n = s_n;
@@ -335,9 +323,13 @@ int skinny_rows_per_block(int variant, int router) {
 // The router takes 16 waves outright: it has few rows, and each of its
 // workgroups pays one device-scope release on the completion counter.
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router) {
+  // The router's finish needs one thread per expert (E <= 512): its
+  // workgroups always have 16 waves (vector) or 8 (MFMA); waves beyond the
+  // K range just idle through the product.
+  if (router) return variant == VAR_MFMA ? 8 : 16;
   const int rows = skinny_rows_per_block(variant, router);
   const int nwg = (N + rows - 1) / rows;
-  int nw = router ? 16 : (1536 + nwg - 1) / nwg;
+  int nw = (1536 + nwg - 1) / nwg;
   int maxw = variant == VAR_MFMA ? (K / 32) / 4 : (K / (bf16 ? 8 : 4)) / 64;
   if (maxw > (variant == VAR_MFMA ? 8 : 16)) maxw = variant == VAR_MFMA ? 8 : 16;
   if (variant == VAR_MFMA) {
@@ -372,41 +364,41 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
     const int nt = (a.M + 15) / 16;
     const size_t lds = (size_t)nw * nt * 256 * sizeof(float);
     switch (nt) {
-      case 1: hipLaunchKernelGGL(skinny_mfma_kernel<1>, grid, block, lds, st, a); break;
-      case 2: hipLaunchKernelGGL(skinny_mfma_kernel<2>, grid, block, lds, st, a); break;
-      case 3: hipLaunchKernelGGL(skinny_mfma_kernel<3>, grid, block, lds, st, a); break;
-      default: hipLaunchKernelGGL(skinny_mfma_kernel<4>, grid, block, lds, st, a); break;
+      case 1: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<1>, grid, block, lds, st, a); break;
+      case 2: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<2>, grid, block, lds, st, a); break;
+      case 3: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<3>, grid, block, lds, st, a); break;
+      default: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<4>, grid, block, lds, st, a); break;
     }
     name = "mfma";
   } else if (a.router) {
     name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
     if (a.bf16) {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 1, 4>), grid, block, 0, st, a);
-      else if (a.M <= 2) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 2, 4>), grid, block, 0, st, a);
-      else if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 1, 4>), grid, block, 0, st, a);
+      else if (a.M <= 2) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 2, 4>), grid, block, 0, st, a);
+      else if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 1, 4>), grid, block, 0, st, a);
-      else if (a.M <= 2) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 2, 4>), grid, block, 0, st, a);
-      else if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 1, 4>), grid, block, 0, st, a);
+      else if (a.M <= 2) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 2, 4>), grid, block, 0, st, a);
+      else if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
     }
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {
-      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 4) hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
     }
     name = "splitk";
   } else {
     if (a.bf16) {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 1, 4>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<bf16_t, 2, 2, 4>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 2, 1, 4>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 2, 2, 4>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 1, 4>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((skinny_valu_kernel<float, 2, 2, 4>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 2, 1, 4>), grid, block, 0, st, a);
+      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 2, 2, 4>), grid, block, 0, st, a);
     }
     name = "gemv";
   }
