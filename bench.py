@@ -129,7 +129,7 @@ def run_moe(args, torch, mb, synth):
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
     kern = {}
     for name, kid in (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
-                      ("expert_down", mb.KERNEL_EXPERT_DOWN), ("combine", mb.KERNEL_COMBINE)):
+                      ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)):
         kern[name] = kernel_times(step, kid, args, torch, mb)
     durs = kern["expert_up"]
     K2 = len(durs)

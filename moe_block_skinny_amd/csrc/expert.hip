@@ -40,7 +40,6 @@
 
 namespace moe {
 
-constexpr int kUpPairs = 4;     // gate/up pairs per up task (4 waves)
 constexpr int kDownRows = 64;   // W2 rows per unfused down task (16 per wave)
 
 __device__ __forceinline__ int entries(const ExpertLaunch& a, const PlanView& p, bool with_shared) {
@@ -49,20 +48,35 @@ __device__ __forceinline__ int entries(const ExpertLaunch& a, const PlanView& p,
 
 // ---- gate/up + SwiGLU --------------------------------------------------------
 
+// Task = (entry, PPT pairs).  Vector-only instantiations: 4 waves, 2 pairs,
+// waves w and w + 2 take the two halves of d for pair w (more loads in
+// flight per pair at no register cost).  With MFMA entries: 8 waves, 4 pairs
+// (the 8-row A tile), split over d; their vector entries use 4 x 2 waves.
+template <int PATHS> struct UpShape {
+  static constexpr int kWaves = PATHS == kPathValu ? 4 : 8;
+  static constexpr int kPairs = kWaves / 2;
+};
+
 template <typename T, int PATHS>
-__global__ __launch_bounds__(256) void expert_up_kernel(ExpertLaunch a) {
+__global__ __launch_bounds__(UpShape<PATHS>::kWaves * 64) void expert_up_kernel(ExpertLaunch a) {
+  constexpr int PPT = UpShape<PATHS>::kPairs;
   __shared__ int32_t s_plan[kMaxPlanWords];
-  __shared__ float s_red[4 * 4 * 64 * 4];
+  __shared__ float s_red[PATHS == kPathValu ? PPT * 2 * 8 : 8 * 4 * 64 * 4];
   const PlanView p = stage_plan(a, s_plan);
-  const int tiles_r = (a.I + kUpPairs - 1) / kUpPairs;
-  const int tiles_s = (a.Is + kUpPairs - 1) / kUpPairs;
+  const int wave = threadIdx.x >> 6;
+  const int tiles_r = (a.I + PPT - 1) / PPT;
+  const int tiles_s = (a.Is + PPT - 1) / PPT;
   const int total = p.n * tiles_r + ((a.Ws13 && !a.skip_shared) ? tiles_s : 0);
   for (int task = blockIdx.x; task < total; task += gridDim.x) {
     const int e_idx = task < p.n * tiles_r ? task / tiles_r : p.n;
     const int tile = task < p.n * tiles_r ? task % tiles_r : task - p.n * tiles_r;
     const ExpertView v = expert_view<T>(a, p, e_idx);
-    if (use_mfma<PATHS>(v.m)) up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairs, s_red);
-    else up_valu_dispatch<T>(a, p.slots, v, tile * kUpPairs + (threadIdx.x >> 6));
+    if (use_mfma<PATHS>(v.m)) {
+      if constexpr (PATHS != kPathValu) up_mfma_dispatch<T>(a, p.slots, v, tile * PPT, s_red);
+    } else {
+      up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+    }
+    __syncthreads();  // s_red is reused by the next task
   }
 }
 
@@ -74,7 +88,7 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
   const PlanView p = stage_plan(a, s_plan);
   const int tiles = (a.d + kDownRows - 1) / kDownRows;
   const int total = entries(a, p, true) * tiles;
-  const YSink sink = {a.Yslot, 0, 0};
+  const YSink sink = {a.Yslot, 0, 0, 0};
   for (int task = blockIdx.x; task < total; task += gridDim.x) {
     const int e_idx = task / tiles, tile = task % tiles;
     const ExpertView v = expert_view<T>(a, p, e_idx);
@@ -96,24 +110,28 @@ __device__ __forceinline__ float combine_one(const float* w_t, int k, int has_sh
   return acc;
 }
 
-template <typename T, int PATHS>
-__global__ __launch_bounds__(512) void expert_down_combine_kernel(ExpertLaunch a) {
+// RT output rows per workgroup: 32 on the vector-only path with short rows
+// (I, Is <= 16 chunks: 8 loads per lane per entry, so the whole grid is
+// resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays
+// within 36 KB at B=64).
+template <typename T, int PATHS, int RT>
+__global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512) void expert_down_combine_kernel(ExpertLaunch a) {
   __shared__ int32_t s_plan[kMaxPlanWords];
-  extern __shared__ float s_y[];   // [B*k + B][16]
+  extern __shared__ float s_y[];   // [B*k + B][RT]
   const PlanView p = stage_plan(a, s_plan);
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * 16;
-  const YSink sink = {s_y, 1, r0};
+  const int r0 = blockIdx.x * RT;
+  const YSink sink = {s_y, 1, r0, RT};
   const int ne = entries(a, p, true);
   for (int e_idx = wave; e_idx < ne; e_idx += nw)
-    down_dispatch<T, PATHS>(a, p.slots, expert_view<T>(a, p, e_idx), r0, sink);
+    down_dispatch<T, PATHS, RT>(a, p.slots, expert_view<T>(a, p, e_idx), r0, sink);
   __syncthreads();
   const int has_shared = a.Ws13 ? 1 : 0;
-  for (int idx = threadIdx.x; idx < a.B * 16; idx += blockDim.x) {
-    const int t = idx >> 4, r = idx & 15;
+  for (int idx = threadIdx.x; idx < a.B * RT; idx += blockDim.x) {
+    const int t = idx / RT, r = idx % RT;
     if (r0 + r >= a.d) continue;
     const float v = combine_one(a.topk_w + (size_t)t * a.k, a.k, has_shared, [&](int j) {
-      return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * 16 + r];
+      return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * RT + r];
     });
     const size_t o = (size_t)t * a.d + r0 + r;
     if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[o] = f32_to_bf16(v);
@@ -151,17 +169,20 @@ static int max_entries(const ExpertLaunch& a) {
 static const int kMaxResidentWG = 256 * 8;
 
 hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
-  const int tiles_r = (a.I + kUpPairs - 1) / kUpPairs;
-  const int tiles_s = (a.Is + kUpPairs - 1) / kUpPairs;
+  const int paths = expert_paths(a.bf16, a.force, a.B);
+  const int ppt = paths == kPathValu ? UpShape<kPathValu>::kPairs : UpShape<kPathBoth>::kPairs;
+  const int threads = paths == kPathValu ? UpShape<kPathValu>::kWaves * 64 : UpShape<kPathBoth>::kWaves * 64;
+  const int tiles_r = (a.I + ppt - 1) / ppt;
+  const int tiles_s = (a.Is + ppt - 1) / ppt;
   const int nslot = a.B * a.k;
   int g = (nslot < a.E ? nslot : a.E) * tiles_r + ((a.Ws13 && !a.skip_shared) ? tiles_s : 0);
   if (g > kMaxResidentWG) g = kMaxResidentWG;
   if (g < 1) g = 1;
-  const int paths = expert_paths(a.bf16, a.force, a.B);
-  if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
-  else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
-  else launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
+  const dim3 grid(g), block(threads);
+  if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), grid, block, 0, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), grid, block, 0, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), grid, block, 0, st, a);
+  else launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathBoth>), grid, block, 0, st, a);
   if (desc) snprintf(desc, desc_len, "up grid=%d%s force=%d", g, a.skip_shared ? " routed-only" : "", a.force);
   return hipGetLastError();
 }
@@ -181,18 +202,24 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
 }
 
 hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
-  const int g = (a.d + 15) / 16;
-  int nw = max_entries(a);
-  if (nw > 8) nw = 8;
-  if (nw < 1) nw = 1;
-  const size_t lds = (size_t)(a.B * a.k + a.B) * 16 * sizeof(float);
   const int paths = expert_paths(a.bf16, a.force, a.B);
+  const int vec = a.bf16 ? 8 : 4;
+  const bool short_rows = a.I <= 16 * vec && (!a.Ws13 || a.Is <= 16 * vec);
+  const int rt = (paths == kPathValu && short_rows) ? 32 : 16;
+  const int g = (a.d + rt - 1) / rt;
+  int nw = max_entries(a);
+  const int maxw = paths == kPathValu ? 16 : 8;
+  if (nw > maxw) nw = maxw;
+  if (nw < 1) nw = 1;
+  const size_t lds = (size_t)(a.B * a.k + a.B) * rt * sizeof(float);
   const dim3 grid(g), block(64 * nw);
-  if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu>), grid, block, lds, st, a);
-  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu>), grid, block, lds, st, a);
-  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma>), grid, block, lds, st, a);
-  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth>), grid, block, lds, st, a);
-  if (desc) snprintf(desc, desc_len, "down+combine grid=%d waves/wg=%d force=%d", g, nw, a.force);
+  if (!a.bf16 && rt == 32) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 32>), grid, block, lds, st, a);
+  else if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 16>), grid, block, lds, st, a);
+  else if (paths == kPathValu && rt == 32) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 32>), grid, block, lds, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 16>), grid, block, lds, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16>), grid, block, lds, st, a);
+  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth, 16>), grid, block, lds, st, a);
+  if (desc) snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d force=%d", g, rt, nw, a.force);
   return hipGetLastError();
 }
 

@@ -128,17 +128,22 @@ __host__ __device__ __forceinline__ int expert_paths(int bf16, int force, int B)
 
 // ---- gate/up + SwiGLU ------------------------------------------------------
 
-// Wave `wave` takes pair i (gate row i, up row I+i) over all of d and writes
-// h[srow][i] for the entry's tokens.
-template <typename T, int MB>
-__device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i) {
+// Pair i (gate row i, up row I+i) of entry v: this wave takes the `half`-th
+// of NH slices of d; h[srow][i] = silu(g) * u for the entry's tokens.  With
+// NH = 2 the two waves of a pair meet in s_part ([4 pairs][2][MB] floats,
+// pair slot ps) and the whole workgroup passes one barrier; with NH = 1 a
+// wave works alone.  Waves whose pair is past I still reach the barrier.
+template <typename T, int MB, int NH>
+__device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i,
+                                        int half, int ps, float* s_part) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int U = MB <= 1 ? 8 : (MB <= 2 ? 4 : 2);
+  constexpr int U = MB <= 1 ? 8 / NH : (MB <= 2 ? 4 : 2);
   const int lane = threadIdx.x & 63;
-  if (i >= v.I) return;
+  const bool live = i < v.I;
   const T* W13 = reinterpret_cast<const T*>(v.W13);
   const T* X = reinterpret_cast<const T*>(a.X);
-  const T* wr[2] = {W13 + (size_t)i * a.d, W13 + (size_t)(v.I + i) * a.d};
+  const int ic = live ? i : 0;
+  const T* wr[2] = {W13 + (size_t)ic * a.d, W13 + (size_t)(v.I + ic) * a.d};
   const T* xr[MB];
   int srow[MB];
 #pragma unroll
@@ -148,9 +153,31 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
     xr[t] = X + (size_t)tok * a.d;
     srow[t] = sr;
   }
+  const int C = a.d / VEC;
   float acc[2][MB];
-  valu_dot<T, 2, MB, U>(wr, xr, v.m, 0, a.d / VEC, acc);
-  if (lane < v.m) {
+  if (live) {
+    valu_dot<T, 2, MB, U>(wr, xr, v.m, half * C / NH, (half + 1) * C / NH, acc);
+  } else {
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[0][t] = acc[1][t] = 0.f;
+  }
+  if constexpr (NH == 2) {
+    if (half == 1 && lane == 0) {
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        s_part[(ps * 2 + 0) * MB + t] = acc[0][t];
+        s_part[(ps * 2 + 1) * MB + t] = acc[1][t];
+      }
+    }
+    __syncthreads();
+    if (half == 1 || !live) return;
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      acc[0][t] += s_part[(ps * 2 + 0) * MB + t];
+      acc[1][t] += s_part[(ps * 2 + 1) * MB + t];
+    }
+  }
+  if (live && lane < v.m) {
     const float g = pick_lane<MB>(acc[0], lane), u = pick_lane<MB>(acc[1], lane);
     int sr = 0;
 #pragma unroll
@@ -160,13 +187,13 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
   }
 }
 
-template <typename T>
+template <typename T, int NH>
 __device__ __forceinline__ void up_valu_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
-                                                 int i) {
-  if (v.m <= 1) up_valu<T, 1>(a, slots, v, i);
-  else if (v.m <= 2) up_valu<T, 2>(a, slots, v, i);
-  else if (v.m <= 4) up_valu<T, 4>(a, slots, v, i);
-  else up_valu<T, 8>(a, slots, v, i);
+                                                 int i, int half, int ps, float* s_part) {
+  if (v.m <= 1) up_valu<T, 1, NH>(a, slots, v, i, half, ps, s_part);
+  else if (v.m <= 2) up_valu<T, 2, NH>(a, slots, v, i, half, ps, s_part);
+  else if (v.m <= 4) up_valu<T, 4, NH>(a, slots, v, i, half, ps, s_part);
+  else up_valu<T, 8, NH>(a, slots, v, i, half, ps, s_part);
 }
 
 // Pairs i0..i0+3 with the whole workgroup: lanes with row%16 in 0..3 load
@@ -234,25 +261,33 @@ __device__ __forceinline__ void up_mfma_dispatch(const ExpertLaunch& a, const in
 }
 
 // Shared-expert gate/up tile `tile` with the whole workgroup (nw waves):
-// the vector shape takes nw pairs (one per wave), the MFMA shape 4 pairs.
+// the vector shape takes nw/2 pairs, each split over two waves into the same
+// two halves of d as the gate/up kernel (so both give identical bits), the
+// MFMA shape 4 pairs.  s_red: the caller's LDS scratch (vector: nw floats *
+// 8 tokens; MFMA: nw * NT KB).
 template <typename T, int PATHS>
 __device__ __forceinline__ void shared_up_task(const ExpertLaunch& a, int tile, float* s_red) {
   const ExpertView v = shared_view(a);
-  const int nw = blockDim.x >> 6;
-  if (use_mfma<PATHS>(v.m)) up_mfma_dispatch<T>(a, nullptr, v, tile * kUpPairsMfma, s_red);
-  else up_valu_dispatch<T>(a, nullptr, v, tile * nw + (threadIdx.x >> 6));
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  if (use_mfma<PATHS>(v.m)) {
+    up_mfma_dispatch<T>(a, nullptr, v, tile * kUpPairsMfma, s_red);
+  } else {
+    const int pp = nw >> 1;
+    up_valu_dispatch<T, 2>(a, nullptr, v, tile * pp + wave % pp, wave / pp, wave % pp, s_red);
+  }
 }
 
 // ---- down projection ---------------------------------------------------------
 
-// Destination of the per-slot outputs of one 16-row tile: either the global
-// Yslot [B][k+1][d] or an LDS tile [B*k + B][16].
+// Destination of the per-slot outputs of one row tile: either the global
+// Yslot [B][k+1][d] or an LDS tile [B*k + B][rt].
 struct YSink {
   float* base;
-  int lds;       // 1: LDS tile rows of 16, else global Yslot
+  int lds;       // 1: LDS tile, rows of rt floats; 0: global Yslot
   int r0;        // first row of the tile (LDS)
+  int rt;        // rows per LDS tile
   __device__ __forceinline__ float* at(const ExpertLaunch& a, int srow, int row) const {
-    if (lds) return base + srow * 16 + (row - r0);
+    if (lds) return base + srow * rt + (row - r0);
     int t, j;
     if (srow < a.B * a.k) { t = srow / a.k; j = srow % a.k; }
     else { t = srow - a.B * a.k; j = a.k; }
@@ -260,14 +295,14 @@ struct YSink {
   }
 };
 
-// Rows r0..r0+15 of entry v with one wave: L lanes per W2 row (L*VEC >= I),
-// P = 64/L rows per load instruction, R = 16/P rows per lane.
-template <typename T, int L>
+// Rows r0..r0+ROWS-1 of entry v with one wave: L lanes per W2 row
+// (L*VEC >= I), P = 64/L rows per load instruction, R = ROWS/P rows per lane.
+template <typename T, int L, int ROWS>
 __device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
                           const YSink& sink) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int P = 64 / L;
-  constexpr int R = 16 / P;
+  constexpr int R = ROWS / P;
   const int lane = threadIdx.x & 63;
   const int c = lane % L, g = lane / L;
   const bool cok = c * VEC < v.I;
@@ -361,9 +396,11 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   }
 }
 
-template <typename T, int PATHS>
+// Rows r0..r0+ROWS-1 of entry v with one wave (the MFMA shape covers 16).
+template <typename T, int PATHS, int ROWS = 16>
 __device__ __forceinline__ void down_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
                                               int r0, const YSink& sink) {
+  static_assert(ROWS == 16 || PATHS == kPathValu, "the MFMA down shape covers 16 rows");
   if (use_mfma<PATHS>(v.m)) {
     if constexpr (sizeof(T) == 2) {
       const int nt = (v.m + 15) / 16;
@@ -375,9 +412,13 @@ __device__ __forceinline__ void down_dispatch(const ExpertLaunch& a, const int32
   } else {
     constexpr int VEC = Elem<T>::VEC;
     const int chunks = v.I / VEC;
-    if (chunks <= 16) down_valu<T, 16>(a, slots, v, r0, sink);
-    else if (chunks <= 32 || sizeof(T) == 2) down_valu<T, 32>(a, slots, v, r0, sink);
-    else if constexpr (sizeof(T) == 4) down_valu<T, 64>(a, slots, v, r0, sink);
+    if constexpr (ROWS > 16) {
+      down_valu<T, 16, ROWS>(a, slots, v, r0, sink);  // host guarantees I <= 16 * VEC
+    } else {
+      if (chunks <= 16) down_valu<T, 16, ROWS>(a, slots, v, r0, sink);
+      else if (chunks <= 32 || sizeof(T) == 2) down_valu<T, 32, ROWS>(a, slots, v, r0, sink);
+      else if constexpr (sizeof(T) == 4) down_valu<T, 64, ROWS>(a, slots, v, r0, sink);
+    }
   }
 }
 

@@ -58,72 +58,110 @@ constexpr int kMaxE = 512;
 constexpr int kMaxK = 16;
 constexpr int kMaxB = 64;
 
-// One wave selects the top-k of one token from its logits lv (lane l holds
-// experts l, l+64, ...).  Each of the k rounds takes the largest remaining
-// key (DPP max + readlane) and, among equal keys, the lowest expert index
-// (first ballot hit: lowest slot i, then lowest lane), and removes it.  Lane
-// j keeps the j-th winner, computes its softmax term, and finds its place in
-// ascending-id order from the other winners.
-__device__ __forceinline__ void topk_select(const SkinnyLaunch& a, int t, const float (&lv)[kMaxE / 64],
-                                            int* s_ids) {
+// One wave selects the top-k of QB tokens at once (their selection chains
+// are independent, so interleaving them fills the issue slots a single
+// chain leaves idle).  For token q, lane l holds the keys of experts
+// l, l+64, ...  Each of the k rounds takes the largest remaining key (DPP max
+// + readlane); its expert is the lowest index holding that key: the first
+// matching slot in each lane, then the lane itself when only one lane
+// matches (the usual case), else the smallest such expert over the wave.
+// Lane j keeps the j-th winner, computes its softmax term, and finds its
+// place in ascending-id order from the other winners.
+template <int QB>
+__device__ __forceinline__ void topk_select(const SkinnyLaunch& a, const int (&tq)[QB],
+                                            const float (&lv)[QB][kMaxE / 64], int* s_ids) {
+  constexpr int NI = kMaxE / 64;
   const int lane = threadIdx.x & 63;
-  const int E = a.N, k = a.k;
-  uint32_t key[kMaxE / 64];
+  const int E = a.N, k = a.k, M = a.M;
+  uint32_t key[QB][NI];
+  int my_e[QB];
+  uint32_t my_key[QB];
 #pragma unroll
-  for (int i = 0; i < kMaxE / 64; ++i) key[i] = lane + 64 * i < E ? ord_key(lv[i]) : 0u;
-  int my_e = 0x7fffffff;
-  uint32_t my_key = 0u;
-  for (int j = 0; j < k; ++j) {
-    uint32_t lm = key[0];
+  for (int q = 0; q < QB; ++q) {
 #pragma unroll
-    for (int i = 1; i < kMaxE / 64; ++i) lm = key[i] > lm ? key[i] : lm;
-    const uint32_t best = wave_max_u32(lm);
-    int win = -1;
-#pragma unroll
-    for (int i = 0; i < kMaxE / 64; ++i) {
-      const uint64_t bal = __ballot(key[i] == best);
-      if (win < 0 && bal) win = 64 * i + __ffsll((long long)bal) - 1;
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxE / 64; ++i)
-      if (lane + 64 * i == win) key[i] = 0u;
-    if (lane == j) { my_e = win; my_key = best; }
+    for (int i = 0; i < NI; ++i) key[q][i] = (tq[q] < M && lane + 64 * i < E) ? ord_key(lv[q][i]) : 0u;
+    my_e[q] = 0x7fffffff;
+    my_key[q] = 0u;
   }
-  // softmax over the selection; winner 0 holds the largest logit
-  const float m = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
-  const float ex = lane < k ? expf(key_value(my_key) - m) : 0.f;
-  const float z = group_sum<64>(ex);
-  int pos = 0;
-  for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(my_e, i) < my_e ? 1 : 0;
-  if (lane < k) {
-    a.topk_ids[(size_t)t * k + pos] = my_e;
-    a.topk_w[(size_t)t * k + pos] = ex / z;
-    s_ids[t * k + pos] = my_e;
+  for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (tq[q] >= M) continue;
+      uint32_t lm = key[q][0];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) lm = key[q][i] > lm ? key[q][i] : lm;
+      const uint32_t best = wave_max_u32(lm);
+      int slot = NI;  // first slot of this lane holding best
+#pragma unroll
+      for (int i = NI - 1; i >= 0; --i) slot = key[q][i] == best ? i : slot;
+      const int e_here = slot < NI ? lane + 64 * slot : 0x7fffffff;
+      const uint64_t bal = __ballot(slot < NI);
+      int win;
+      if (__popcll(bal) == 1) {
+        win = __builtin_amdgcn_readlane(e_here, __ffsll((long long)bal) - 1);
+      } else {  // equal keys in several lanes: lowest expert index wins
+        int v = e_here;
+        auto mn = [](int x, int y) { return x < y ? x : y; };
+        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false));
+        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false));
+        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false));
+        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, false));
+        win = mn(mn(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                 mn(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (lane + 64 * i == win) key[q][i] = 0u;
+      if (lane == j) { my_e[q] = win; my_key[q] = best; }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if (tq[q] >= M) continue;
+    const int t = tq[q];
+    // softmax over the selection; winner 0 holds the largest logit
+    const float m = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key[q], 0));
+    const float ex = lane < k ? expf(key_value(my_key[q]) - m) : 0.f;
+    const float z = group_sum<64>(ex);
+    int pos = 0;
+    for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(my_e[q], i) < my_e[q] ? 1 : 0;
+    if (lane < k) {
+      a.topk_ids[(size_t)t * k + pos] = my_e[q];
+      a.topk_w[(size_t)t * k + pos] = ex / z;
+      s_ids[t * k + pos] = my_e[q];
+    }
   }
 }
 
-// The wave's tokens t = wave, wave + nw, ... in batches of four: all logit
-// loads of a batch are issued (clamped addresses, no branches) before any is
-// used, so a batch costs one memory round trip.
+// The wave's tokens t = wave, wave + nw, ... in groups of four: all logit
+// loads of a group are issued (clamped addresses, no branches) before any is
+// used, so a group costs one memory round trip, and its four selections run
+// interleaved.
 __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, int* s_ids) {
   constexpr int QB = 4;
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.N, M = a.M;
   for (int t0 = wave; t0 < M; t0 += nw * QB) {
     float lv[QB][kMaxE / 64];
+    int tq[QB];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      const int t = t0 + nw * q;
-      const int tc = t < M ? t : M - 1;
+      tq[q] = t0 + nw * q;
+      const int tc = tq[q] < M ? tq[q] : M - 1;
 #pragma unroll
       for (int i = 0; i < kMaxE / 64; ++i) {
         const int e = lane + 64 * i;
         lv[q][i] = ld_after_acquire(&a.logits[(size_t)tc * E + (e < E ? e : E - 1)]);
       }
     }
+    if (tq[1] < M) topk_select<QB>(a, tq, lv, s_ids);
+    else {  // a lone token: skip the idle chains
+      const int t1[1] = {tq[0]};
+      float l1[1][kMaxE / 64];
 #pragma unroll
-    for (int q = 0; q < QB; ++q)
-      if (t0 + nw * q < M) topk_select(a, t0 + nw * q, lv[q], s_ids);
+      for (int i = 0; i < kMaxE / 64; ++i) l1[0][i] = lv[0][i];
+      topk_select<1>(a, t1, l1, s_ids);
+    }
   }
 }
 
@@ -203,7 +241,7 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   constexpr int VEC = Elem<T>::VEC;
   __shared__ float s_red[16 * RB * MB];
   if (a.router && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
-    shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, nullptr);
+    shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, s_red);
     return;
   }
   const int nw = blockDim.x >> 6;
@@ -347,7 +385,8 @@ int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router
 // shape takes one pair per wave, the MFMA shape four pairs per workgroup.
 int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
   const bool mfma = expert_paths(ex.bf16, ex.force, ex.B) != kPathValu;
-  return mfma ? (ex.Is + kUpPairsMfma - 1) / kUpPairsMfma : (ex.Is + nw - 1) / nw;
+  const int pp = nw / 2;
+  return mfma ? (ex.Is + kUpPairsMfma - 1) / kUpPairsMfma : (ex.Is + pp - 1) / pp;
 }
 
 hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
