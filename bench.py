@@ -116,30 +116,30 @@ def run_moe(args, torch, mb, synth):
     # algorithmic bytes per set: every selected expert's weights once, the
     # router and shared expert, x (and bias) read once, out written once
     per_set = []
-    up_bytes = []
     for s in sets:
         n = int(torch.unique(s["ids"]).numel())
         bias_b = 0 if s["bias"] is None else s["bias"].numel() * 4
         b = cfg.E * cfg.d * esz + n * expert_bytes + shared_bytes + 2 * cfg.B * cfg.d * esz + bias_b
-        per_set.append((n, b))
-        # the gate/up launch streams the routed experts' gate/up rows (the
-        # shared expert's run inside the router launch), reads x and writes h
-        up_bytes.append(n * 2 * cfg.I * cfg.d * esz + cfg.B * cfg.d * esz + cfg.B * cfg.k * cfg.I * 4)
+        per_set.append((n, b, launch_bytes(cfg, n, esz, bias_b)))
     avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
-    kern = {}
+    kern, kbytes = {}, {}
     for name, kid in (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
                       ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)):
         kern[name] = kernel_times(step, kid, args, torch, mb)
-    durs = kern["expert_up"]
-    K2 = len(durs)
-    up_total = sum(up_bytes[i % R] for i in range(K2))
-    achieved = up_total / (sum(durs) * 1e-3)  / 1e9            # GB/s
+        # the profiled launches run sets warmup + steps + i (see kernel_times)
+        kbytes[name] = [per_set[(args.warmup + args.steps + i) % R][2][name] for i in range(len(kern[name]))]
+    # the dominant kernel: the largest share of the block's time
+    dom = max(kern, key=lambda k: sum(kern[k]))
+    durs = kern[dom]
+    achieved = sum(kbytes[dom]) / (sum(durs) * 1e-3) / 1e9         # GB/s
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=stored_traffic(cfg.name, "expert_up_kernel"),
-                kernel="expert_up_kernel", bytes_per_launch=round(up_total / K2),
-                avg_us=round(sum(durs) / K2 * 1e3, 3))
+                traffic=stored_traffic(cfg.name, dom),
+                kernel=KERNEL_SYMBOL[dom], bytes_per_launch=round(sum(kbytes[dom]) / len(durs)),
+                avg_us=round(sum(durs) / len(durs) * 1e3, 3))
+    per_kernel = {k: dict(us=round(sum(v) / len(v) * 1e3, 3),
+                          gbs=round(sum(kbytes[k]) / (sum(v) * 1e-3) / 1e9, 1)) for k, v in kern.items()}
     us = ms * 1e3
     gbs = avg_bytes / (us * 1e-6) / 1e9
     config = dict(workload="%s: decode MoE block, one TP weight shard, B=%d, d=%d, E=%d, top-%d, "
@@ -148,10 +148,31 @@ def run_moe(args, torch, mb, synth):
                   B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is, rotate=R,
                   distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
                   gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
-                  kernels_us={k: round(sum(v) / len(v) * 1e3, 3) for k, v in kern.items()},
+                  kernels=per_kernel,
                   variant=mb.last_variant())
     cpu = None if args.no_cpu_baseline else cpu_baseline_moe(cfg, args)
     return us, ms, cfg.dtype, config, roof, cpu
+
+
+# symbol (as a kernel trace names it) of each launch of the block
+KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel (router mode)", "expert_up": "expert_up_kernel",
+                 "expert_down_combine": "expert_down_combine_kernel"}
+
+
+def launch_bytes(cfg, n, esz, bias_b):
+    """Algorithmic HBM bytes of each launch of the block, for n distinct
+    routed experts: the weights it streams (once), the activations it must
+    read and the results it must write.  Workspace traffic between launches
+    (h, fp32) is counted as the producer's output and the consumer's input;
+    the router's logits, the completion counter and the plan are not."""
+    B, d, E, k, I, Is = cfg.B, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is
+    x = B * d * esz
+    route = E * d * esz + x + bias_b + B * k * 8 + (2 * Is * d * esz + B * Is * 4 if Is else 0)
+    up = n * 2 * I * d * esz + x + B * k * I * 4
+    down = n * d * I * esz + B * k * I * 4 + B * k * 4 + B * d * esz
+    if Is:
+        down += d * Is * esz + B * Is * 4
+    return {"route": route, "expert_up": up, "expert_down_combine": down}
 
 
 # ---------------------------------------------------------------- dense
@@ -178,7 +199,8 @@ def run_dense(args, torch, mb, synth):
     achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=stored_traffic("dense_b%d" % B, "skinny_kernel"), kernel="skinny_kernel",
+                traffic=stored_traffic("dense_b%d" % B, "skinny_gemm"),
+                kernel="skinny_valu_kernel / skinny_mfma_kernel",
                 bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
     us = ms * 1e3
     config = dict(workload="dense skinny GEMM (attention input projection): Y[%d x %d] = "
@@ -217,8 +239,8 @@ def run_copy(args, torch):
 
 # ---------------------------------------------------------------- traffic
 
-def stored_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` measured by rocprofv3 counters
+def stored_traffic(workload, launch):
+    """HBM bytes per launch of `launch` (route, expert_up, ...) measured by rocprofv3 counters
     (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a 256 MiB copy)
     and stored in profiles/traffic.json, or None when the library sources have
     changed since the counters were taken."""
@@ -231,7 +253,7 @@ def stored_traffic(workload, kernel):
         return None
     if t.get("source_digest") != hip_build.source_digest():
         return None
-    k = t.get("workloads", {}).get(workload, {}).get(kernel)
+    k = t.get("workloads", {}).get(workload, {}).get(launch)
     return None if k is None else k.get("bytes_per_launch")
 
 

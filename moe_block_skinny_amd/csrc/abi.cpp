@@ -28,7 +28,7 @@ thread_local char g_err[512] = "";
 thread_local char g_variant[256] = "";
 std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 
-constexpr int kMaxB = 64, kMaxE = 512, kMaxK = 16, kMaxI = 256;
+constexpr int kMaxI = 256;   // kMaxB, kMaxE, kMaxK: route_core.hpp
 constexpr size_t kAlign = 256;
 
 // Profiling hook: events recorded by the dispatch of one kernel.
@@ -202,7 +202,7 @@ moe_status_t hip_status(hipError_t e, const char* what) {
 moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
                        const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
                        float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
-                       const ExpertLaunch* shared = nullptr) {
+                       const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr) {
   const int bf16 = dt == MOE_DT_BF16;
   int v;
   moe_status_t s = resolve_skinny(bf16, B, d, &v);
@@ -218,6 +218,7 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.variant = v;
   a.S = skinny_default_splits(v, bf16, B, E, d, 1);
   a.router = 1;
+  a.finish = finish;
   if (shared) a.ex = *shared;
   a.bias = bias;
   a.bias_ld = bias_ld;
@@ -228,6 +229,7 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.topk_ids = ids;
   a.topk_w = w;
   a.plan = plan;
+  if (logits) *logits = a.logits;
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
 }
 
@@ -497,17 +499,30 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   ex.topk_w = tw;
   ex.out = out;
   ex.out_bf16 = bf16;
-  // The shared expert's gate/up needs no routing, so it runs inside the
-  // router launch when both take the same kernel family (vector or MFMA).
-  // The router kernel's shape family must match the shared expert's: the
-  // vector router kernel carries only the vector gate/up, the MFMA one only
-  // the MFMA gate/up.
+  // Two schedules.  Small batch on the vector shape (B*k <= 64): the router
+  // launch only scores; the gate/up launch selects the top-k and builds the
+  // plan in every workgroup (no cross-workgroup handshake) and runs the
+  // shared expert's gate/up first.  Otherwise the router's last workgroup
+  // selects and plans, and the shared expert's gate/up runs inside the
+  // router launch when both take the same kernel family (the vector router
+  // kernel carries only the vector gate/up, the MFMA one only the MFMA one).
   const int paths = expert_paths(bf16, force, B);
-  ex.skip_shared = Ws13 && (paths == kPathValu ? v != VAR_MFMA : v == VAR_MFMA);
+  const bool route_in_up = paths == kPathValu && v != VAR_MFMA && B * k <= 64;
   char d1[200] = "", d2[128] = "", d3[128] = "";
-  if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
-                     st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
-    return s;
+  if (route_in_up) {
+    ex.skip_shared = 0;
+    ex.ids_out = ids;
+    ex.w_out = tw;
+    ex.plan_out = plan;
+    if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, st, d1,
+                       sizeof d1, nullptr, 0, &ex.logits)))
+      return s;
+  } else {
+    ex.skip_shared = Ws13 && (paths == kPathValu ? v != VAR_MFMA : v == VAR_MFMA);
+    if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
+                       st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
+      return s;
+  }
   {
     if ((s = hip_status(launch_expert_up(ex, st, d2, sizeof d2), "expert gate/up launch"))) return s;
   }

@@ -62,15 +62,39 @@ __global__ __launch_bounds__(UpShape<PATHS>::kWaves * 64) void expert_up_kernel(
   constexpr int PPT = UpShape<PATHS>::kPairs;
   __shared__ int32_t s_plan[kMaxPlanWords];
   __shared__ float s_red[PATHS == kPathValu ? PPT * 2 * 8 : 8 * 4 * 64 * 4];
-  const PlanView p = stage_plan(a, s_plan);
   const int wave = threadIdx.x >> 6;
   const int tiles_r = (a.I + PPT - 1) / PPT;
-  const int tiles_s = (a.Is + PPT - 1) / PPT;
-  const int total = p.n * tiles_r + ((a.Ws13 && !a.skip_shared) ? tiles_s : 0);
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int e_idx = task < p.n * tiles_r ? task / tiles_r : p.n;
-    const int tile = task < p.n * tiles_r ? task % tiles_r : task - p.n * tiles_r;
-    const ExpertView v = expert_view<T>(a, p, e_idx);
+  const int tiles_s = (a.Ws13 && !a.skip_shared) ? (a.Is + PPT - 1) / PPT : 0;
+  // Tasks: with routing here (vector shape only), the shared expert's tiles
+  // first -- they need no plan and keep HBM busy while the routed
+  // workgroups select -- then the routed tiles; otherwise the routed tiles,
+  // then the shared ones.
+  const bool here = PATHS == kPathValu && a.logits != nullptr;
+  PlanView p;
+  int task0 = blockIdx.x;
+  if constexpr (PATHS == kPathValu) {
+    if (here) {
+      for (; task0 < tiles_s; task0 += gridDim.x) {
+        up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+        __syncthreads();
+      }
+      __shared__ TopkScratch s_tk[UpShape<PATHS>::kWaves];
+      __shared__ int32_t s_ids[64];
+      __shared__ float s_w[64];
+      p = route_here(a, s_plan, s_tk, s_ids, s_w);
+    } else {
+      p = stage_plan(a, s_plan);
+    }
+  } else {
+    p = stage_plan(a, s_plan);
+  }
+  const int first = here ? tiles_s : 0;                    // first routed task
+  const int total = first + p.n * tiles_r + (here ? 0 : tiles_s);
+  for (int task = task0; task < total; task += gridDim.x) {
+    const int rt = task - first;
+    const bool routed = rt < p.n * tiles_r;
+    const ExpertView v = routed ? expert_view<T>(a, p, rt / tiles_r) : shared_view(a);
+    const int tile = routed ? rt % tiles_r : rt - p.n * tiles_r;
     if (use_mfma<PATHS>(v.m)) {
       if constexpr (PATHS != kPathValu) up_mfma_dispatch<T>(a, p.slots, v, tile * PPT, s_red);
     } else {
@@ -117,8 +141,10 @@ __device__ __forceinline__ float combine_one(const float* w_t, int k, int has_sh
 template <typename T, int PATHS, int RT>
 __global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512) void expert_down_combine_kernel(ExpertLaunch a) {
   __shared__ int32_t s_plan[kMaxPlanWords];
+  __shared__ float s_tw[kMaxB * kMaxK];
   extern __shared__ float s_y[];   // [B*k + B][RT]
-  const PlanView p = stage_plan(a, s_plan);
+  for (int i = threadIdx.x; i < a.B * a.k; i += blockDim.x) s_tw[i] = a.topk_w[i];
+  const PlanView p = stage_plan(a, s_plan);   // its barrier also covers s_tw
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * RT;
   const YSink sink = {s_y, 1, r0, RT};
@@ -130,7 +156,7 @@ __global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512) void expert_down_c
   for (int idx = threadIdx.x; idx < a.B * RT; idx += blockDim.x) {
     const int t = idx / RT, r = idx % RT;
     if (r0 + r >= a.d) continue;
-    const float v = combine_one(a.topk_w + (size_t)t * a.k, a.k, has_shared, [&](int j) {
+    const float v = combine_one(s_tw + t * a.k, a.k, has_shared, [&](int j) {
       return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * RT + r];
     });
     const size_t o = (size_t)t * a.d + r0 + r;
@@ -176,14 +202,19 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
   const int tiles_s = (a.Is + ppt - 1) / ppt;
   const int nslot = a.B * a.k;
   int g = (nslot < a.E ? nslot : a.E) * tiles_r + ((a.Ws13 && !a.skip_shared) ? tiles_s : 0);
-  if (g > kMaxResidentWG) g = kMaxResidentWG;
+  // the whole grid resident at once (vector shape: 4 workgroups per CU), so
+  // no workgroup stages the plan, or selects, after others have finished
+  const int cap = paths == kPathValu ? 4 * 256 : kMaxResidentWG;
+  if (g > cap) g = cap;
   if (g < 1) g = 1;
   const dim3 grid(g), block(threads);
   if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), grid, block, 0, st, a);
   else launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathBoth>), grid, block, 0, st, a);
-  if (desc) snprintf(desc, desc_len, "up grid=%d%s force=%d", g, a.skip_shared ? " routed-only" : "", a.force);
+  if (desc)
+    snprintf(desc, desc_len, "up grid=%d%s%s force=%d", g, a.skip_shared ? " routed-only" : "",
+             a.logits ? " +top-k/plan" : "", a.force);
   return hipGetLastError();
 }
 

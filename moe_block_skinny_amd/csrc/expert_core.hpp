@@ -19,6 +19,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "route_core.hpp"
 
 namespace moe {
 
@@ -33,6 +34,19 @@ struct PlanView {
   const int32_t* slots;
 };
 
+// View of a plan held in LDS.
+__device__ __forceinline__ PlanView plan_view(const ExpertLaunch& a, const int32_t* s_plan) {
+  const int nslot = a.B * a.k;
+  const int maxa = nslot < a.E ? nslot : a.E;
+  PlanView p;
+  p.maxa = maxa;
+  p.n = s_plan[0];
+  p.active = s_plan + 1;
+  p.offs = s_plan + 1 + maxa;
+  p.slots = s_plan + 2 + 2 * maxa;
+  return p;
+}
+
 // Copy the plan into LDS with the whole workgroup (one coalesced pass) and
 // return a view of it.  Ends with a barrier.
 __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s_plan) {
@@ -41,13 +55,40 @@ __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s
   const int words = 2 + 2 * maxa + nslot;
   for (int i = threadIdx.x; i < words; i += blockDim.x) s_plan[i] = a.plan[i];
   __syncthreads();
-  PlanView p;
-  p.maxa = maxa;
-  p.n = s_plan[0];
-  p.active = s_plan + 1;
-  p.offs = s_plan + 1 + maxa;
-  p.slots = s_plan + 2 + 2 * maxa;
-  return p;
+  return plan_view(a, s_plan);
+}
+
+// Routing inside the gate/up launch (B*k <= 64): the workgroup selects the
+// top-k of all B tokens from the router's logits [B][E] (bias included) and
+// builds the plan in LDS -- the same functions, hence the same bits, as the
+// router's finishing workgroup.  The last workgroup of the grid also stores
+// ids, weights and plan for the down launch and the caller.  Ends with a
+// barrier.
+__device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s_plan, TopkScratch* s_tk,
+                                               int32_t* s_ids, float* s_w) {
+  constexpr int QB = 2;
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  const bool writer = blockIdx.x == gridDim.x - 1;
+  const int B = a.B, E = a.E, k = a.k;
+  for (int t0 = wave; t0 < B; t0 += nw * QB) {
+    float lv[QB][kNI];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int t = t0 + nw * q;
+      load_logit_row(a.logits, t < B ? t : B - 1, E, lv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int t = t0 + nw * q;
+      if (t < B)
+        topk_wave(lv[q], E, k, s_tk[wave], s_ids + t * k, s_w + t * k, writer ? a.ids_out + (size_t)t * k : nullptr,
+                  writer ? a.w_out + (size_t)t * k : nullptr);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) plan_wave(s_ids, B * k, E, reinterpret_cast<int*>(s_tk), s_plan, writer ? a.plan_out : nullptr);
+  __syncthreads();
+  return plan_view(a, s_plan);
 }
 
 // Entry e_idx of the plan: a routed expert (e_idx < n) or the shared one.
@@ -137,7 +178,7 @@ template <typename T, int MB, int NH>
 __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i,
                                         int half, int ps, float* s_part) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int U = MB <= 1 ? 8 / NH : (MB <= 2 ? 4 : 2);
+  constexpr int U = MB <= 1 ? 8 / NH : (MB <= 2 ? 4 : (MB <= 4 ? 2 : 1));
   const int lane = threadIdx.x & 63;
   const bool live = i < v.I;
   const T* W13 = reinterpret_cast<const T*>(v.W13);

@@ -32,6 +32,13 @@ struct ExpertLaunch {
   const float* topk_w;      // [B][k]
   void* out;                // [B][d]
   int out_bf16;
+  // routing inside the gate/up launch (fused block, B*k <= 64, vector
+  // shape): router logits [B][E] with the bias added; the last workgroup
+  // stores ids, weights (= topk_w) and the plan (= plan)
+  const float* logits;
+  int32_t* ids_out;
+  float* w_out;
+  int32_t* plan_out;
 };
 
 // Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
@@ -48,8 +55,9 @@ struct SkinnyLaunch {
   // store mode
   void* Y;
   int y_bf16;
-  // router mode (router != 0)
+  // router mode (router != 0); finish = 0: logits only (no top-k, no plan)
   int router;
+  int finish;
   const float* bias;
   int bias_ld;
   float* logits;            // [M][N] workspace

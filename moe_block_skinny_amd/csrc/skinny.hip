@@ -54,119 +54,34 @@ __device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n
 
 // ---- router finish: top-k, weights, plan (one workgroup) ------------------
 
-constexpr int kMaxE = 512;
-constexpr int kMaxK = 16;
-constexpr int kMaxB = 64;
-
-// One wave selects the top-k of QB tokens at once (their selection chains
-// are independent, so interleaving them fills the issue slots a single
-// chain leaves idle).  For token q, lane l holds the keys of experts
-// l, l+64, ...  Each of the k rounds takes the largest remaining key (DPP max
-// + readlane); its expert is the lowest index holding that key: the first
-// matching slot in each lane, then the lane itself when only one lane
-// matches (the usual case), else the smallest such expert over the wave.
-// Lane j keeps the j-th winner, computes its softmax term, and finds its
-// place in ascending-id order from the other winners.
-template <int QB>
-__device__ __forceinline__ void topk_select(const SkinnyLaunch& a, const int (&tq)[QB],
-                                            const float (&lv)[QB][kMaxE / 64], int* s_ids) {
-  constexpr int NI = kMaxE / 64;
-  const int lane = threadIdx.x & 63;
-  const int E = a.N, k = a.k, M = a.M;
-  uint32_t key[QB][NI];
-  int my_e[QB];
-  uint32_t my_key[QB];
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) key[q][i] = (tq[q] < M && lane + 64 * i < E) ? ord_key(lv[q][i]) : 0u;
-    my_e[q] = 0x7fffffff;
-    my_key[q] = 0u;
-  }
-  for (int j = 0; j < k; ++j) {
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      if (tq[q] >= M) continue;
-      uint32_t lm = key[q][0];
-#pragma unroll
-      for (int i = 1; i < NI; ++i) lm = key[q][i] > lm ? key[q][i] : lm;
-      const uint32_t best = wave_max_u32(lm);
-      int slot = NI;  // first slot of this lane holding best
-#pragma unroll
-      for (int i = NI - 1; i >= 0; --i) slot = key[q][i] == best ? i : slot;
-      const int e_here = slot < NI ? lane + 64 * slot : 0x7fffffff;
-      const uint64_t bal = __ballot(slot < NI);
-      int win;
-      if (__popcll(bal) == 1) {
-        win = __builtin_amdgcn_readlane(e_here, __ffsll((long long)bal) - 1);
-      } else {  // equal keys in several lanes: lowest expert index wins
-        int v = e_here;
-        auto mn = [](int x, int y) { return x < y ? x : y; };
-        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false));
-        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false));
-        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false));
-        v = mn(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xf, 0xf, false));
-        win = mn(mn(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-                 mn(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (lane + 64 * i == win) key[q][i] = 0u;
-      if (lane == j) { my_e[q] = win; my_key[q] = best; }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    if (tq[q] >= M) continue;
-    const int t = tq[q];
-    // softmax over the selection; winner 0 holds the largest logit
-    const float m = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key[q], 0));
-    const float ex = lane < k ? expf(key_value(my_key[q]) - m) : 0.f;
-    const float z = group_sum<64>(ex);
-    int pos = 0;
-    for (int i = 0; i < k; ++i) pos += __builtin_amdgcn_readlane(my_e[q], i) < my_e[q] ? 1 : 0;
-    if (lane < k) {
-      a.topk_ids[(size_t)t * k + pos] = my_e[q];
-      a.topk_w[(size_t)t * k + pos] = ex / z;
-      s_ids[t * k + pos] = my_e[q];
-    }
-  }
-}
-
-// The wave's tokens t = wave, wave + nw, ... in groups of four: all logit
-// loads of a group are issued (clamped addresses, no branches) before any is
-// used, so a group costs one memory round trip, and its four selections run
-// interleaved.
-__device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, int* s_ids) {
+// Top-k of every token: waves take tokens wave, wave + nw, ..., with the
+// logits of four tokens loaded before any is used (one memory round trip
+// per group); ids and weights go to LDS and to the caller's arrays.
+__device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* s_tk, int32_t* s_ids, float* s_w) {
   constexpr int QB = 4;
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int E = a.N, M = a.M;
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  const int E = a.N, M = a.M, k = a.k;
   for (int t0 = wave; t0 < M; t0 += nw * QB) {
-    float lv[QB][kMaxE / 64];
-    int tq[QB];
+    float lv[QB][kNI];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      tq[q] = t0 + nw * q;
-      const int tc = tq[q] < M ? tq[q] : M - 1;
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i) {
-        const int e = lane + 64 * i;
-        lv[q][i] = ld_after_acquire(&a.logits[(size_t)tc * E + (e < E ? e : E - 1)]);
-      }
+      const int t = t0 + nw * q;
+      load_logit_row(a.logits, t < M ? t : M - 1, E, lv[q]);
     }
-    if (tq[1] < M) topk_select<QB>(a, tq, lv, s_ids);
-    else {  // a lone token: skip the idle chains
-      const int t1[1] = {tq[0]};
-      float l1[1][kMaxE / 64];
 #pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i) l1[0][i] = lv[0][i];
-      topk_select<1>(a, t1, l1, s_ids);
+    for (int q = 0; q < QB; ++q) {
+      const int t = t0 + nw * q;
+      if (t < M)
+        topk_wave(lv[q], E, k, s_tk[wave], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
+                  a.topk_w + (size_t)t * k);
     }
   }
 }
 
 __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
-  __shared__ int s_ids[kMaxB * kMaxK];
+  __shared__ int32_t s_ids[kMaxB * kMaxK];
+  __shared__ float s_w[kMaxB * kMaxK];
+  __shared__ TopkScratch s_tk[16];
   __shared__ unsigned long long s_mask[kMaxE];
   __shared__ int s_cnt[kMaxE];
   __shared__ int s_act[kMaxE];
@@ -174,7 +89,12 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int M = a.M, E = a.N, k = a.k, nslot = M * k;
 
-  topk_tokens(a, s_ids);
+  topk_tokens(a, s_tk, s_ids, s_w);
+  __syncthreads();
+  if (nslot <= 64) {  // one wave sorts the slots
+    if (wave == 0) plan_wave(s_ids, nslot, E, reinterpret_cast<int*>(s_tk), a.plan, nullptr);
+    return;
+  }
   for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
   __syncthreads();
   // bit t of s_mask[e] is set when token t selected expert e (B <= 64)
@@ -226,7 +146,7 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
 // Router tail: every router workgroup arrives once; the last runs the finish.
 __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   __shared__ int s_flag;
-  if (!a.router) return;
+  if (!a.router || !a.finish) return;
   if (!arrive_last(a.done_counter, (uint32_t)a.router_wgs, &s_flag)) return;
   route_finish(a);
 }
@@ -236,11 +156,11 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
 // Workgroup: RB weight rows starting at blockIdx.x * RB, all K.  Wave w
 // takes the 64-chunk blocks w, w + NW, w + 2 NW, ... of every row (one 1 KB
 // segment per row per load instruction); U blocks per lane are in flight.
-template <typename T, int RB, int MB, int U>
+template <typename T, int RB, int MB, int U, bool ROUTER>
 __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   constexpr int VEC = Elem<T>::VEC;
   __shared__ float s_red[16 * RB * MB];
-  if (a.router && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
+  if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
     shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, s_red);
     return;
   }
@@ -294,7 +214,7 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
     for (int w = 0; w < nw; ++w) v += s_red[(w * RB + r) * MB + t];
     if (n < a.N && t < a.M) finish_value(a, t, n, v);
   }
-  router_tail(a);
+  if constexpr (ROUTER) router_tail(a);
 }
 
 // ---- MFMA kernel (bf16) --------------------------------------------------
@@ -305,11 +225,11 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
 // Wave w takes the 4-step blocks w, w + NW, ... (128 K elements per row, 256
 // contiguous bytes, over four back-to-back loads).  The accumulator of tile
 // nt holds, in lane l, rows 4*(l/16)+i, token l%16.
-template <int NT>
+template <int NT, bool ROUTER>
 __global__ __launch_bounds__(512) void skinny_mfma_kernel(SkinnyLaunch a) {
   constexpr int SB = 4;  // K steps per block
   extern __shared__ float s_dyn[];  // [NW][NT][64][4]
-  if (a.router && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
+  if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
     shared_up_task<bf16_t, kPathMfma>(a.ex, blockIdx.x - a.router_wgs, s_dyn);
     return;
   }
@@ -345,7 +265,7 @@ __global__ __launch_bounds__(512) void skinny_mfma_kernel(SkinnyLaunch a) {
     const int n = n0 + 4 * (l >> 4) + i, t = nt * 16 + (l & 15);
     if (n < a.N && t < a.M) finish_value(a, t, n, v);
   }
-  router_tail(a);
+  if constexpr (ROUTER) router_tail(a);
 }
 
 // ---- host side -----------------------------------------------------------
@@ -389,6 +309,15 @@ int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
   return mfma ? (ex.Is + kUpPairsMfma - 1) / kUpPairsMfma : (ex.Is + pp - 1) / pp;
 }
 
+// Router launches take the instantiation with the router's finish and side
+// job compiled in (and their LDS); plain products the one without.
+template <typename K>
+static void launch_as(const SkinnyLaunch& a, K router_kernel, K plain_kernel, dim3 grid, dim3 block, size_t lds,
+                      hipStream_t st) {
+  if (a.router) launch(K_ROUTE, router_kernel, grid, block, (uint32_t)lds, st, a);
+  else launch(K_SKINNY, plain_kernel, grid, block, (uint32_t)lds, st, a);
+}
+
 hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
   SkinnyLaunch a = a0;
   const int rows = skinny_rows_per_block(a.variant, a.router);
@@ -403,47 +332,47 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
     const int nt = (a.M + 15) / 16;
     const size_t lds = (size_t)nw * nt * 256 * sizeof(float);
     switch (nt) {
-      case 1: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<1>, grid, block, lds, st, a); break;
-      case 2: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<2>, grid, block, lds, st, a); break;
-      case 3: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<3>, grid, block, lds, st, a); break;
-      default: launch(a.router ? K_ROUTE : K_SKINNY, skinny_mfma_kernel<4>, grid, block, lds, st, a); break;
+      case 1: launch_as(a, skinny_mfma_kernel<1, true>, skinny_mfma_kernel<1, false>, grid, block, lds, st); break;
+      case 2: launch_as(a, skinny_mfma_kernel<2, true>, skinny_mfma_kernel<2, false>, grid, block, lds, st); break;
+      case 3: launch_as(a, skinny_mfma_kernel<3, true>, skinny_mfma_kernel<3, false>, grid, block, lds, st); break;
+      default: launch_as(a, skinny_mfma_kernel<4, true>, skinny_mfma_kernel<4, false>, grid, block, lds, st); break;
     }
     name = "mfma";
   } else if (a.router) {
     name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
     if (a.bf16) {
-      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 1, 4>), grid, block, 0, st, a);
-      else if (a.M <= 2) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 2, 4>), grid, block, 0, st, a);
-      else if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 1, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 2, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 4, 2, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 8, 1, true>, grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 1, 4>), grid, block, 0, st, a);
-      else if (a.M <= 2) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 2, 4>), grid, block, 0, st, a);
-      else if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<float, 4, 1, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<float, 4, 2, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<float, 4, 4, 2, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<float, 4, 8, 1, true>, grid, block, 0, st, a);
     }
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {
-      if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 4, 2>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 4) launch(K_SKINNY, skinny_valu_kernel<bf16_t, 4, 4, 2, false>, grid, block, 0, st, a);
+      else launch(K_SKINNY, skinny_valu_kernel<bf16_t, 4, 8, 1, false>, grid, block, 0, st, a);
     } else {
-      if (a.M <= 4) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 4, 2>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 4, 8, 1>), grid, block, 0, st, a);
+      if (a.M <= 4) launch(K_SKINNY, skinny_valu_kernel<float, 4, 4, 2, false>, grid, block, 0, st, a);
+      else launch(K_SKINNY, skinny_valu_kernel<float, 4, 8, 1, false>, grid, block, 0, st, a);
     }
     name = "splitk";
   } else {
     if (a.bf16) {
-      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 2, 1, 4>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<bf16_t, 2, 2, 4>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_SKINNY, skinny_valu_kernel<bf16_t, 2, 1, 4, false>, grid, block, 0, st, a);
+      else launch(K_SKINNY, skinny_valu_kernel<bf16_t, 2, 2, 4, false>, grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 2, 1, 4>), grid, block, 0, st, a);
-      else launch(a.router ? K_ROUTE : K_SKINNY, (skinny_valu_kernel<float, 2, 2, 4>), grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_SKINNY, skinny_valu_kernel<float, 2, 1, 4, false>, grid, block, 0, st, a);
+      else launch(K_SKINNY, skinny_valu_kernel<float, 2, 2, 4, false>, grid, block, 0, st, a);
     }
     name = "gemv";
   }
   if (desc)
-    snprintf(desc, desc_len, "%s M=%d N=%d K=%d waves/wg=%d grid=%d%s", name, a.M, a.N, a.K, nw, nwg,
-             extra ? " +shared gate/up" : "");
+    snprintf(desc, desc_len, "%s M=%d N=%d K=%d waves/wg=%d grid=%d%s%s", name, a.M, a.N, a.K, nw, nwg,
+             extra ? " +shared gate/up" : "", a.router && !a.finish ? " logits-only" : "");
   return hipGetLastError();
 }
 
