@@ -113,6 +113,7 @@ def run_moe(args, torch, mb, synth):
                      s["bias"], s["bias_ld"], topk_ids=s["ids"])
 
     ms = timed_loop(step, args, torch)
+    route_in_up = "top-k/plan" in mb.last_variant()
     # algorithmic bytes per set: every selected expert's weights once, the
     # router and shared expert, x (and bias) read once, out written once
     per_set = []
@@ -120,7 +121,7 @@ def run_moe(args, torch, mb, synth):
         n = int(torch.unique(s["ids"]).numel())
         bias_b = 0 if s["bias"] is None else s["bias"].numel() * 4
         b = cfg.E * cfg.d * esz + n * expert_bytes + shared_bytes + 2 * cfg.B * cfg.d * esz + bias_b
-        per_set.append((n, b, launch_bytes(cfg, n, esz, bias_b)))
+        per_set.append((n, b, launch_bytes(cfg, n, esz, bias_b, route_in_up)))
     avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
     kern, kbytes = {}, {}
@@ -159,16 +160,25 @@ KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel (router mode)
                  "expert_down_combine": "expert_down_combine_kernel"}
 
 
-def launch_bytes(cfg, n, esz, bias_b):
+def launch_bytes(cfg, n, esz, bias_b, route_in_up):
     """Algorithmic HBM bytes of each launch of the block, for n distinct
     routed experts: the weights it streams (once), the activations it must
     read and the results it must write.  Workspace traffic between launches
-    (h, fp32) is counted as the producer's output and the consumer's input;
-    the router's logits, the completion counter and the plan are not."""
+    (h and, when the gate/up launch selects, the logits; fp32) is counted as
+    the producer's output and the consumer's input; the completion counter
+    and the plan are not.  The shared expert's gate/up runs in the gate/up
+    launch when that launch also selects (small batch), else in the router
+    launch."""
     B, d, E, k, I, Is = cfg.B, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is
     x = B * d * esz
-    route = E * d * esz + x + bias_b + B * k * 8 + (2 * Is * d * esz + B * Is * 4 if Is else 0)
+    shared_up = 2 * Is * d * esz + B * Is * 4 if Is else 0
+    route = E * d * esz + x + bias_b
     up = n * 2 * I * d * esz + x + B * k * I * 4
+    if route_in_up:
+        route += B * E * 4                      # logits out
+        up += B * E * 4 + B * k * 8 + shared_up  # logits in, ids + weights out
+    else:
+        route += B * k * 8 + shared_up
     down = n * d * I * esz + B * k * I * 4 + B * k * 4 + B * d * esz
     if Is:
         down += d * Is * esz + B * Is * 4

@@ -206,12 +206,18 @@ moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const 
 moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
                          int has_shared, void* out, void* stream);
 
-/* The whole block in three launches, every intermediate in ws:
- *   1. router scoring + top-k + plan, with the shared expert's gate/up
- *      (which needs no routing) in the same launch;
- *   2. routed experts' gate/up + SwiGLU;
+/* The whole block in three launches, every intermediate in ws.
+ * Small batch on the vector shape (B*k <= 64):
+ *   1. router scoring only (logits + bias to ws);
+ *   2. gate/up + SwiGLU: every workgroup selects the top-k of all tokens
+ *      and builds the plan itself (no handshake between workgroups); the
+ *      shared expert's tiles, which need no routing, go first; one
+ *      workgroup stores topk_ids, topk_w and the plan;
  *   3. down projection of every expert fused with the weighted combine: the
  *      per-slot outputs never leave the chip.
+ * Otherwise: 1. router scoring + top-k + plan (the last workgroup to finish
+ * selects), with the shared expert's gate/up in the same launch; 2. routed
+ * gate/up + SwiGLU; 3. as above.
  * Same scope and results as moe_route, moe_expert_ffn and moe_combine in
  * sequence (bit for bit with the vector-ALU shapes; with the MFMA shape the
  * shared expert's K split differs, within fp32 rounding).  topk_ids /
