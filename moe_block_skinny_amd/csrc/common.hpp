@@ -70,6 +70,20 @@ __device__ __forceinline__ float dot_chunk(u32x4 w, u32x4 x, float acc, bf16_t) 
   acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), as_bf16x2(x3), acc, false);
   return acc;
 }
+// fp32 activations as bf16 pairs: hi = RNE(x), lo = RNE(x - hi), so x =
+// hi + lo to about 16 significant bits.  Elements 2i and 2i+1 go to the low
+// and high halves of word i, as in a bf16 weight chunk.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+  const bf16_t la = f32_to_bf16(a - bf16_to_f32(ha)), lb = f32_to_bf16(b - bf16_to_f32(hb));
+  hi = (uint32_t)ha | ((uint32_t)hb << 16);
+  lo = (uint32_t)la | ((uint32_t)lb << 16);
+}
+// bf16 weight chunk against an activation chunk given as hi/lo bf16 pairs:
+// the hi terms first, then the lo terms.
+__device__ __forceinline__ float dot_chunk_hilo(u32x4 w, u32x4 hi, u32x4 lo) {
+  return dot_chunk(w, lo, dot_chunk(w, hi, 0.f, bf16_t()), bf16_t());
+}
 __device__ __forceinline__ float dot_chunk(u32x4 w, u32x4 x, float acc, float) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -138,26 +138,59 @@ __device__ __forceinline__ float combine_one(const float* w_t, int k, int has_sh
 // (I, Is <= 16 chunks: 8 loads per lane per entry, so the whole grid is
 // resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays
 // within 36 KB at B=64).
-template <typename T, int PATHS, int RT>
+template <typename T, int PATHS, int RT, bool PIPE>
 __global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512) void expert_down_combine_kernel(ExpertLaunch a) {
+  // PIPE (vector shape, short rows, h fits in LDS): h is staged in LDS with
+  // the plan and each wave prefetches its next entry's W2 rows
+  // (down_valu_pipe)
   __shared__ int32_t s_plan[kMaxPlanWords];
   __shared__ float s_tw[kMaxB * kMaxK];
-  extern __shared__ float s_y[];   // [B*k + B][RT]
+  extern __shared__ float s_dyn[];   // s_y [B*k + B][rt], then (PIPE) h [B*k + B][hld]
+  const int rt = PIPE ? a.down_rows : RT;
+  float* s_y = s_dyn;
+  float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
   for (int i = threadIdx.x; i < a.B * a.k; i += blockDim.x) s_tw[i] = a.topk_w[i];
-  const PlanView p = stage_plan(a, s_plan);   // its barrier also covers s_tw
+  if constexpr (PIPE) {
+    // h to LDS: fp32 as is, or for bf16 weights as bf16 hi/lo word rows
+    const int nrows = a.B * a.k + a.B;
+    const int n4 = nrows * a.hld / 4;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(a.h)[i];
+      if constexpr (sizeof(T) == 2) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16x2(x.x, x.y, h0, l0);
+        split_bf16x2(x.z, x.w, h1, l1);
+        uint32_t* hw = reinterpret_cast<uint32_t*>(s_h);
+        hw[2 * i] = h0;
+        hw[2 * i + 1] = h1;
+        hw[(size_t)nrows * a.hld / 2 + 2 * i] = l0;
+        hw[(size_t)nrows * a.hld / 2 + 2 * i + 1] = l1;
+      } else {
+        reinterpret_cast<f32x4*>(s_h)[i] = x;
+      }
+    }
+  }
+  __shared__ int s_order[PIPE ? kMaxB * kMaxK + kMaxB : 1];
+  const PlanView p = stage_plan(a, s_plan);   // its barrier also covers s_tw and s_h
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * RT;
-  const YSink sink = {s_y, 1, r0, RT};
+  const int r0 = blockIdx.x * rt;
+  const YSink sink = {s_y, 1, r0, rt};
   const int ne = entries(a, p, true);
-  for (int e_idx = wave; e_idx < ne; e_idx += nw)
-    down_dispatch<T, PATHS, RT>(a, p.slots, expert_view<T>(a, p, e_idx), r0, sink);
+  if constexpr (PIPE) {
+    if (wave == 0) order_entries(a, p, ne, s_order);
+    __syncthreads();
+    down_valu_pipe<T, RT>(a, p, ne, s_order, r0, rt, sink, s_h);
+  } else {
+    for (int e_idx = wave; e_idx < ne; e_idx += nw)
+      down_dispatch<T, PATHS, RT>(a, p.slots, expert_view<T>(a, p, e_idx), r0, sink);
+  }
   __syncthreads();
   const int has_shared = a.Ws13 ? 1 : 0;
-  for (int idx = threadIdx.x; idx < a.B * RT; idx += blockDim.x) {
-    const int t = idx / RT, r = idx % RT;
+  for (int idx = threadIdx.x; idx < a.B * rt; idx += blockDim.x) {
+    const int t = idx / rt, r = idx % rt;
     if (r0 + r >= a.d) continue;
     const float v = combine_one(s_tw + t * a.k, a.k, has_shared, [&](int j) {
-      return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * RT + r];
+      return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * rt + r];
     });
     const size_t o = (size_t)t * a.d + r0 + r;
     if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[o] = f32_to_bf16(v);
@@ -192,7 +225,9 @@ static int max_entries(const ExpertLaunch& a) {
   return (nslot < a.E ? nslot : a.E) + (a.Ws13 ? 1 : 0);
 }
 
-static const int kMaxResidentWG = 256 * 8;
+static const int kCUs = 256;                   // compute units of an MI355X
+static const int kMaxResidentWG = kCUs * 8;
+static const size_t kMaxStagedH = 72 * 1024;   // h staged in LDS by the 32-row down+combine
 
 hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
   const int paths = expert_paths(a.bf16, a.force, a.B);
@@ -232,25 +267,37 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
+hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
+  ExpertLaunch a = a0;
   const int paths = expert_paths(a.bf16, a.force, a.B);
   const int vec = a.bf16 ? 8 : 4;
   const bool short_rows = a.I <= 16 * vec && (!a.Ws13 || a.Is <= 16 * vec);
-  const int rt = (paths == kPathValu && short_rows) ? 32 : 16;
+  const size_t h_bytes = (size_t)(a.B * a.k + a.B) * a.hld * sizeof(float);
+  // prefetching shape: one 16-wave workgroup per CU (its register count
+  // allows no second), rows split evenly in multiples of 4, up to 28
+  const int rt_pipe = 4 * ((a.d + 4 * kCUs - 1) / (4 * kCUs));
+  const bool pipe = paths == kPathValu && short_rows && h_bytes <= kMaxStagedH && rt_pipe <= 28;
+  int rt = 16;
+  if (pipe) {
+    rt = rt_pipe;
+    a.down_rows = rt;
+  }
   const int g = (a.d + rt - 1) / rt;
   int nw = max_entries(a);
   const int maxw = paths == kPathValu ? 16 : 8;
   if (nw > maxw) nw = maxw;
   if (nw < 1) nw = 1;
-  const size_t lds = (size_t)(a.B * a.k + a.B) * rt * sizeof(float);
+  const size_t lds = (size_t)(a.B * a.k + a.B) * rt * sizeof(float) + (pipe ? h_bytes : 0);
   const dim3 grid(g), block(64 * nw);
-  if (!a.bf16 && rt == 32) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 32>), grid, block, lds, st, a);
-  else if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 16>), grid, block, lds, st, a);
-  else if (paths == kPathValu && rt == 32) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 32>), grid, block, lds, st, a);
-  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 16>), grid, block, lds, st, a);
-  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16>), grid, block, lds, st, a);
-  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth, 16>), grid, block, lds, st, a);
-  if (desc) snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d force=%d", g, rt, nw, a.force);
+  if (!a.bf16 && pipe) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 28, true>), grid, block, lds, st, a);
+  else if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 16, false>), grid, block, lds, st, a);
+  else if (pipe) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 28, true>), grid, block, lds, st, a);
+  else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 16, false>), grid, block, lds, st, a);
+  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16, false>), grid, block, lds, st, a);
+  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth, 16, false>), grid, block, lds, st, a);
+  if (desc)
+    snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d%s force=%d", g, rt, nw,
+             pipe ? " prefetch" : "", a.force);
   return hipGetLastError();
 }
 

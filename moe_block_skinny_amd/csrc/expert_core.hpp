@@ -364,8 +364,17 @@ __device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* 
 #pragma unroll
     for (int e = 0; e < VEC; ++e) xs[e] = cok ? hp[e] : 0.f;
     float acc[R];
+    if constexpr (sizeof(T) == 2) {
+      uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_f32x(wv[r], xs, 0.f, T()));
+      for (int q = 0; q < 4; ++q) split_bf16x2(xs[2 * q], xs[2 * q + 1], hi[q], lo[q]);
+      const u32x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_hilo(wv[r], h4, l4));
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_f32x(wv[r], xs, 0.f, T()));
+    }
     if (c == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -373,6 +382,137 @@ __device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* 
         if (row < a.d) *sink.at(a, sr, row) = acc[r];
       }
     }
+  }
+}
+
+// Values every lane of the wave holds alike, moved to scalar registers so the
+// compiler sees uniform control flow (and does not wait for every load in
+// flight where lanes could have diverged).
+// (Integers only: a pointer passed through readfirstlane would lose its
+// global address space and turn its loads into flat ones.)
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ ExpertView wave_uniform(ExpertView v) {
+  v.m = wave_uniform(v.m);
+  v.I = wave_uniform(v.I);
+  v.slot0 = wave_uniform(v.slot0);
+  return v;
+}
+
+// Rows r0 .. r0 + rows - 1 (rows a multiple of 4, at most ROWS) of the
+// entries this wave is given, vector shape with L = 16 lanes per W2 row
+// (I <= 16 * VEC).  Entry order: s_order lists the entries by falling token
+// count and the waves take them in snake order (w, 2nw-1-w, 2nw+w, ...), so
+// the waves' token totals come out close.  The W2 rows of the wave's next
+// entry are requested before the current entry's products (two register
+// buffers used in turn, so no copy waits on a load), so a wave always has
+// one entry in flight.  Every load is issued unconditionally from a clamped
+// address -- past the last entry, and for row slots past `rows`, from rows
+// this wave reads anyway -- so the compiler never has to wait for all loads
+// at a branch.  h is read from LDS (s_h: bf16 hi/lo word rows for bf16
+// weights, fp32 rows otherwise), so waiting for it never waits for the
+// prefetch.  Same products in the same order as down_valu<T, 16, *>, hence
+// the same bits.
+template <typename T, int ROWS>
+__device__ __forceinline__ void down_valu_pipe(const ExpertLaunch& a, const PlanView& p, int ne, const int* s_order,
+                                               int r0, int rows, const YSink& sink, const void* s_h) {
+  constexpr int L = 16;
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int P = 64 / L;
+  constexpr int R = ROWS / P;
+  const int lane = threadIdx.x & 63;
+  const int nw = wave_uniform(blockDim.x >> 6), w = wave_uniform(threadIdx.x >> 6);
+  const int c = lane % L, g = lane / L;
+  const int rbase = r0 + g;
+  const int rn = rows / P;   // row slots in use (uniform)
+  const int hw = a.hld / 2;  // words per bf16 hi (or lo) row
+  const int nrows = a.B * a.k + a.B;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  ne = wave_uniform(ne);
+  auto pos = [&](int j) { return j * nw + ((j & 1) ? nw - 1 - w : w); };
+  if (pos(0) >= ne) return;
+  auto load = [&](const ExpertView& v, u32x4(&wv)[R]) {
+    const char* W2 = reinterpret_cast<const char*>(v.W2);
+    const int cc = (c * VEC < v.I ? c * VEC : 0) * (int)sizeof(T);
+    const int ld = v.I * (int)sizeof(T);   // bytes per W2 row
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int row = rbase + P * (r < rn ? r : 0);
+      row = row < a.d ? row : a.d - 1;
+      wv[r] = ld128_stream(W2 + (unsigned)(row * ld + cc));
+    }
+  };
+  auto products = [&](const ExpertView& v, const u32x4(&wv)[R]) {
+    const bool cok = c * VEC < v.I;
+    for (int t = 0; t < v.m; ++t) {
+      int tok, sr;
+      token_of(a, p.slots, v, t, tok, sr);
+      float acc[R];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t* hh = static_cast<const uint32_t*>(s_h) + (size_t)sr * hw + (cok ? c * 4 : 0);
+        const uint32_t* hl = hh + (size_t)nrows * hw;
+        const u32x4 h4 = cok ? *reinterpret_cast<const u32x4*>(hh) : zero;
+        const u32x4 l4 = cok ? *reinterpret_cast<const u32x4*>(hl) : zero;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = rbase + P * r;
+          acc[r] = group_sum<L>(dot_chunk_hilo((cok && row < a.d) ? wv[r] : zero, h4, l4));
+        }
+      } else {
+        const float* hp = static_cast<const float*>(s_h) + (size_t)sr * a.hld + (cok ? c * VEC : 0);
+        float xs[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) xs[q] = cok ? hp[q] : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = rbase + P * r;
+          acc[r] = group_sum<L>(dot_chunk_f32x((cok && row < a.d) ? wv[r] : zero, xs, 0.f, T()));
+        }
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = rbase + P * r;
+          if (r < rn && row < a.d) *sink.at(a, sr, row) = acc[r];
+        }
+      }
+    }
+  };
+  auto view = [&](int j) { return wave_uniform(expert_view<T>(a, p, s_order[pos(j)])); };
+  ExpertView v = view(0);
+  u32x4 b0[R], b1[R];
+  load(v, b0);
+  for (int j = 0;;) {
+    // past the last entry the "next" loads re-read this entry's rows (cached)
+    bool more = pos(j + 1) < ne;
+    ExpertView vn = more ? view(j + 1) : v;
+    load(vn, b1);
+    products(v, b0);
+    if (!more) break;
+    v = vn;
+    ++j;
+    more = pos(j + 1) < ne;
+    vn = more ? view(j + 1) : v;
+    load(vn, b0);
+    products(v, b1);
+    if (!more) break;
+    v = vn;
+    ++j;
+  }
+}
+
+// Entries of the plan (routed, then the shared one) ordered by falling token
+// count, ties by entry index, into s_order -- one wave, by ranking.
+__device__ __forceinline__ void order_entries(const ExpertLaunch& a, const PlanView& p, int ne, int* s_order) {
+  const int lane = threadIdx.x & 63;
+  for (int i0 = 0; i0 < ne; i0 += 64) {
+    const int i = i0 + lane;
+    const int mi = i < ne ? (i < p.n ? p.offs[i + 1] - p.offs[i] : a.B) : -1;
+    int rank = 0;
+    for (int j = 0; j < ne; ++j) {
+      const int mj = j < p.n ? p.offs[j + 1] - p.offs[j] : a.B;
+      rank += (mj > mi || (mj == mi && j < i)) ? 1 : 0;
+    }
+    if (i < ne) s_order[rank] = i;
   }
 }
 

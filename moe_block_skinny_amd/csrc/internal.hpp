@@ -39,6 +39,7 @@ struct ExpertLaunch {
   int32_t* ids_out;
   float* w_out;
   int32_t* plan_out;
+  int down_rows;            // rows per workgroup of the prefetching down+combine
 };
 
 // Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
