@@ -158,7 +158,9 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   X [B][K] dtype, W [N][K] dtype, Y [B][N] of y_dtype (dtype or
  *   MOE_DT_F32).  1 <= B <= 64; K a multiple of 8 (bf16) or 4 (fp32), and of
  *   32 for the mfma shape (bf16 only).  Output rounded to nearest-even when
- *   y_dtype is bf16.  Needs no workspace (ws may be NULL, ws_bytes 0). */
+ *   y_dtype is bf16.  Workspace: moe_workspace_bytes(MOE_OP_SKINNY_GEMM,
+ *   ...) bytes, zero-filled once (0 for fp32; for bf16 the mfma shape keeps
+ *   fp32 partial sums of its K slices there); ws may be NULL when 0. */
 moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
                          int y_dtype, void* ws, size_t ws_bytes, void* stream);
 

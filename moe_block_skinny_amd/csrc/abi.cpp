@@ -97,19 +97,32 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
   return MOE_OK;
 }
 
-// Router workspace: fp32 logits [B][E] and the completion counter.  The
-// dense product needs none.
+// Skinny-product workspace: router logits fp32 [B][E] and its completion
+// counter (router only); with bf16 (where the MFMA shape may run) the fp32
+// partial sums of its K slices [slices][B][N] and one arrival counter per
+// 64-row group.
 struct SkinnyWs {
-  size_t logits, done, total;
+  size_t logits, done, part, rg, total;
 };
 
-SkinnyWs skinny_ws(int B, int N, bool router) {
+SkinnyWs skinny_ws(int B, int N, int K, int bf16, bool router) {
   SkinnyWs w;
   size_t o = 0;
   w.logits = o;
   if (router) o = up(o + (size_t)B * N * 4);
   w.done = o;
   if (router) o = up(o + 4);
+  w.part = w.rg = o;
+  if (bf16 && K >= 32) {
+    int ks = 1, steps = 0;
+    skinny_mfma_slices(B, N, K, &ks, &steps);
+    if (ks > 1) {
+      w.part = o;
+      o = up(o + (size_t)ks * B * N * 4);
+      w.rg = o;
+      o = up(o + (size_t)((N + 63) / 64) * 4);
+    }
+  }
   w.total = o;
   return w;
 }
@@ -135,7 +148,7 @@ struct BlockWs {
 
 BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   BlockWs b;
-  b.route = skinny_ws(B, E, true);
+  b.route = skinny_ws(B, E, d, bf16, true);
   b.ffn = expert_ws(B, k, I, Is);
   size_t o = 0;
   b.route_off = o;
@@ -207,11 +220,13 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   int v;
   moe_status_t s = resolve_skinny(bf16, B, d, &v);
   if (s) return s;
-  const SkinnyWs L = skinny_ws(B, E, true);
+  const SkinnyWs L = skinny_ws(B, E, d, bf16, true);
   SkinnyLaunch a = {};
   a.bf16 = bf16;
   a.X = X;
   a.W = Wr;
+  a.part = reinterpret_cast<float*>(ws + L.part);
+  a.rg_counter = reinterpret_cast<uint32_t*>(ws + L.rg);
   a.M = B;
   a.N = E;
   a.K = d;
@@ -335,10 +350,10 @@ size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I,
   switch (op) {
     case MOE_OP_SKINNY_GEMM:
       if (N <= 0 || K <= 0) return 0;
-      return skinny_ws(B, N, false).total;
+      return skinny_ws(B, N, K, bf16, false).total;
     case MOE_OP_ROUTE:
       if (E <= 0 || d <= 0) return 0;
-      return skinny_ws(B, E, true).total;
+      return skinny_ws(B, E, d, bf16, true).total;
     case MOE_OP_EXPERT_FFN:
       if (k <= 0) return 0;
       return expert_ws(B, k, I, Is).total;
@@ -370,12 +385,15 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   int v;
   s = resolve_skinny(bf16, B, K, &v);
   if (s) return s;
-  (void)ws;
-  (void)ws_bytes;
+  const SkinnyWs L = skinny_ws(B, N, K, bf16, false);
+  if (L.total && !aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   SkinnyLaunch a = {};
   a.bf16 = bf16;
   a.X = X;
   a.W = W;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + L.part);
+  a.rg_counter = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.rg);
   a.M = B;
   a.N = N;
   a.K = K;
@@ -408,7 +426,7 @@ moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, con
   int v;
   s = resolve_skinny(bf16, B, d, &v);
   if (s) return s;
-  const size_t need = skinny_ws(B, E, true).total;
+  const size_t need = skinny_ws(B, E, d, bf16, true).total;
   if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
   if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   char desc[160];

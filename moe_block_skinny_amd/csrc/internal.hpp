@@ -69,10 +69,17 @@ struct SkinnyLaunch {
   float* topk_w;
   int32_t* plan;
   // router workgroups are blockIdx < router_wgs; in the fused block the
-  // remaining shared_tiles workgroups run the shared expert's gate/up (ex)
+  // remaining shared_tiles workgroups run the shared expert's gate/up (ex);
+  // router_arrivals workgroups arrive on done_counter
   int router_wgs;
   int shared_tiles;
+  int router_arrivals;
   ExpertLaunch ex;
+  // MFMA shape: K in ks_n slices of ks_steps 32-steps; with ks_n > 1 fp32
+  // partial sums [ks_n][M][N] in part, one arrival counter per 64-row group
+  int ks_n, ks_steps;
+  float* part;
+  uint32_t* rg_counter;
 };
 
 struct CombineLaunch {
@@ -111,6 +118,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // Row blocks of the skinny kernel for a given variant (host-side geometry).
 int skinny_rows_per_block(int variant, int router);
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router);
+// K slices of the MFMA shape (also sizes the partial-sum workspace)
+void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps);
 int shared_up_tiles_host(const ExpertLaunch& ex, int nw);
 
 }  // namespace moe

@@ -57,9 +57,13 @@ __device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n
 // Top-k of every token: waves take tokens wave, wave + nw, ..., with the
 // logits of four tokens loaded before any is used (one memory round trip
 // per group); ids and weights go to LDS and to the caller's arrays.
+constexpr int kTopkWaves = 8;   // waves that select (each holds a TopkScratch)
+
 __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* s_tk, int32_t* s_ids, float* s_w) {
   constexpr int QB = 4;
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  const int nw = (blockDim.x >> 6) < kTopkWaves ? (blockDim.x >> 6) : kTopkWaves;
+  const int wave = threadIdx.x >> 6;
+  if (wave >= nw) return;
   const int E = a.N, M = a.M, k = a.k;
   for (int t0 = wave; t0 < M; t0 += nw * QB) {
     float lv[QB][kNI];
@@ -81,7 +85,7 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
 __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   __shared__ int32_t s_ids[kMaxB * kMaxK];
   __shared__ float s_w[kMaxB * kMaxK];
-  __shared__ TopkScratch s_tk[16];
+  __shared__ TopkScratch s_tk[kTopkWaves];
   __shared__ unsigned long long s_mask[kMaxE];
   __shared__ int s_cnt[kMaxE];
   __shared__ int s_act[kMaxE];
@@ -102,27 +106,31 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   __syncthreads();
   // exclusive prefix sums over experts of slot counts and of "is active",
   // packed in one int (counts <= 1024 in the low half, actives <= 512 in
-  // the high half): a DPP scan per wave, wave totals through LDS.
-  __shared__ int s_wtot[16];
-  const int nwv = (E + 63) >> 6;
-  int incl = 0, packed = 0;
-  if (tid < nwv * 64) {
-    const int c = tid < E ? __popcll(s_mask[tid]) : 0;
-    packed = c | ((c > 0 ? 1 : 0) << 16);
-    incl = wave_incl_scan(packed);
-    if (lane == 63) s_wtot[wave] = incl;
+  // the high half): a DPP scan per 64-expert group (waves take groups in
+  // turn, so any workgroup size works), group totals through LDS.
+  __shared__ int s_wtot[kMaxE / 64];
+  __shared__ int s_incl[kMaxE];
+  const int nwv = (E + 63) >> 6, nw = blockDim.x >> 6;
+  for (int grp = wave; grp < nwv; grp += nw) {
+    const int e = grp * 64 + lane;
+    const int c = e < E ? __popcll(s_mask[e]) : 0;
+    const int packed = c | ((c > 0 ? 1 : 0) << 16);
+    const int incl = wave_incl_scan(packed);
+    s_incl[e] = incl - packed;   // exclusive within the group
+    if (lane == 63) s_wtot[grp] = incl;
   }
   __syncthreads();
-  if (tid < E) {
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int grp = e >> 6;
     int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wtot[w];
-    const int ex = base + incl - packed;
-    s_cnt[tid] = ex & 0xffff;
-    s_act[tid] = ex >> 16;
+    for (int g = 0; g < grp; ++g) base += s_wtot[g];
+    const int ex = base + s_incl[e];
+    s_cnt[e] = ex & 0xffff;
+    s_act[e] = ex >> 16;
   }
   if (tid == 0) {
     int tot = 0;
-    for (int w = 0; w < nwv; ++w) tot += s_wtot[w];
+    for (int g = 0; g < nwv; ++g) tot += s_wtot[g];
     s_n = tot >> 16;
   }
   __syncthreads();
@@ -147,7 +155,7 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
 __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   __shared__ int s_flag;
   if (!a.router || !a.finish) return;
-  if (!arrive_last(a.done_counter, (uint32_t)a.router_wgs, &s_flag)) return;
+  if (!arrive_last(a.done_counter, (uint32_t)a.router_arrivals, &s_flag)) return;
   route_finish(a);
 }
 
@@ -219,90 +227,207 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
 
 // ---- MFMA kernel (bf16) --------------------------------------------------
 
-// Workgroup: 16 weight rows (A operand: lane l holds row l%16, K elements
-// 8*(l/16) .. +7 of each 32-wide step) against NT tiles of 16 activation
-// rows (B operand: lane l holds token l%16 of the tile, same K elements).
-// Wave w takes the 4-step blocks w, w + NW, ... (128 K elements per row, 256
-// contiguous bytes, over four back-to-back loads).  The accumulator of tile
-// nt holds, in lane l, rows 4*(l/16)+i, token l%16.
+// Workgroup of 4 waves = 64 weight rows (wave w: rows n0 + 16 w .. + 15, the
+// A operand of v_mfma_f32_16x16x32_bf16) over one K slice (blockIdx ->
+// row group, slice).  The slice's activation rows pass through LDS in chunks
+// of kChunk 32-steps: loaded once per workgroup with coalesced 128-bit loads
+// and read by all 4 waves as the B operand (the per-wave loads of a 16-token
+// B tile touch 16 cache lines each; that traffic, four times the weight
+// bytes at 64 tokens, saturated the L1 address path).  Weights for the next
+// chunk and activations for the next chunk are requested before the current
+// chunk is multiplied; two weight buffers are used in turn.  With several
+// slices the workgroups store fp32 partial sums [slice][M][N]; the last of a
+// row group's slices to arrive adds them in slice order (deterministic).
+constexpr int kMfmaRows = 64;
+constexpr int kMfmaWaves = 4;
+constexpr int kMaxSlices = 8;
+constexpr int kChunk = 8;                   // 32-steps per LDS chunk
+constexpr int kXRow = kChunk * 64 + 16;     // bytes per token row in LDS (padded)
+
+void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
+  (void)M;
+  const int rg = (N + kMfmaRows - 1) / kMfmaRows;
+  const int J = K / 32;
+  const int nchunk = (J + kChunk - 1) / kChunk;
+  int ks = 256 / rg;                         // at most one workgroup per CU:
+  if (ks > kMaxSlices) ks = kMaxSlices;      // a second one would double the time;
+                                             // the cap bounds the partial traffic
+  if (ks > nchunk) ks = nchunk;
+  if (ks < 1) ks = 1;
+  const int chunks = (nchunk + ks - 1) / ks;
+  *ks_steps = chunks * kChunk;
+  *ks_n = (J + *ks_steps - 1) / *ks_steps;
+}
+
 template <int NT, bool ROUTER>
-__global__ __launch_bounds__(512) void skinny_mfma_kernel(SkinnyLaunch a) {
-  constexpr int SB = 4;  // K steps per block
-  extern __shared__ float s_dyn[];  // [NW][NT][64][4]
+__global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaunch a) {
+  __shared__ __align__(16) unsigned char s_x[NT * 16 * kXRow];
   if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
+    extern __shared__ float s_dyn[];
     shared_up_task<bf16_t, kPathMfma>(a.ex, blockIdx.x - a.router_wgs, s_dyn);
     return;
   }
-  const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int PIECES = NT * 16 * kChunk * 4;                 // 16-byte pieces per chunk
+  constexpr int PPT = (PIECES + kMfmaWaves * 64 - 1) / (kMfmaWaves * 64);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int rgi = blockIdx.x / a.ks_n, ks = blockIdx.x % a.ks_n;
+  const int n0 = rgi * kMfmaRows + wave * 16;
   const int J = a.K / 32;
+  const int s0 = ks * a.ks_steps;
+  const int s1 = s0 + a.ks_steps < J ? s0 + a.ks_steps : J;
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
-  const bf16_t* wr = W + (size_t)(n0 + row < a.N ? n0 + row : a.N - 1) * a.K;
-  const bf16_t* xr[NT];
-  bool xok[NT];
+  const bool wok = n0 + row < a.N;
+  const bf16_t* wr = W + (size_t)(wok ? n0 + row : a.N - 1) * a.K + kq * 8;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // activation pieces of this thread: p = tid + 256 i -> token p / (4 kChunk), piece p % (4 kChunk)
+  auto ld_x = [&](int c, u32x4(&xv)[PPT]) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int tok = nt * 16 + row;
-    xok[nt] = tok < a.M;
-    xr[nt] = X + (size_t)(xok[nt] ? tok : 0) * a.K;
-  }
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + i * kMfmaWaves * 64;
+      const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
+      const int j = c + q / 4;
+      const int tc = t < a.M ? t : 0, jc = j < s1 ? j : s1 - 1;
+      xv[i] = ld128(X + (size_t)tc * a.K + (size_t)jc * 32 + (q & 3) * 8);
+    }
+  };
+  static_assert(PIECES % (kMfmaWaves * 64) == 0, "whole pieces per thread");
+  auto st_x = [&](int c, const u32x4(&xv)[PPT]) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + i * kMfmaWaves * 64;
+      const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
+      const bool ok = t < a.M && c + q / 4 < s1;
+      *reinterpret_cast<u32x4*>(s_x + t * kXRow + q * 16) = ok ? xv[i] : zero;
+    }
+  };
+  // weight rows of chunk c (past the slice end: an activation row, cached)
+  auto ld_w = [&](int c, bool real, u32x4(&wv)[kChunk]) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int j = c + u < s1 ? c + u : s1 - 1;
+      wv[u] = ld128_stream(real ? wr + (size_t)j * 32 : X);
+    }
+  };
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_kloop<NT, SB>(wr, n0 + row < a.N, xr, xok, kq, J, wave, nw, acc);
+  // steps of a partial chunk past the slice end hold zero activations in LDS
+  // (st_x), so every chunk is multiplied whole, without a branch per step
+  auto mul = [&](const u32x4(&wv)[kChunk]) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int u = 0; u < kChunk; ++u) {
+      const u32x4 av = wok ? wv[u] : zero;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_dyn[((wave * NT + nt) * 64 + lane) * 4 + i] = acc[nt][i];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < NT * 256; idx += blockDim.x) {
-    const int nt = idx >> 8, l = (idx >> 2) & 63, i = idx & 3;
-    float v = 0.f;
-    for (int w = 0; w < nw; ++w) v += s_dyn[((w * NT + nt) * 64 + l) * 4 + i];
-    const int n = n0 + 4 * (l >> 4) + i, t = nt * 16 + (l & 15);
-    if (n < a.N && t < a.M) finish_value(a, t, n, v);
+      for (int nt = 0; nt < NT; ++nt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(s_x + (nt * 16 + row) * kXRow + (u * 4 + kq) * 16);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                          __builtin_bit_cast(bf16x8, bv), acc[nt], 0, 0, 0);
+      }
+    }
+  };
+  u32x4 xv[PPT], w0[kChunk], w1[kChunk];
+  int c = s0;
+  ld_x(c, xv);
+  ld_w(c, true, w0);
+  // Barriers here only order LDS (lds_barrier): a full __syncthreads would
+  // also wait for every global load in flight, the weight prefetch included.
+  for (;;) {
+    lds_barrier();              // the previous chunk's LDS reads are done
+    st_x(c, xv);
+    lds_barrier();
+    int cn = c + kChunk;
+    bool more = cn < s1;
+    ld_x(more ? cn : c, xv);
+    ld_w(more ? cn : c, more, w1);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the products
+    mul(w0);
+    if (!more) break;
+    c = cn;
+    lds_barrier();
+    st_x(c, xv);
+    lds_barrier();
+    cn = c + kChunk;
+    more = cn < s1;
+    ld_x(more ? cn : c, xv);
+    ld_w(more ? cn : c, more, w0);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w1);
+    if (!more) break;
+    c = cn;
+  }
+  if (a.ks_n == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 4 * kq + i, t = nt * 16 + row;
+        if (n < a.N && t < a.M) finish_value(a, t, n, acc[nt][i]);
+      }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 4 * kq + i, t = nt * 16 + row;
+        if (n < a.N && t < a.M) a.part[((size_t)ks * a.M + t) * a.N + n] = acc[nt][i];
+      }
+    __shared__ int s_last;
+    if (!arrive_last(a.rg_counter + rgi, (uint32_t)a.ks_n, &s_last)) return;
+    // each thread: 4 consecutive rows of one token per pass, all slices'
+    // partials requested before any is added (one memory round trip)
+    const int nb = rgi * kMfmaRows;
+    for (int idx = tid * 4; idx < kMfmaRows * a.M; idx += blockDim.x * 4) {
+      const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
+      const bool vec = (a.N & 3) == 0 && n + 4 <= a.N;   // else scalar below
+      const int nc = vec ? n : 0;
+      f32x4 pv[kMaxSlices];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) {
+        const int qc = q < a.ks_n ? q : 0;
+        pv[q] = *reinterpret_cast<const f32x4*>(&a.part[((size_t)qc * a.M + t) * a.N + nc]);
+      }
+      if (vec) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kMaxSlices; ++q)
+          if (q < a.ks_n) v += pv[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) finish_value(a, t, n + i, v[i]);
+      } else {
+        for (int i = 0; i < 4 && n + i < a.N; ++i) {
+          float v = 0.f;
+          for (int q = 0; q < a.ks_n; ++q) v += ld_after_acquire(&a.part[((size_t)q * a.M + t) * a.N + n + i]);
+          finish_value(a, t, n + i, v);
+        }
+      }
+    }
   }
   if constexpr (ROUTER) router_tail(a);
 }
 
-// ---- host side -----------------------------------------------------------
-
 int skinny_rows_per_block(int variant, int router) {
-  if (variant == VAR_MFMA) return 16;
+  if (variant == VAR_MFMA) return kMfmaRows;
   if (router || variant == VAR_SPLITK) return 4;
   return 2;
 }
-
-// Waves per workgroup (the in-workgroup K split): enough for ~1536 waves per
-// launch, at most 16, and no wave with less than one 1 KB block per row.
-// The router takes 16 waves outright: it has few rows, and each of its
-// workgroups pays one device-scope release on the completion counter.
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router) {
-  // The router's finish needs one thread per expert (E <= 512): its
-  // workgroups always have 16 waves (vector) or 8 (MFMA); waves beyond the
-  // K range just idle through the product.
-  if (router) return variant == VAR_MFMA ? 8 : 16;
+  (void)M;
+  if (variant == VAR_MFMA) return kMfmaWaves;
+  // The router's workgroups have 16 waves (the finish is shared among them);
+  // waves beyond the K range just idle through the product.
+  if (router) return 16;
   const int rows = skinny_rows_per_block(variant, router);
   const int nwg = (N + rows - 1) / rows;
   int nw = (1536 + nwg - 1) / nwg;
-  int maxw = variant == VAR_MFMA ? (K / 32) / 4 : (K / (bf16 ? 8 : 4)) / 64;
-  if (maxw > (variant == VAR_MFMA ? 8 : 16)) maxw = variant == VAR_MFMA ? 8 : 16;
-  if (variant == VAR_MFMA) {
-    // dynamic LDS nw * nt KB plus the router's static LDS within 64 KB
-    const int nt = (M + 15) / 16;
-    if (maxw > 40 / nt) maxw = 40 / nt;
-  }
+  int maxw = (K / (bf16 ? 8 : 4)) / 64;
+  if (maxw > 16) maxw = 16;
   if (maxw < 1) maxw = 1;
   if (nw > maxw) nw = maxw;
   if (nw < 1) nw = 1;
   return nw;
 }
-
-// Shared-expert gate/up workgroups appended to the router grid: the vector
-// shape takes one pair per wave, the MFMA shape four pairs per workgroup.
 int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
   const bool mfma = expert_paths(ex.bf16, ex.force, ex.B) != kPathValu;
   const int pp = nw / 2;
@@ -321,16 +446,25 @@ static void launch_as(const SkinnyLaunch& a, K router_kernel, K plain_kernel, di
 hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
   SkinnyLaunch a = a0;
   const int rows = skinny_rows_per_block(a.variant, a.router);
-  const int nwg = (a.N + rows - 1) / rows;
+  const int nrg = (a.N + rows - 1) / rows;
   const int nw = a.S;
+  if (a.variant == VAR_MFMA) {
+    skinny_mfma_slices(a.M, a.N, a.K, &a.ks_n, &a.ks_steps);
+  } else {
+    a.ks_n = 1;
+    a.ks_steps = 0;
+  }
+  const int nwg = nrg * a.ks_n;
   a.router_wgs = nwg;
+  a.router_arrivals = nrg;
   const int extra = (a.router && a.ex.Ws13) ? shared_up_tiles_host(a.ex, nw) : 0;
   a.shared_tiles = extra;
   dim3 grid((unsigned)(nwg + extra)), block((unsigned)(64 * nw));
   const char* name = "?";
   if (a.variant == VAR_MFMA) {
+    if (a.ks_n > 1 && (!a.part || !a.rg_counter)) return hipErrorInvalidValue;
     const int nt = (a.M + 15) / 16;
-    const size_t lds = (size_t)nw * nt * 256 * sizeof(float);
+    const size_t lds = extra ? (size_t)nw * nt * 256 * sizeof(float) : 0;   // the shared gate/up's reduction
     switch (nt) {
       case 1: launch_as(a, skinny_mfma_kernel<1, true>, skinny_mfma_kernel<1, false>, grid, block, lds, st); break;
       case 2: launch_as(a, skinny_mfma_kernel<2, true>, skinny_mfma_kernel<2, false>, grid, block, lds, st); break;
@@ -371,8 +505,9 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
     name = "gemv";
   }
   if (desc)
-    snprintf(desc, desc_len, "%s M=%d N=%d K=%d waves/wg=%d grid=%d%s%s", name, a.M, a.N, a.K, nw, nwg,
-             extra ? " +shared gate/up" : "", a.router && !a.finish ? " logits-only" : "");
+    snprintf(desc, desc_len, "%s M=%d N=%d K=%d waves/wg=%d grid=%d%s%s%s", name, a.M, a.N, a.K, nw, nwg,
+             a.ks_n > 1 ? " k-slices" : "", extra ? " +shared gate/up" : "",
+             a.router && !a.finish ? " logits-only" : "");
   return hipGetLastError();
 }
 

@@ -48,8 +48,10 @@ def test_workspace_bytes():
     assert f(mb.OP_EXPERT_FFN, mb.DT_BF16, B=64, d=7168, E=384, k=8, I=256, Is=256) >= (512 + 64) * 256 * 4
     blk = f(mb.OP_BLOCK, mb.DT_BF16, B=8, d=7168, E=384, k=8, I=128, Is=128)
     assert blk >= f(mb.OP_ROUTE, mb.DT_BF16, B=8, d=7168, E=384, k=8) + (8 * 8 + 8) * 128 * 4
-    # the dense product splits K inside a workgroup: no workspace at all
-    assert f(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=64, N=3072, K=7168) == 0
+    # the dense product: no workspace for fp32 (vector shapes only); bf16
+    # sizes the MFMA shape's K-slice partial sums (fp32 [slices][B][N])
+    assert f(mb.OP_SKINNY_GEMM, mb.DT_F32, B=8, N=3072, K=7168) == 0
+    assert f(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=64, N=3072, K=7168) >= 2 * 64 * 3072 * 4
 
 
 def status_str():
