@@ -17,7 +17,9 @@ Inputs are resident in HBM before the timed region.  W warm-up steps, then
 exactly K timed steps between two synchronised HIP events.
 
 Prints ONE JSON line.  Besides the headline, it carries
-  roofline:     the dominant kernel (expert gate/up) timed with HIP events
+  roofline:     the dominant kernel (the fused block kernel where the block
+                runs as one launch, else the launch with the largest time)
+                timed with HIP events
                 that its own dispatch records (hipExtLaunchKernel, on the
                 launch stream), algorithmic bytes / duration against the
                 8 TB/s HBM peak; traffic = counter-measured HBM bytes per
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--kernel-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused"],
+                    help="moe_block schedule: one fused launch where it applies, or three launches")
     return ap.parse_args()
 
 
@@ -112,7 +116,9 @@ def run_moe(args, torch, mb, synth):
         mb.moe_block(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, s["Ws13"], s["Ws2"],
                      s["bias"], s["bias_ld"], topk_ids=s["ids"])
 
+    mb.set_block_schedule(args.schedule)
     ms = timed_loop(step, args, torch)
+    fused = "fused" in mb.last_variant()
     route_in_up = "top-k/plan" in mb.last_variant()
     # algorithmic bytes per set: every selected expert's weights once, the
     # router and shared expert, x (and bias) read once, out written once
@@ -125,11 +131,14 @@ def run_moe(args, torch, mb, synth):
     avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
     kern, kbytes = {}, {}
-    for name, kid in (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
-                      ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)):
+    launches = ((("block", mb.KERNEL_BLOCK),) if fused else
+                (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
+                 ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)))
+    for name, kid in launches:
         kern[name] = kernel_times(step, kid, args, torch, mb)
         # the profiled launches run sets warmup + steps + i (see kernel_times)
-        kbytes[name] = [per_set[(args.warmup + args.steps + i) % R][2][name] for i in range(len(kern[name]))]
+        sel = (lambda i: per_set[i][1]) if fused else (lambda i: per_set[i][2][name])
+        kbytes[name] = [sel((args.warmup + args.steps + i) % R) for i in range(len(kern[name]))]
     # the dominant kernel: the largest share of the block's time
     dom = max(kern, key=lambda k: sum(kern[k]))
     durs = kern[dom]
@@ -157,7 +166,7 @@ def run_moe(args, torch, mb, synth):
 
 # symbol (as a kernel trace names it) of each launch of the block
 KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel (router mode)", "expert_up": "expert_up_kernel",
-                 "expert_down_combine": "expert_down_combine_kernel"}
+                 "expert_down_combine": "expert_down_combine_kernel", "block": "moe_block_kernel"}
 
 
 def launch_bytes(cfg, n, esz, bias_b, route_in_up):

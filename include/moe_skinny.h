@@ -113,6 +113,15 @@ const char* moe_last_variant(void);
  * setting. */
 int moe_set_variant(int variant);
 
+/* Schedule of moe_block: MOE_SCHEDULE_AUTO (currently three launches: on
+ * MI355X the fused launch's two grid-wide barriers cost more than the kernel
+ * boundaries they replace), MOE_SCHEDULE_LAUNCHES (three launches) or
+ * MOE_SCHEDULE_FUSED (one launch; MOE_EUNSUPPORTED outside its scope).  Also set by the MOE_BLOCK_SCHEDULE environment
+ * variable (auto, launches, fused).  Both schedules give identical bits.
+ * Returns the previous setting. */
+typedef enum { MOE_SCHEDULE_AUTO = 0, MOE_SCHEDULE_LAUNCHES = 1, MOE_SCHEDULE_FUSED = 2 } moe_schedule_t;
+int moe_set_block_schedule(int schedule);
+
 /* int32 words of a routing plan for B tokens, top-k of E experts:
  * 2 + 2*min(E, B*k) + B*k.  Layout, with maxa = min(E, B*k):
  *   plan[0]                    n, the number of distinct experts selected
@@ -137,7 +146,8 @@ typedef enum {
   MOE_KERNEL_EXPERT_UP = 1,    /* expert gate/up + SwiGLU */
   MOE_KERNEL_EXPERT_DOWN = 2,  /* expert down projection */
   MOE_KERNEL_COMBINE = 3,      /* weighted combine */
-  MOE_KERNEL_SKINNY = 4        /* dense skinny product */
+  MOE_KERNEL_SKINNY = 4,       /* dense skinny product */
+  MOE_KERNEL_BLOCK = 5         /* the whole block in one launch (moe_block) */
 } moe_kernel_t;
 
 /* Profiling hook (for timing one kernel with HIP events on the stream it is
@@ -208,8 +218,18 @@ moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const 
 moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
                          int has_shared, void* out, void* stream);
 
-/* The whole block in three launches, every intermediate in ws.
- * Small batch on the vector shape (B*k <= 64):
+/* The whole block, every intermediate in ws.
+ * Small batch on the vector shape with short expert rows (B*k <= 64, I and
+ * Is at most 16 vector chunks -- 128 bf16, 64 fp32), on request ONE launch
+ * (schedule "fused"): one 16-wave workgroup per compute unit, all resident,
+ * runs router scoring (and the shared expert's gate/up), waits at a
+ * grid-wide barrier, selects the top-k and builds the plan in every
+ * workgroup, runs the routed gate/up, waits at a second barrier, then the
+ * down projection with the weighted combine.  The barrier words live in ws
+ * (count words return to zero after every call).  Used only when the
+ * device reports room for one workgroup per compute unit.
+ * By default, and outside that scope, three launches (schedule
+ * "launches"); with B*k <= 64:
  *   1. router scoring only (logits + bias to ws);
  *   2. gate/up + SwiGLU: every workgroup selects the top-k of all tokens
  *      and builds the plan itself (no handshake between workgroups); the

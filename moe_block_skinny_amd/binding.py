@@ -20,8 +20,10 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 DT_F32, DT_BF16 = 0, 1
 VARIANT_AUTO, VARIANT_GEMV, VARIANT_SPLITK, VARIANT_MFMA = range(4)
 OP_SKINNY_GEMM, OP_ROUTE, OP_EXPERT_FFN, OP_BLOCK = range(4)
-KERNEL_ROUTE, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_SKINNY = range(5)
+KERNEL_ROUTE, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_SKINNY, KERNEL_BLOCK = range(6)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "splitk": VARIANT_SPLITK, "mfma": VARIANT_MFMA}
+SCHEDULE_AUTO, SCHEDULE_LAUNCHES, SCHEDULE_FUSED = range(3)
+SCHEDULES = {"auto": SCHEDULE_AUTO, "launches": SCHEDULE_LAUNCHES, "fused": SCHEDULE_FUSED}
 
 # name: (restype, argtypes)
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -31,6 +33,7 @@ SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_last_variant": (ctypes.c_char_p, []),
     "moe_set_variant": (_I, [_I]),
+    "moe_set_block_schedule": (_I, [_I]),
     "moe_plan_words": (_I, [_I, _I, _I]),
     "moe_workspace_bytes": (_Z, [_I] * 10),
     "moe_workspace_init": (_I, [_P, _Z, _P]),
@@ -102,6 +105,11 @@ def last_variant() -> str:
 def set_variant(name_or_id) -> int:
     v = VARIANTS[name_or_id] if isinstance(name_or_id, str) else int(name_or_id)
     return lib.moe_set_variant(v)
+
+
+def set_block_schedule(name_or_id) -> int:
+    v = SCHEDULES[name_or_id] if isinstance(name_or_id, str) else int(name_or_id)
+    return lib.moe_set_block_schedule(v)
 
 
 def plan_words(B: int, k: int, E: int) -> int:

@@ -27,6 +27,7 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local char g_variant[256] = "";
 std::atomic<int> g_force{-1};  // -1: not yet read from the environment
+std::atomic<int> g_sched{-1};  // block schedule; -1: not yet read from the environment
 
 constexpr int kMaxI = 256;   // kMaxB, kMaxE, kMaxK: route_core.hpp
 constexpr size_t kAlign = 256;
@@ -37,9 +38,9 @@ struct ProfileHook {
   hipEvent_t start = nullptr, stop = nullptr;
 } g_prof;
 
-static_assert(K_ROUTE == MOE_KERNEL_ROUTE && K_EXPERT_UP == MOE_KERNEL_EXPERT_UP &&
-                  K_EXPERT_DOWN == MOE_KERNEL_EXPERT_DOWN && K_COMBINE == MOE_KERNEL_COMBINE &&
-                  K_SKINNY == MOE_KERNEL_SKINNY,
+static_assert((int)K_ROUTE == (int)MOE_KERNEL_ROUTE && (int)K_EXPERT_UP == (int)MOE_KERNEL_EXPERT_UP &&
+                  (int)K_EXPERT_DOWN == (int)MOE_KERNEL_EXPERT_DOWN && (int)K_COMBINE == (int)MOE_KERNEL_COMBINE &&
+                  (int)K_SKINNY == (int)MOE_KERNEL_SKINNY && (int)K_BLOCK == (int)MOE_KERNEL_BLOCK,
               "kernel ids");
 
 moe_status_t fail(moe_status_t s, const char* fmt, ...) {
@@ -63,6 +64,22 @@ int forced() {
     int expect = -1;
     g_force.compare_exchange_strong(expect, f);
     f = g_force.load();
+  }
+  return f;
+}
+
+int schedule() {
+  int f = g_sched.load();
+  if (f < 0) {
+    f = MOE_SCHEDULE_AUTO;
+    const char* e = getenv("MOE_BLOCK_SCHEDULE");
+    if (e) {
+      if (!strcmp(e, "launches")) f = MOE_SCHEDULE_LAUNCHES;
+      else if (!strcmp(e, "fused")) f = MOE_SCHEDULE_FUSED;
+    }
+    int expect = -1;
+    g_sched.compare_exchange_strong(expect, f);
+    f = g_sched.load();
   }
   return f;
 }
@@ -143,7 +160,7 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 struct BlockWs {
   SkinnyWs route;
   ExpertWs ffn;
-  size_t route_off, ffn_off, ids, w, plan, total;
+  size_t route_off, ffn_off, ids, w, plan, sync, total;
 };
 
 BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
@@ -161,6 +178,8 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   o = up(o + (size_t)B * k * 4);
   b.plan = o;
   o = up(o + (size_t)moe_plan_words(B, k, E) * 4);
+  b.sync = o;   // fused kernel: 2 count lines, 2 x kBlockMaxGrid flag lines, a status line
+  o = up(o + (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4);
   b.total = o;
   return b;
 }
@@ -212,14 +231,11 @@ moe_status_t hip_status(hipError_t e, const char* what) {
 
 // ---- launch helpers (arguments already validated) ---------------------------
 
-moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
-                       const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
-                       float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
-                       const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr) {
+// Router launch arguments (variant v already resolved).
+SkinnyLaunch route_launch(int dt, int v, int B, int d, int E, int k, const void* X, const void* Wr,
+                          const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
+                          float* logits_out, char* ws, int finish) {
   const int bf16 = dt == MOE_DT_BF16;
-  int v;
-  moe_status_t s = resolve_skinny(bf16, B, d, &v);
-  if (s) return s;
   const SkinnyWs L = skinny_ws(B, E, d, bf16, true);
   SkinnyLaunch a = {};
   a.bf16 = bf16;
@@ -234,7 +250,6 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.S = skinny_default_splits(v, bf16, B, E, d, 1);
   a.router = 1;
   a.finish = finish;
-  if (shared) a.ex = *shared;
   a.bias = bias;
   a.bias_ld = bias_ld;
   a.logits = reinterpret_cast<float*>(ws + L.logits);
@@ -244,6 +259,18 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
   a.topk_ids = ids;
   a.topk_w = w;
   a.plan = plan;
+  return a;
+}
+
+moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
+                       const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
+                       float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
+                       const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr) {
+  int v;
+  moe_status_t s = resolve_skinny(dt == MOE_DT_BF16, B, d, &v);
+  if (s) return s;
+  SkinnyLaunch a = route_launch(dt, v, B, d, E, k, X, Wr, bias, bias_ld, ids, w, plan, logits_out, ws, finish);
+  if (shared) a.ex = *shared;
   if (logits) *logits = a.logits;
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
 }
@@ -323,7 +350,7 @@ moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event)
     g_prof.start = g_prof.stop = nullptr;
     return MOE_OK;
   }
-  if (kernel < MOE_KERNEL_ROUTE || kernel > MOE_KERNEL_SKINNY) return fail(MOE_EINVAL, "unknown kernel %d", kernel);
+  if (kernel < MOE_KERNEL_ROUTE || kernel > MOE_KERNEL_BLOCK) return fail(MOE_EINVAL, "unknown kernel %d", kernel);
   if (!start_event || !stop_event) return fail(MOE_EINVAL, "both events or neither");
   g_prof.kernel = kernel;
   g_prof.start = reinterpret_cast<hipEvent_t>(start_event);
@@ -336,6 +363,13 @@ int moe_set_variant(int variant) {
   const int prev = forced();
   if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_MFMA) return prev;
   g_force.store(variant);
+  return prev;
+}
+
+int moe_set_block_schedule(int sched) {
+  const int prev = schedule();
+  if (sched < MOE_SCHEDULE_AUTO || sched > MOE_SCHEDULE_FUSED) return prev;
+  g_sched.store(sched);
   return prev;
 }
 
@@ -526,7 +560,33 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   // kernel carries only the vector gate/up, the MFMA one only the MFMA one).
   const int paths = expert_paths(bf16, force, B);
   const bool route_in_up = paths == kPathValu && v != VAR_MFMA && B * k <= 64;
+  const int sched = schedule();
+  // AUTO takes the three launches: on MI355X each grid-wide barrier of the
+  // fused kernel (atomic arrival, flag broadcast, acquire) costs more than
+  // a kernel boundary, so the fused launch is only selected on request.
+  const bool fused = route_in_up && sched == MOE_SCHEDULE_FUSED && moe_block_fused_grid(ex, bf16, B) > 0;
+  if (sched == MOE_SCHEDULE_FUSED && !fused)
+    return fail(MOE_EUNSUPPORTED, "the fused block kernel does not cover these sizes (B*k <= 64, short expert rows)");
   char d1[200] = "", d2[128] = "", d3[128] = "";
+  if (fused) {
+    // The whole block in one launch (fused.hip)
+    BlockLaunch f = {};
+    f.r = route_launch(dtype, v, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, 0);
+    f.ex = ex;
+    f.ex.skip_shared = 0;
+    f.ex.logits = f.r.logits;
+    f.ex.ids_out = ids;
+    f.ex.w_out = tw;
+    f.ex.plan_out = plan;
+    uint32_t* sync = reinterpret_cast<uint32_t*>(w + L.sync);
+    f.count = sync;
+    f.flags_r = sync + 2 * kFlagStride;
+    f.flags_h = f.flags_r + (size_t)kBlockMaxGrid * kFlagStride;
+    f.status = f.flags_h + (size_t)kBlockMaxGrid * kFlagStride;
+    if ((s = hip_status(launch_moe_block_fused(f, st, d1, sizeof d1), "fused block launch"))) return s;
+    record("moe_block", B, d1);
+    return MOE_OK;
+  }
   if (route_in_up) {
     ex.skip_shared = 0;
     ex.ids_out = ids;

@@ -297,6 +297,76 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   return last;
 }
 
+// Store of a value that workgroups of the same launch on other XCDs will
+// read: a device-coherent store (relaxed agent-scope atomic; on this GPU a
+// store that writes through this XCD's L2), complete at device scope once
+// the storing wave's memory counter has drained.  Publishing such values
+// then needs no L2 write-back (buffer_wbl2), which every XCD serialises
+// across its workgroups (a few hundred ns each).
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Grid-wide barrier in two halves, for a launch whose workgroups are all
+// resident at once.  Words in caller memory, zero before the first use: a
+// count, and one flag word per workgroup, kFlagStride words apart (each on a
+// line of its own: many workgroups polling one line would queue behind each
+// other at the memory side).
+// grid_arrive: every wave waits until its stores are complete (the values
+// other workgroups read are st_coherent stores, so complete means visible
+// at device scope), then thread 0 counts the workgroup on `count` with a
+// relaxed atomic and returns the workgroup's flag read before arriving.  The
+// workgroup that arrives last of `expected` saw every other arrival, each
+// made after that workgroup's stores completed; it resets the count and
+// stores flag + 1 into every workgroup's flag.
+// grid_wait: thread 0 polls its flag until it moves on, then acquires
+// (invalidating this compute unit's L1 and the XCD's L2 lines that might
+// hold stale copies) and waits for that to finish; the barrier after it
+// orders the other waves' loads after the invalidate (they share those
+// caches; one invalidate per wave would be paid 16 times per workgroup).
+// Work placed between the halves overlaps the wait.  The count returns to
+// zero after every barrier.  A wait gives up after spin_limit polls and sets
+// *status to 1, so no wave is left spinning.
+constexpr int kFlagStride = 32;   // 128 bytes
+
+__device__ __forceinline__ uint32_t grid_arrive(uint32_t* count, uint32_t* flags, uint32_t expected, int* s_last) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* mine = flags + (size_t)blockIdx.x * kFlagStride;
+  uint32_t g = 0u;
+  if (threadIdx.x == 0) {
+    g = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == expected - 1u;
+    if (last) __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last[0] = last ? 1 : 0;
+    s_last[1] = (int)g;
+  }
+  __syncthreads();
+  if (s_last[0] && threadIdx.x < 64) {
+    const uint32_t next = (uint32_t)s_last[1] + 1u;
+    for (uint32_t i = threadIdx.x; i < gridDim.x; i += 64)
+      __hip_atomic_store(flags + (size_t)i * kFlagStride, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return g;
+}
+
+__device__ __forceinline__ void grid_wait(const uint32_t* flags, uint32_t g0, int spin_limit, uint32_t* status) {
+  if (threadIdx.x == 0) {
+    const uint32_t* mine = flags + (size_t)blockIdx.x * kFlagStride;
+    for (int n = 0; __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0; ++n) {
+      if (n >= spin_limit) {
+        __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+}
+
 // Read of a value another workgroup of this launch produced, by the last
 // workgroup after arrive_last's acquire fence.  A plain load: the fence keeps
 // the compiler from moving it above the synchronisation and has invalidated

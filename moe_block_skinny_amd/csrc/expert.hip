@@ -122,18 +122,6 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
 
 // ---- down projection + combine -> out ----------------------------------------
 
-// out[t][r] = sum_j w[t][j] * y[t*k+j][r] (j ascending), then + y[B*k+t][r]
-// for the shared expert: fp32 fused multiply-adds in this order.
-template <typename LoadY>
-__device__ __forceinline__ float combine_one(const float* w_t, int k, int has_shared, LoadY y) {
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < k) acc = __builtin_fmaf(w_t[j], y(j), acc);
-  if (has_shared) acc += y(k);
-  return acc;
-}
-
 // RT output rows per workgroup: 32 on the vector-only path with short rows
 // (I, Is <= 16 chunks: 8 loads per lane per entry, so the whole grid is
 // resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays

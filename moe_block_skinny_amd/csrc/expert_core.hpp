@@ -61,16 +61,18 @@ __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s
 // Routing inside the gate/up launch (B*k <= 64): the workgroup selects the
 // top-k of all B tokens from the router's logits [B][E] (bias included) and
 // builds the plan in LDS -- the same functions, hence the same bits, as the
-// router's finishing workgroup.  The last workgroup of the grid also stores
+// router's finishing workgroup.  s_tk: one TopkScratch per selecting wave
+// (at most kTopkWaves).  The last workgroup of the grid also stores
 // ids, weights and plan for the down launch and the caller.  Ends with a
 // barrier.
 __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s_plan, TopkScratch* s_tk,
                                                int32_t* s_ids, float* s_w) {
   constexpr int QB = 2;
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+  const int nw = (blockDim.x >> 6) < kTopkWaves ? (blockDim.x >> 6) : kTopkWaves;
+  const int wave = threadIdx.x >> 6;
   const bool writer = blockIdx.x == gridDim.x - 1;
   const int B = a.B, E = a.E, k = a.k;
-  for (int t0 = wave; t0 < B; t0 += nw * QB) {
+  for (int t0 = wave; wave < nw && t0 < B; t0 += nw * QB) {
     float lv[QB][kNI];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
@@ -171,9 +173,12 @@ __host__ __device__ __forceinline__ int expert_paths(int bf16, int force, int B)
 
 // Pair i (gate row i, up row I+i) of entry v: this wave takes the `half`-th
 // of NH slices of d; h[srow][i] = silu(g) * u for the entry's tokens.  With
-// NH = 2 the two waves of a pair meet in s_part ([4 pairs][2][MB] floats,
-// pair slot ps) and the whole workgroup passes one barrier; with NH = 1 a
-// wave works alone.  Waves whose pair is past I still reach the barrier.
+// NH = 2 the two waves of a pair meet in s_part ([pair slots][2][8] floats,
+// pair slot ps; the stride is fixed so that pairs of entries with different
+// token counts can share a workgroup) and the whole workgroup passes one
+// barrier; with NH = 1 a wave works alone.  Waves whose pair is past I still
+// reach the barrier.
+constexpr int kPartStride = 8;
 template <typename T, int MB, int NH>
 __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i,
                                         int half, int ps, float* s_part) {
@@ -206,16 +211,16 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
     if (half == 1 && lane == 0) {
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
-        s_part[(ps * 2 + 0) * MB + t] = acc[0][t];
-        s_part[(ps * 2 + 1) * MB + t] = acc[1][t];
+        s_part[(ps * 2 + 0) * kPartStride + t] = acc[0][t];
+        s_part[(ps * 2 + 1) * kPartStride + t] = acc[1][t];
       }
     }
     __syncthreads();
     if (half == 1 || !live) return;
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
-      acc[0][t] += s_part[(ps * 2 + 0) * MB + t];
-      acc[1][t] += s_part[(ps * 2 + 1) * MB + t];
+      acc[0][t] += s_part[(ps * 2 + 0) * kPartStride + t];
+      acc[1][t] += s_part[(ps * 2 + 1) * kPartStride + t];
     }
   }
   if (live && lane < v.m) {
@@ -224,7 +229,7 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
 #pragma unroll
     for (int t = 0; t < MB; ++t)
       if (t == lane) sr = srow[t];
-    a.h[(size_t)sr * a.hld + i] = silu(g) * u;
+    st_coherent(&a.h[(size_t)sr * a.hld + i], silu(g) * u);
   }
 }
 
@@ -283,7 +288,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
       }
       int tok, sr;
       token_of(a, slots, v, t, tok, sr);
-      a.h[(size_t)sr * a.hld + i0 + q] = silu(g) * u;
+      st_coherent(&a.h[(size_t)sr * a.hld + i0 + q], silu(g) * u);
     }
   }
   __syncthreads();
@@ -316,6 +321,20 @@ __device__ __forceinline__ void shared_up_task(const ExpertLaunch& a, int tile, 
     const int pp = nw >> 1;
     up_valu_dispatch<T, 2>(a, nullptr, v, tile * pp + wave % pp, wave / pp, wave % pp, s_red);
   }
+}
+
+// ---- weighted combine ---------------------------------------------------------
+
+// out[t][r] = sum_j w[t][j] * y[t*k+j][r] (j ascending), then + y[B*k+t][r]
+// for the shared expert: fp32 fused multiply-adds in this order.
+template <typename LoadY>
+__device__ __forceinline__ float combine_one(const float* w_t, int k, int has_shared, LoadY y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < k) acc = __builtin_fmaf(w_t[j], y(j), acc);
+  if (has_shared) acc += y(k);
+  return acc;
 }
 
 // ---- down projection ---------------------------------------------------------

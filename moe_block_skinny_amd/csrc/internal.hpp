@@ -82,6 +82,27 @@ struct SkinnyLaunch {
   uint32_t* rg_counter;
 };
 
+// The whole block in one launch (fused kernel, small batch on the vector
+// shape): the router product r (logits into r.logits, 16-wave workgroups of
+// kBlockRouterRows rows), then in every workgroup the top-k and plan, the
+// gate/up of the routed experts, and the down projection with the weighted
+// combine (ex, with ex.down_rows rows per workgroup).  Workgroups meet at
+// two grid-wide barriers (grid_arrive / grid_wait: a count word each, zero
+// between calls, and a flag line per workgroup each); a wait that outlasts
+// spin_limit polls sets *status.
+constexpr int kBlockMaxGrid = 512;   // flag lines per barrier in the workspace
+struct BlockLaunch {
+  SkinnyLaunch r;
+  ExpertLaunch ex;
+  uint32_t* count;          // router barrier at [0], h barrier at [kFlagStride]
+  uint32_t* flags_r;        // kBlockMaxGrid flag lines of 128 bytes
+  uint32_t* flags_h;
+  uint32_t* status;         // 0; 1 after a wait gave up (never expected)
+  int router_tasks;         // ceil(E / kBlockRouterRows)
+  int shared_tasks;         // shared-expert gate/up tasks of 2 pairs
+  int spin_limit;
+};
+
 struct CombineLaunch {
   int out_bf16;
   int B, d, k, has_shared;
@@ -91,7 +112,9 @@ struct CombineLaunch {
 };
 
 // Kernel ids of the profiling hook (same values as the public moe_kernel_t).
-enum KernelId { K_ROUTE = 0, K_EXPERT_UP = 1, K_EXPERT_DOWN = 2, K_COMBINE = 3, K_SKINNY = 4, K_NONE = -1 };
+enum KernelId {
+  K_ROUTE = 0, K_EXPERT_UP = 1, K_EXPERT_DOWN = 2, K_COMBINE = 3, K_SKINNY = 4, K_BLOCK = 5, K_NONE = -1
+};
 
 // Events armed for kernel `id` by moe_profile_events (abi.cpp), if any.
 bool profile_events_for(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -114,6 +137,10 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
 hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// Fused block: the workgroups it would launch (0: the fused kernel cannot
+// hold the whole grid resident, so it must not be used), and the launch.
+int moe_block_fused_grid(const ExpertLaunch& ex, int bf16, int B);
+hipError_t launch_moe_block_fused(BlockLaunch& f, hipStream_t st, char* desc, size_t desc_len);
 
 // Row blocks of the skinny kernel for a given variant (host-side geometry).
 int skinny_rows_per_block(int variant, int router);

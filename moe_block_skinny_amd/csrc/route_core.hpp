@@ -27,6 +27,8 @@ constexpr int kMaxK = 16;
 constexpr int kMaxB = 64;
 constexpr int kNI = kMaxE / 64;   // logits per lane
 
+constexpr int kTopkWaves = 8;     // waves of a workgroup that select (each holds a TopkScratch)
+
 // LDS scratch of one wave for topk_wave.
 struct TopkScratch {
   uint64_t cand[kMaxE];

@@ -34,30 +34,16 @@
 #include "common.hpp"
 #include "expert_core.hpp"
 #include "internal.hpp"
+#include "skinny_core.hpp"
 
 namespace moe {
 
-
-// ---- epilogue ---------------------------------------------------------------
-
-__device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n, float v) {
-  if (a.router) {
-    if (a.bias) v += a.bias[(size_t)t * a.bias_ld + n];
-    a.logits[(size_t)t * a.N + n] = v;
-    if (a.logits_out) a.logits_out[(size_t)t * a.N + n] = v;
-  } else if (a.y_bf16) {
-    reinterpret_cast<bf16_t*>(a.Y)[(size_t)t * a.N + n] = f32_to_bf16(v);
-  } else {
-    reinterpret_cast<float*>(a.Y)[(size_t)t * a.N + n] = v;
-  }
-}
 
 // ---- router finish: top-k, weights, plan (one workgroup) ------------------
 
 // Top-k of every token: waves take tokens wave, wave + nw, ..., with the
 // logits of four tokens loaded before any is used (one memory round trip
 // per group); ids and weights go to LDS and to the caller's arrays.
-constexpr int kTopkWaves = 8;   // waves that select (each holds a TopkScratch)
 
 __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* s_tk, int32_t* s_ids, float* s_w) {
   constexpr int QB = 4;
@@ -161,67 +147,24 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
 
 // ---- vector-ALU kernels (gemv / splitk) ----------------------------------
 
-// Workgroup: RB weight rows starting at blockIdx.x * RB, all K.  Wave w
-// takes the 64-chunk blocks w, w + NW, w + 2 NW, ... of every row (one 1 KB
-// segment per row per load instruction); U blocks per lane are in flight.
+// Router rows per workgroup: E = 384 router rows spread over 192 compute
+// units (one 16-wave workgroup each).  A compute unit keeps only so many
+// loads in flight, so a launch that leaves CUs idle streams proportionally
+// slower: with 4 rows per workgroup the 96 workgroups took ~3x the time of
+// one memory round trip.
+constexpr int kRouterRows = 2;
+
+// Workgroup: RB weight rows starting at blockIdx.x * RB (valu_rows).
 template <typename T, int RB, int MB, int U, bool ROUTER>
 __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
-  constexpr int VEC = Elem<T>::VEC;
-  __shared__ float s_red[16 * RB * MB];
+  // the product's wave partials, or the shared gate/up's pair exchange
+  // (8 pair slots of 2 x kPartStride floats)
+  __shared__ float s_red[16 * RB * MB > 16 * kPartStride ? 16 * RB * MB : 16 * kPartStride];
   if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
     shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, s_red);
     return;
   }
-  const int nw = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * RB;
-  const T* W = reinterpret_cast<const T*>(a.W);
-  const T* X = reinterpret_cast<const T*>(a.X);
-  const T* wr[RB];
-  const T* xr[MB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) wr[r] = W + (size_t)(n0 + r < a.N ? n0 + r : a.N - 1) * a.K;
-#pragma unroll
-  for (int t = 0; t < MB; ++t) xr[t] = X + (size_t)(t < a.M ? t : 0) * a.K;
-  const int C = a.K / VEC;
-  float acc[RB][MB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int t = 0; t < MB; ++t) acc[r][t] = 0.f;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int blk = wave; blk * 64 < C; blk += nw * U) {
-    u32x4 wv[U][RB], xv[U][MB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (blk + u * nw) * 64 + lane;
-      const bool ok = c < C;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) wv[u][r] = ok ? ld128_stream(wr[r] + (size_t)c * VEC) : zero;
-#pragma unroll
-      for (int t = 0; t < MB; ++t) xv[u][t] = (ok && t < a.M) ? ld128(xr[t] + (size_t)c * VEC) : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int t = 0; t < MB; ++t) acc[r][t] = dot_chunk(wv[u][r], xv[u][t], acc[r][t], T());
-  }
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int t = 0; t < MB; ++t) {
-      const float v = group_sum<64>(acc[r][t]);
-      if (lane == 0) s_red[(wave * RB + r) * MB + t] = v;
-    }
-  __syncthreads();
-  if (threadIdx.x < RB * MB) {
-    const int r = threadIdx.x / MB, t = threadIdx.x % MB, n = n0 + r;
-    float v = 0.f;
-    for (int w = 0; w < nw; ++w) v += s_red[(w * RB + r) * MB + t];
-    if (n < a.N && t < a.M) finish_value(a, t, n, v);
-  }
+  valu_rows<T, RB, MB, U>(a, blockIdx.x * RB, s_red);
   if constexpr (ROUTER) router_tail(a);
 }
 
@@ -409,7 +352,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
 
 int skinny_rows_per_block(int variant, int router) {
   if (variant == VAR_MFMA) return kMfmaRows;
-  if (router || variant == VAR_SPLITK) return 4;
+  if (router) return kRouterRows;
+  if (variant == VAR_SPLITK) return 4;
   return 2;
 }
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router) {
@@ -475,15 +419,15 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
   } else if (a.router) {
     name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
     if (a.bf16) {
-      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 1, 4, true>, grid, block, 0, st, a);
-      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 2, 4, true>, grid, block, 0, st, a);
-      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 4, 2, true>, grid, block, 0, st, a);
-      else launch(K_ROUTE, skinny_valu_kernel<bf16_t, 4, 8, 1, true>, grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<bf16_t, kRouterRows, 1, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<bf16_t, kRouterRows, 2, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<bf16_t, kRouterRows, 4, 2, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<bf16_t, kRouterRows, 8, 1, true>, grid, block, 0, st, a);
     } else {
-      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<float, 4, 1, 4, true>, grid, block, 0, st, a);
-      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<float, 4, 2, 4, true>, grid, block, 0, st, a);
-      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<float, 4, 4, 2, true>, grid, block, 0, st, a);
-      else launch(K_ROUTE, skinny_valu_kernel<float, 4, 8, 1, true>, grid, block, 0, st, a);
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 1, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 2, 4, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 4, 2, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 8, 1, true>, grid, block, 0, st, a);
     }
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {

@@ -1,0 +1,90 @@
+// skinny_core.hpp -- the vector-ALU skinny product of a row block: RB
+// weight rows over all of K for up to MB activation rows, with the whole
+// workgroup (its waves split K and meet in LDS in fixed wave order), and
+// the epilogue that stores a result or turns it into a router logit.  Used
+// by the skinny kernels and by the fused block kernel, which therefore give
+// identical bits.
+//
+// Source: "vLLM 如何用智能体辅助优化 Kimi K3 解码性能", part 1 §1 (a
+// small-matrix kernel at batch 1-2, split-K at larger batch) and part 1 §3
+// (router scores per token).
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+// Result (t, n) of the product: a router logit (+ bias) or a stored value.
+__device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n, float v) {
+  if (a.router) {
+    if (a.bias) v += a.bias[(size_t)t * a.bias_ld + n];
+    st_coherent(&a.logits[(size_t)t * a.N + n], v);   // read by other workgroups of the launch
+    if (a.logits_out) a.logits_out[(size_t)t * a.N + n] = v;
+  } else if (a.y_bf16) {
+    reinterpret_cast<bf16_t*>(a.Y)[(size_t)t * a.N + n] = f32_to_bf16(v);
+  } else {
+    reinterpret_cast<float*>(a.Y)[(size_t)t * a.N + n] = v;
+  }
+}
+
+// Rows n0 .. n0 + RB - 1, all K, with the whole workgroup.  Wave w takes the
+// 64-chunk blocks w, w + NW, w + 2 NW, ... of every row (one 1 KB segment per
+// row per load instruction); U blocks per lane are in flight.  s_red holds
+// NW * RB * MB floats.  Ends after a barrier; threads < RB * MB finish one
+// value each.
+template <typename T, int RB, int MB, int U>
+__device__ __forceinline__ void valu_rows(const SkinnyLaunch& a, int n0, float* s_red) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const T* W = reinterpret_cast<const T*>(a.W);
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const T* wr[RB];
+  const T* xr[MB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) wr[r] = W + (size_t)(n0 + r < a.N ? n0 + r : a.N - 1) * a.K;
+#pragma unroll
+  for (int t = 0; t < MB; ++t) xr[t] = X + (size_t)(t < a.M ? t : 0) * a.K;
+  const int C = a.K / VEC;
+  float acc[RB][MB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[r][t] = 0.f;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int blk = wave; blk * 64 < C; blk += nw * U) {
+    u32x4 wv[U][RB], xv[U][MB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (blk + u * nw) * 64 + lane;
+      const bool ok = c < C;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) wv[u][r] = ok ? ld128_stream(wr[r] + (size_t)c * VEC) : zero;
+#pragma unroll
+      for (int t = 0; t < MB; ++t) xv[u][t] = (ok && t < a.M) ? ld128(xr[t] + (size_t)c * VEC) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int t = 0; t < MB; ++t) acc[r][t] = dot_chunk(wv[u][r], xv[u][t], acc[r][t], T());
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      const float v = group_sum<64>(acc[r][t]);
+      if (lane == 0) s_red[(wave * RB + r) * MB + t] = v;
+    }
+  __syncthreads();
+  if (threadIdx.x < RB * MB) {
+    const int r = threadIdx.x / MB, t = threadIdx.x % MB, n = n0 + r;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += s_red[(w * RB + r) * MB + t];
+    if (n < a.N && t < a.M) finish_value(a, t, n, v);
+  }
+}
+
+}  // namespace moe
