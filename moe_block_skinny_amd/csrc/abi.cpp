@@ -29,7 +29,7 @@ thread_local char g_variant[256] = "";
 std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 std::atomic<int> g_sched{-1};  // block schedule; -1: not yet read from the environment
 
-constexpr int kMaxI = 256;   // kMaxB, kMaxE, kMaxK: route_core.hpp
+constexpr int kMaxI = kMaxInter;   // kMaxB, kMaxE, kMaxK, kMaxInter: route_core.hpp
 constexpr size_t kAlign = 256;
 
 // Profiling hook: events recorded by the dispatch of one kernel.
@@ -596,7 +596,9 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
                        sizeof d1, nullptr, 0, &ex.logits)))
       return s;
   } else {
-    ex.skip_shared = Ws13 && (paths == kPathValu ? v != VAR_MFMA : v == VAR_MFMA);
+    // the vector router launch carries the shared expert's vector gate/up;
+    // otherwise it is a task of the gate/up launch
+    ex.skip_shared = Ws13 && paths == kPathValu && v != VAR_MFMA;
     if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
                        st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
       return s;

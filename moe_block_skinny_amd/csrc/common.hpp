@@ -7,10 +7,12 @@
 // wait; the fix confined that load type to static weights):
 //   * only weights, which no kernel of the library ever writes, are read with
 //     plain or non-temporal loads;
-//   * anything produced inside the same launch by another workgroup (the
-//     router logits) is read only after the acquire fence of a completion
-//     counter (arrive_last), which the compiler cannot hoist a load above and
-//     which invalidates the non-coherent caches first.
+//   * anything produced inside the same launch by another workgroup (router
+//     logits, K-slice partial sums, h in the fused block) is stored
+//     device-coherent (st_coherent) and read only after the acquire fence of
+//     a completion counter or grid barrier (arrive_last, grid_wait), which
+//     the compiler cannot hoist a load above and which invalidates the
+//     non-coherent caches first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -274,27 +276,31 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---- cross-workgroup completion counters ---------------------------------
 
-// Called by every thread of a workgroup after it stored its results.  Returns
-// true in the workgroup that arrives last of `expected` on `counter`, which
-// also resets the counter to zero for the next launch.  Each wave first waits
-// until its own stores are acknowledged (they are in this XCD's L2); then one
-// release atomic per workgroup writes the L2 back and counts the arrival, and
-// only the last workgroup pays the acquire (L2 invalidate) before it reads
-// what the others wrote.  A device-scope fence costs tens of nanoseconds and
-// is serialised across the device, so there is exactly one per workgroup.
+// Called by every thread of a workgroup after it stored its results, which
+// other workgroups read, with st_coherent (below).  Returns true in the
+// workgroup that arrives last of `expected` on `counter`, which also resets
+// the counter to zero for the next launch.  Each wave first waits until its
+// stores are complete (device-coherent stores: visible to every XCD); then
+// thread 0 counts the arrival with a relaxed atomic -- no L2 write-back,
+// which every XCD would serialise across its workgroups -- and only the last
+// workgroup acquires (invalidates its caches, once, by thread 0; the barrier
+// orders the other waves' loads after it) before it reads what the others
+// wrote.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (old == expected - 1u);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old == expected - 1u);
+    if (last) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     *lds_flag = last;
   }
   __syncthreads();
-  const bool last = *lds_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return *lds_flag != 0;
 }
 
 // Store of a value that workgroups of the same launch on other XCDs will
@@ -370,8 +376,7 @@ __device__ __forceinline__ void grid_wait(const uint32_t* flags, uint32_t g0, in
 // Read of a value another workgroup of this launch produced, by the last
 // workgroup after arrive_last's acquire fence.  A plain load: the fence keeps
 // the compiler from moving it above the synchronisation and has invalidated
-// the caches it could be served stale from.  (Device-scope atomic loads would
-// also be coherent, but this GPU serialises them: ~150 ns each.)
+// the caches it could be served stale from.
 __device__ __forceinline__ float ld_after_acquire(const float* p) { return *p; }
 
 // Orderable 32-bit key of a logit: larger key <=> larger value (finite

@@ -48,59 +48,94 @@ __device__ __forceinline__ int entries(const ExpertLaunch& a, const PlanView& p,
 
 // ---- gate/up + SwiGLU --------------------------------------------------------
 
-// Task = (entry, PPT pairs).  Vector-only instantiations: 4 waves, 2 pairs,
-// waves w and w + 2 take the two halves of d for pair w (more loads in
-// flight per pair at no register cost).  With MFMA entries: 8 waves, 4 pairs
-// (the 8-row A tile), split over d; their vector entries use 4 x 2 waves.
-template <int PATHS> struct UpShape {
-  static constexpr int kWaves = PATHS == kPathValu ? 4 : 8;
-  static constexpr int kPairs = kWaves / 2;
-};
+// Vector-only instantiations: tasks (entry, 2 pairs), 4 waves, waves w and
+// w + 2 take the two halves of d for pair w (more loads in flight per pair
+// at no register cost).  With MFMA entries: an entry with more than 8 tokens
+// has tasks of 32 pairs (64 weight rows, up_mfma), the others tasks of 2
+// pairs as above; every workgroup lists the tasks per entry in LDS (a
+// prefix over the plan) and walks them.
+constexpr int kUpWaves = 4;
+constexpr int kUpPairsValu = 2;
 
 template <typename T, int PATHS>
-__global__ __launch_bounds__(UpShape<PATHS>::kWaves * 64) void expert_up_kernel(ExpertLaunch a) {
-  constexpr int PPT = UpShape<PATHS>::kPairs;
+__global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a) {
+  constexpr int PPT = kUpPairsValu;
   __shared__ int32_t s_plan[kMaxPlanWords];
-  __shared__ float s_red[PATHS == kPathValu ? PPT * 2 * 8 : 8 * 4 * 64 * 4];
+  __shared__ float s_red[PPT * 2 * kPartStride];
   const int wave = threadIdx.x >> 6;
   const int tiles_r = (a.I + PPT - 1) / PPT;
   const int tiles_s = (a.Ws13 && !a.skip_shared) ? (a.Is + PPT - 1) / PPT : 0;
-  // Tasks: with routing here (vector shape only), the shared expert's tiles
-  // first -- they need no plan and keep HBM busy while the routed
-  // workgroups select -- then the routed tiles; otherwise the routed tiles,
-  // then the shared ones.
-  const bool here = PATHS == kPathValu && a.logits != nullptr;
-  PlanView p;
-  int task0 = blockIdx.x;
   if constexpr (PATHS == kPathValu) {
+    // Tasks: with routing here, the shared expert's tiles first -- they
+    // need no plan and keep HBM busy while the routed workgroups select --
+    // then the routed tiles; otherwise the routed tiles, then the shared ones.
+    const bool here = a.logits != nullptr;
+    PlanView p;
+    int task0 = blockIdx.x;
     if (here) {
       for (; task0 < tiles_s; task0 += gridDim.x) {
         up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
         __syncthreads();
       }
-      __shared__ TopkScratch s_tk[UpShape<PATHS>::kWaves];
+      __shared__ TopkScratch s_tk[kUpWaves];
       __shared__ int32_t s_ids[64];
       __shared__ float s_w[64];
       p = route_here(a, s_plan, s_tk, s_ids, s_w);
     } else {
       p = stage_plan(a, s_plan);
     }
-  } else {
-    p = stage_plan(a, s_plan);
-  }
-  const int first = here ? tiles_s : 0;                    // first routed task
-  const int total = first + p.n * tiles_r + (here ? 0 : tiles_s);
-  for (int task = task0; task < total; task += gridDim.x) {
-    const int rt = task - first;
-    const bool routed = rt < p.n * tiles_r;
-    const ExpertView v = routed ? expert_view<T>(a, p, rt / tiles_r) : shared_view(a);
-    const int tile = routed ? rt % tiles_r : rt - p.n * tiles_r;
-    if (use_mfma<PATHS>(v.m)) {
-      if constexpr (PATHS != kPathValu) up_mfma_dispatch<T>(a, p.slots, v, tile * PPT, s_red);
-    } else {
+    const int first = here ? tiles_s : 0;                    // first routed task
+    const int total = first + p.n * tiles_r + (here ? 0 : tiles_s);
+    for (int task = task0; task < total; task += gridDim.x) {
+      const int rt = task - first;
+      const bool routed = rt < p.n * tiles_r;
+      const ExpertView v = routed ? expert_view<T>(a, p, rt / tiles_r) : shared_view(a);
+      const int tile = routed ? rt % tiles_r : rt - p.n * tiles_r;
       up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+      __syncthreads();  // s_red is reused by the next task
     }
-    __syncthreads();  // s_red is reused by the next task
+  } else {
+    __shared__ __align__(16) unsigned char s_x[MfmaX<4, kUpMfmaChunks>::kLdsBytes];
+    __shared__ int s_tstart[kMaxE + 2];
+    const PlanView p = stage_plan(a, s_plan);
+    const int ne = p.n + (tiles_s > 0 ? 1 : 0);   // routed entries, then the shared one
+    const int tiles_m = (a.I + kUpPairsMfma - 1) / kUpPairsMfma;
+    const int tiles_ms = (a.Is + kUpPairsMfma - 1) / kUpPairsMfma;
+    // s_tstart[e]: first task of entry e (one wave, 64 entries per pass)
+    if (wave == 0) {
+      const int lane = threadIdx.x & 63;
+      int base = 0;
+      for (int e0 = 0; e0 < ne; e0 += 64) {
+        const int e = e0 + lane;
+        int n = 0;
+        if (e < ne) {
+          const bool sh = e >= p.n;
+          const int m = sh ? a.B : p.offs[e + 1] - p.offs[e];
+          n = use_mfma<PATHS>(m) ? (sh ? tiles_ms : tiles_m) : (sh ? tiles_s : tiles_r);
+        }
+        const int incl = wave_incl_scan(n);
+        if (e < ne) s_tstart[e] = base + incl - n;
+        base += __builtin_amdgcn_readlane(incl, 63);
+      }
+      if (lane == 0) s_tstart[ne] = base;
+    }
+    __syncthreads();
+    const int total = s_tstart[ne];
+    for (int task = blockIdx.x; task < total; task += gridDim.x) {
+      // entry of the task: the last e with s_tstart[e] <= task
+      int lo = 0, hi = ne - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tstart[mid] <= task) lo = mid;
+        else hi = mid - 1;
+      }
+      const int e = wave_uniform(lo);
+      const ExpertView v = e < p.n ? expert_view<T>(a, p, e) : shared_view(a);
+      const int tile = task - s_tstart[e];
+      if (use_mfma<PATHS>(v.m)) up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x);
+      else up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+      __syncthreads();  // s_red / s_x are reused by the next task
+    }
   }
 }
 
@@ -127,7 +162,8 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
 // resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays
 // within 36 KB at B=64).
 template <typename T, int PATHS, int RT, bool PIPE>
-__global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512) void expert_down_combine_kernel(ExpertLaunch a) {
+__global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512, PATHS == kPathValu ? 1 : 4)
+void expert_down_combine_kernel(ExpertLaunch a) {
   // PIPE (vector shape, short rows, h fits in LDS): h is staged in LDS with
   // the plan and each wave prefetches its next entry's W2 rows
   // (down_valu_pipe)
@@ -219,18 +255,17 @@ static const size_t kMaxStagedH = 72 * 1024;   // h staged in LDS by the 32-row 
 
 hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
   const int paths = expert_paths(a.bf16, a.force, a.B);
-  const int ppt = paths == kPathValu ? UpShape<kPathValu>::kPairs : UpShape<kPathBoth>::kPairs;
-  const int threads = paths == kPathValu ? UpShape<kPathValu>::kWaves * 64 : UpShape<kPathBoth>::kWaves * 64;
-  const int tiles_r = (a.I + ppt - 1) / ppt;
-  const int tiles_s = (a.Is + ppt - 1) / ppt;
+  const int tiles_r = (a.I + kUpPairsValu - 1) / kUpPairsValu;
+  const int tiles_s = (a.Is + kUpPairsValu - 1) / kUpPairsValu;
   const int nslot = a.B * a.k;
   int g = (nslot < a.E ? nslot : a.E) * tiles_r + ((a.Ws13 && !a.skip_shared) ? tiles_s : 0);
-  // the whole grid resident at once (vector shape: 4 workgroups per CU), so
-  // no workgroup stages the plan, or selects, after others have finished
-  const int cap = paths == kPathValu ? 4 * 256 : kMaxResidentWG;
+  // vector shape: the whole grid resident at once (4 workgroups per CU), so
+  // no workgroup stages the plan, or selects, after others have finished;
+  // with MFMA tasks: two workgroups per CU, walking the task list
+  const int cap = paths == kPathValu ? 4 * kCUs : 2 * kCUs;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
-  const dim3 grid(g), block(threads);
+  const dim3 grid(g), block(kUpWaves * 64);
   if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), grid, block, 0, st, a);

@@ -11,20 +11,23 @@
 //   m <= 8 : vector ALU.  Gate/up: one wave per pair over the whole of d, so
 //            SwiGLU happens in registers.  Down: L lanes per W2 row (L*VEC >=
 //            I), 64/L rows per load instruction.
-//   m > 8  : MFMA 16x16x32 bf16.  Gate/up: a 16-row A tile holding 4 gate +
-//            4 up rows; the waves of the workgroup split d and meet in LDS.
+//   m > 8  : MFMA 16x16x32 bf16.  Gate/up: 64 weight rows (32 gate/up
+//            pairs) per task over all of d, the entry's token rows gathered
+//            into LDS and shared by the four waves (mfma_core.hpp).
 //            Down: 16 W2 rows per wave over all of I; h (fp32) enters as a
 //            bf16 hi/lo pair so it keeps ~16 mantissa bits.
 #pragma once
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "mfma_core.hpp"
 #include "route_core.hpp"
 
 namespace moe {
 
 constexpr int kMaxPlanWords = 2 + 2 * 512 + 64 * 16;
-constexpr int kUpPairsMfma = 4;   // gate/up pairs per MFMA up task
+constexpr int kUpPairsMfma = 32;  // gate/up pairs per MFMA up task (64 weight rows)
+constexpr int kUpMfmaChunks = 2;  // chunks in flight per wave (two workgroups per CU)
 
 // Routing plan staged in LDS (see moe_plan_words for the layout).
 struct PlanView {
@@ -242,85 +245,76 @@ __device__ __forceinline__ void up_valu_dispatch(const ExpertLaunch& a, const in
   else up_valu<T, 8, NH>(a, slots, v, i, half, ps, s_part);
 }
 
-// Pairs i0..i0+3 with the whole workgroup: lanes with row%16 in 0..3 load
-// gate rows, 4..7 up rows, 8..15 stay zero; wave w covers the w-th of nw
-// slices of the K steps.  s_red holds nw * NT * 1 KB.
+// Pairs p0 .. p0+31 of entry v (m > 8 tokens) over all of d with the four
+// waves of the workgroup (mfma_rows): wave w's A rows 0-7 are the gate rows
+// of pairs p0+8w .. p0+8w+7, rows 8-15 the up rows of the same pairs, so
+// after the product lane l < 32 holds gate sums of pairs p0 + 8w + 4(l/16)
+// + q (q = 0..3) for token nt*16 + l%16 and lane l + 32 the matching up
+// sums; SwiGLU pairs them across the two lane halves.  The entry's token
+// rows are gathered into LDS (s_x).
 template <int NT>
-__device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i0, float* s_red) {
-  const int nw = blockDim.x >> 6;
+__device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int p0,
+                                        unsigned char* s_x) {
+  constexpr int PPT = MfmaX<NT>::kPerThread;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
+  const int pair = p0 + 8 * wave + (row & 7);
+  const bool wok = pair < v.I;
   const bf16_t* W13 = reinterpret_cast<const bf16_t*>(v.W13);
+  const bf16_t* wr = W13 + (size_t)((row < 8 ? 0 : v.I) + (wok ? pair : 0)) * a.d + kq * 8;
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
-  int wrow = -1;
-  if (row < 4 && i0 + row < v.I) wrow = i0 + row;
-  else if (row >= 4 && row < 8 && i0 + row - 4 < v.I) wrow = v.I + i0 + row - 4;
-  const bf16_t* wr = W13 + (size_t)(wrow >= 0 ? wrow : 0) * a.d;
-  const bf16_t* xr[NT];
-  bool xok[NT];
+  const bf16_t* xrow[PPT];
+  bool xok[PPT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int ti = nt * 16 + row;
+  for (int i = 0; i < PPT; ++i) {
+    const int t = mfma_piece_token<NT>(i);
     int tok = 0, sr = 0;
-    xok[nt] = ti < v.m;
-    if (xok[nt]) token_of(a, slots, v, ti, tok, sr);
-    xr[nt] = X + (size_t)tok * a.d;
+    xok[i] = t < v.m;
+    if (xok[i]) token_of(a, slots, v, t, tok, sr);
+    xrow[i] = X + (size_t)tok * a.d;
   }
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_kloop<NT, NT <= 2 ? 4 : 2>(wr, wrow >= 0, xr, xok, kq, a.d / 32, wave, nw, acc);
+  mfma_rows<NT, kUpMfmaChunks>(wr, wok, xrow, xok, 0, a.d / 32, s_x, acc);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_red[((wave * NT + nt) * 64 + lane) * 4 + q] = acc[nt][q];
-  __syncthreads();
-  // thread (q, t): pair i0+q, token t.  Gate sums sit in lanes 0..15 (rows
-  // 0..3) and up sums in lanes 16..31 (rows 4..7) of each wave's tile.
-  for (int idx = threadIdx.x; idx < 4 * 64; idx += blockDim.x) {
-    const int q = idx >> 6, t = idx & 63;
-    if (t < v.m && i0 + q < v.I) {
-      const int nt = t >> 4, l = t & 15;
-      float g = 0.f, u = 0.f;
-      for (int w = 0; w < nw; ++w) {
-        g += s_red[((w * NT + nt) * 64 + l) * 4 + q];
-        u += s_red[((w * NT + nt) * 64 + 16 + l) * 4 + q];
+    for (int q = 0; q < 4; ++q) {
+      const float g = acc[nt][q];
+      const float u = __shfl_xor(acc[nt][q], 32);
+      const int i = p0 + 8 * wave + 4 * (lane >> 4) + q;
+      const int t = nt * 16 + (lane & 15);
+      if (lane < 32 && i < v.I && t < v.m) {
+        int tok, sr;
+        token_of(a, slots, v, t, tok, sr);
+        st_coherent(&a.h[(size_t)sr * a.hld + i], silu(g) * u);
       }
-      int tok, sr;
-      token_of(a, slots, v, t, tok, sr);
-      st_coherent(&a.h[(size_t)sr * a.hld + i0 + q], silu(g) * u);
     }
-  }
-  __syncthreads();
 }
 
 template <typename T>
 __device__ __forceinline__ void up_mfma_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
-                                                 int i0, float* s_red) {
+                                                 int p0, unsigned char* s_x) {
   if constexpr (sizeof(T) == 2) {
     const int nt = (v.m + 15) / 16;
-    if (nt <= 1) up_mfma<1>(a, slots, v, i0, s_red);
-    else if (nt == 2) up_mfma<2>(a, slots, v, i0, s_red);
-    else if (nt == 3) up_mfma<3>(a, slots, v, i0, s_red);
-    else up_mfma<4>(a, slots, v, i0, s_red);
+    if (nt <= 1) up_mfma<1>(a, slots, v, p0, s_x);
+    else if (nt == 2) up_mfma<2>(a, slots, v, p0, s_x);
+    else if (nt == 3) up_mfma<3>(a, slots, v, p0, s_x);
+    else up_mfma<4>(a, slots, v, p0, s_x);
   }
 }
 
-// Shared-expert gate/up tile `tile` with the whole workgroup (nw waves):
-// the vector shape takes nw/2 pairs, each split over two waves into the same
-// two halves of d as the gate/up kernel (so both give identical bits), the
-// MFMA shape 4 pairs.  s_red: the caller's LDS scratch (vector: nw floats *
-// 8 tokens; MFMA: nw * NT KB).
-template <typename T, int PATHS>
+// Shared-expert gate/up tile `tile` with the whole workgroup (nw waves) on
+// the vector shape: nw/2 pairs, each split over two waves into the same two
+// halves of d as the gate/up kernel (so both give identical bits).  s_red:
+// the caller's LDS scratch (nw/2 pair slots of 2 x kPartStride floats).
+template <typename T>
 __device__ __forceinline__ void shared_up_task(const ExpertLaunch& a, int tile, float* s_red) {
   const ExpertView v = shared_view(a);
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
-  if (use_mfma<PATHS>(v.m)) {
-    up_mfma_dispatch<T>(a, nullptr, v, tile * kUpPairsMfma, s_red);
-  } else {
-    const int pp = nw >> 1;
-    up_valu_dispatch<T, 2>(a, nullptr, v, tile * pp + wave % pp, wave / pp, wave % pp, s_red);
-  }
+  const int pp = nw >> 1;
+  up_valu_dispatch<T, 2>(a, nullptr, v, tile * pp + wave % pp, wave / pp, wave % pp, s_red);
 }
 
 // ---- weighted combine ---------------------------------------------------------
@@ -538,59 +532,62 @@ __device__ __forceinline__ void order_entries(const ExpertLaunch& a, const PlanV
 template <int NT>
 __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
                           const YSink& sink) {
+  constexpr int JM = kMaxInter / 32;   // K steps of the longest row
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
   const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
   const bf16_t* wr = W2 + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
-  const float* hr[NT];
-  bool ok[NT];
-  int srow[NT];
+  const int J = wave_uniform(v.I / 32);
+  // all K steps of the wave's 16 rows requested at once (steps past J
+  // re-read the last one), then each token tile's h: one memory round trip
+  // per tile instead of one per step
+  u32x4 wv[JM];
+#pragma unroll
+  for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int ti = nt * 16 + row;
     int tok = 0, sr = 0;
-    ok[nt] = ti < v.m;
-    if (ok[nt]) token_of(a, slots, v, ti, tok, sr);
-    hr[nt] = a.h + (size_t)sr * a.hld;
-    srow[nt] = sr;
-  }
-  f32x4 acc[NT];
+    const bool ok = ti < v.m;
+    if (ok) token_of(a, slots, v, ti, tok, sr);
+    const float* hr = a.h + (size_t)(ok ? sr : 0) * a.hld;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // h in two halves of the steps (register pressure: two workgroups of
+    // eight waves share a CU)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int J = v.I / 32;
-  for (int j = 0; j < J; ++j) {
-    const size_t off = (size_t)(j * 4 + kq) * 8;
-    const u32x4 av = ld128_stream(wr + off);
+    for (int jh = 0; jh < JM; jh += JM / 2) {
+      f32x4 h0[JM / 2], h1[JM / 2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
-      if (ok[nt]) {
-        const f32x4 h0 = *reinterpret_cast<const f32x4*>(hr[nt] + off);
-        const f32x4 h1 = *reinterpret_cast<const f32x4*>(hr[nt] + off + 4);
-        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      for (int jj = 0; jj < JM / 2; ++jj) {
+        const int j = jh + jj;
+        const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+        h0[jj] = *reinterpret_cast<const f32x4*>(hr + off);
+        h1[jj] = *reinterpret_cast<const f32x4*>(hr + off + 4);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16_t a0 = f32_to_bf16(hv[2 * e]), a1 = f32_to_bf16(hv[2 * e + 1]);
-          const bf16_t b0 = f32_to_bf16(hv[2 * e] - bf16_to_f32(a0));
-          const bf16_t b1 = f32_to_bf16(hv[2 * e + 1] - bf16_to_f32(a1));
-          hi[e] = (uint32_t)a0 | ((uint32_t)a1 << 16);
-          lo[e] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      for (int jj = 0; jj < JM / 2; ++jj) {
+        const int j = jh + jj;
+        if (j < J) {
+          uint32_t hi[4], lo[4];
+          split_bf16x2(h0[jj].x, h0[jj].y, hi[0], lo[0]);
+          split_bf16x2(h0[jj].z, h0[jj].w, hi[1], lo[1]);
+          split_bf16x2(h1[jj].x, h1[jj].y, hi[2], lo[2]);
+          split_bf16x2(h1[jj].z, h1[jj].w, hi[3], lo[3]);
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          const u32x4 hv4 = ok ? u32x4{hi[0], hi[1], hi[2], hi[3]} : zero;
+          const u32x4 lv4 = ok ? u32x4{lo[0], lo[1], lo[2], lo[3]} : zero;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                        __builtin_bit_cast(bf16x8, hv4), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                        __builtin_bit_cast(bf16x8, lv4), acc, 0, 0, 0);
         }
       }
-      const u32x4 hv4 = {hi[0], hi[1], hi[2], hi[3]}, lv4 = {lo[0], lo[1], lo[2], lo[3]};
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                        __builtin_bit_cast(bf16x8, hv4), acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                        __builtin_bit_cast(bf16x8, lv4), acc[nt], 0, 0, 0);
     }
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (ok[nt]) {
+    if (ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 4 * kq + i;
-        if (r < a.d) *sink.at(a, srow[nt], r) = acc[nt][i];
+        if (r < a.d) *sink.at(a, sr, r) = acc[i];
       }
     }
   }

@@ -26,6 +26,7 @@ constexpr int kMaxE = 512;
 constexpr int kMaxK = 16;
 constexpr int kMaxB = 64;
 constexpr int kNI = kMaxE / 64;   // logits per lane
+constexpr int kMaxInter = 256;    // expert intermediate size (bf16; fp32: 256 as well)
 
 constexpr int kTopkWaves = 8;     // waves of a workgroup that select (each holds a TopkScratch)
 

@@ -45,9 +45,10 @@ namespace moe {
 // logits of four tokens loaded before any is used (one memory round trip
 // per group); ids and weights go to LDS and to the caller's arrays.
 
+template <int NTK>
 __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* s_tk, int32_t* s_ids, float* s_w) {
   constexpr int QB = 4;
-  const int nw = (blockDim.x >> 6) < kTopkWaves ? (blockDim.x >> 6) : kTopkWaves;
+  const int nw = (blockDim.x >> 6) < NTK ? (blockDim.x >> 6) : NTK;
   const int wave = threadIdx.x >> 6;
   if (wave >= nw) return;
   const int E = a.N, M = a.M, k = a.k;
@@ -68,10 +69,12 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
   }
 }
 
+// NTK: waves that select (each holds a TopkScratch in LDS).
+template <int NTK>
 __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   __shared__ int32_t s_ids[kMaxB * kMaxK];
   __shared__ float s_w[kMaxB * kMaxK];
-  __shared__ TopkScratch s_tk[kTopkWaves];
+  __shared__ TopkScratch s_tk[NTK];
   __shared__ unsigned long long s_mask[kMaxE];
   __shared__ int s_cnt[kMaxE];
   __shared__ int s_act[kMaxE];
@@ -79,7 +82,7 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int M = a.M, E = a.N, k = a.k, nslot = M * k;
 
-  topk_tokens(a, s_tk, s_ids, s_w);
+  topk_tokens<NTK>(a, s_tk, s_ids, s_w);
   __syncthreads();
   if (nslot <= 64) {  // one wave sorts the slots
     if (wave == 0) plan_wave(s_ids, nslot, E, reinterpret_cast<int*>(s_tk), a.plan, nullptr);
@@ -142,7 +145,15 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   __shared__ int s_flag;
   if (!a.router || !a.finish) return;
   if (!arrive_last(a.done_counter, (uint32_t)a.router_arrivals, &s_flag)) return;
-  route_finish(a);
+  route_finish<kTopkWaves>(a);
+}
+
+// The finish as a launch of its own (one 16-wave workgroup, 16 selecting
+// waves), after a logits-only router launch whose workgroups have too few
+// waves to select many tokens quickly (the MFMA shape has 4).
+constexpr int kFinishWaves = 16;
+__global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyLaunch a) {
+  route_finish<kFinishWaves>(a);
 }
 
 // ---- vector-ALU kernels (gemv / splitk) ----------------------------------
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   // (8 pair slots of 2 x kPartStride floats)
   __shared__ float s_red[16 * RB * MB > 16 * kPartStride ? 16 * RB * MB : 16 * kPartStride];
   if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
-    shared_up_task<T, kPathValu>(a.ex, blockIdx.x - a.router_wgs, s_red);
+    shared_up_task<T>(a.ex, blockIdx.x - a.router_wgs, s_red);
     return;
   }
   valu_rows<T, RB, MB, U>(a, blockIdx.x * RB, s_red);
@@ -170,22 +181,13 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
 
 // ---- MFMA kernel (bf16) --------------------------------------------------
 
-// Workgroup of 4 waves = 64 weight rows (wave w: rows n0 + 16 w .. + 15, the
-// A operand of v_mfma_f32_16x16x32_bf16) over one K slice (blockIdx ->
-// row group, slice).  The slice's activation rows pass through LDS in chunks
-// of kChunk 32-steps: loaded once per workgroup with coalesced 128-bit loads
-// and read by all 4 waves as the B operand (the per-wave loads of a 16-token
-// B tile touch 16 cache lines each; that traffic, four times the weight
-// bytes at 64 tokens, saturated the L1 address path).  Weights for the next
-// chunk and activations for the next chunk are requested before the current
-// chunk is multiplied; two weight buffers are used in turn.  With several
-// slices the workgroups store fp32 partial sums [slice][M][N]; the last of a
-// row group's slices to arrive adds them in slice order (deterministic).
-constexpr int kMfmaRows = 64;
-constexpr int kMfmaWaves = 4;
+// Workgroup of 4 waves = 64 weight rows (wave w: rows n0 + 16 w .. + 15)
+// over one K slice (blockIdx -> row group, slice), by mfma_rows
+// (mfma_core.hpp: activation chunks staged through LDS, double-buffered
+// weights).  With several slices the workgroups store fp32 partial sums
+// [slice][M][N]; the last of a row group's slices to arrive adds them in
+// slice order (deterministic).
 constexpr int kMaxSlices = 8;
-constexpr int kChunk = 8;                   // 32-steps per LDS chunk
-constexpr int kXRow = kChunk * 64 + 16;     // bytes per token row in LDS (padded)
 
 void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
   (void)M;
@@ -204,14 +206,10 @@ void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
 
 template <int NT, bool ROUTER>
 __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaunch a) {
-  __shared__ __align__(16) unsigned char s_x[NT * 16 * kXRow];
-  if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
-    extern __shared__ float s_dyn[];
-    shared_up_task<bf16_t, kPathMfma>(a.ex, blockIdx.x - a.router_wgs, s_dyn);
-    return;
-  }
-  constexpr int PIECES = NT * 16 * kChunk * 4;                 // 16-byte pieces per chunk
-  constexpr int PPT = (PIECES + kMfmaWaves * 64 - 1) / (kMfmaWaves * 64);
+  // two chunks (16 KB of weights per wave) in flight (four measured slower)
+  constexpr int U = 2;
+  __shared__ __align__(16) unsigned char s_x[MfmaX<NT, U>::kLdsBytes];
+  constexpr int PPT = MfmaX<NT>::kPerThread;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
   const int rgi = blockIdx.x / a.ks_n, ks = blockIdx.x % a.ks_n;
@@ -223,83 +221,18 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
   const bool wok = n0 + row < a.N;
   const bf16_t* wr = W + (size_t)(wok ? n0 + row : a.N - 1) * a.K + kq * 8;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  // activation pieces of this thread: p = tid + 256 i -> token p / (4 kChunk), piece p % (4 kChunk)
-  auto ld_x = [&](int c, u32x4(&xv)[PPT]) {
+  const bf16_t* xrow[PPT];
+  bool xok[PPT];
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = tid + i * kMfmaWaves * 64;
-      const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
-      const int j = c + q / 4;
-      const int tc = t < a.M ? t : 0, jc = j < s1 ? j : s1 - 1;
-      xv[i] = ld128(X + (size_t)tc * a.K + (size_t)jc * 32 + (q & 3) * 8);
-    }
-  };
-  static_assert(PIECES % (kMfmaWaves * 64) == 0, "whole pieces per thread");
-  auto st_x = [&](int c, const u32x4(&xv)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pc = tid + i * kMfmaWaves * 64;
-      const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
-      const bool ok = t < a.M && c + q / 4 < s1;
-      *reinterpret_cast<u32x4*>(s_x + t * kXRow + q * 16) = ok ? xv[i] : zero;
-    }
-  };
-  // weight rows of chunk c (past the slice end: an activation row, cached)
-  auto ld_w = [&](int c, bool real, u32x4(&wv)[kChunk]) {
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const int j = c + u < s1 ? c + u : s1 - 1;
-      wv[u] = ld128_stream(real ? wr + (size_t)j * 32 : X);
-    }
-  };
+  for (int i = 0; i < PPT; ++i) {
+    const int t = mfma_piece_token<NT>(i);
+    xok[i] = t < a.M;
+    xrow[i] = X + (size_t)(xok[i] ? t : 0) * a.K;
+  }
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // steps of a partial chunk past the slice end hold zero activations in LDS
-  // (st_x), so every chunk is multiplied whole, without a branch per step
-  auto mul = [&](const u32x4(&wv)[kChunk]) {
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const u32x4 av = wok ? wv[u] : zero;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(s_x + (nt * 16 + row) * kXRow + (u * 4 + kq) * 16);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc[nt], 0, 0, 0);
-      }
-    }
-  };
-  u32x4 xv[PPT], w0[kChunk], w1[kChunk];
-  int c = s0;
-  ld_x(c, xv);
-  ld_w(c, true, w0);
-  // Barriers here only order LDS (lds_barrier): a full __syncthreads would
-  // also wait for every global load in flight, the weight prefetch included.
-  for (;;) {
-    lds_barrier();              // the previous chunk's LDS reads are done
-    st_x(c, xv);
-    lds_barrier();
-    int cn = c + kChunk;
-    bool more = cn < s1;
-    ld_x(more ? cn : c, xv);
-    ld_w(more ? cn : c, more, w1);
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the products
-    mul(w0);
-    if (!more) break;
-    c = cn;
-    lds_barrier();
-    st_x(c, xv);
-    lds_barrier();
-    cn = c + kChunk;
-    more = cn < s1;
-    ld_x(more ? cn : c, xv);
-    ld_w(more ? cn : c, more, w0);
-    __builtin_amdgcn_sched_barrier(0);
-    mul(w1);
-    if (!more) break;
-    c = cn;
-  }
+  mfma_rows<NT, U>(wr, wok, xrow, xok, s0, s1, s_x, acc);
   if (a.ks_n == 1) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -314,7 +247,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = n0 + 4 * kq + i, t = nt * 16 + row;
-        if (n < a.N && t < a.M) a.part[((size_t)ks * a.M + t) * a.N + n] = acc[nt][i];
+        if (n < a.N && t < a.M) st_coherent(&a.part[((size_t)ks * a.M + t) * a.N + n], acc[nt][i]);
       }
     __shared__ int s_last;
     if (!arrive_last(a.rg_counter + rgi, (uint32_t)a.ks_n, &s_last)) return;
@@ -347,7 +280,6 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
       }
     }
   }
-  if constexpr (ROUTER) router_tail(a);
 }
 
 int skinny_rows_per_block(int variant, int router) {
@@ -373,18 +305,8 @@ int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router
   return nw;
 }
 int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
-  const bool mfma = expert_paths(ex.bf16, ex.force, ex.B) != kPathValu;
   const int pp = nw / 2;
-  return mfma ? (ex.Is + kUpPairsMfma - 1) / kUpPairsMfma : (ex.Is + pp - 1) / pp;
-}
-
-// Router launches take the instantiation with the router's finish and side
-// job compiled in (and their LDS); plain products the one without.
-template <typename K>
-static void launch_as(const SkinnyLaunch& a, K router_kernel, K plain_kernel, dim3 grid, dim3 block, size_t lds,
-                      hipStream_t st) {
-  if (a.router) launch(K_ROUTE, router_kernel, grid, block, (uint32_t)lds, st, a);
-  else launch(K_SKINNY, plain_kernel, grid, block, (uint32_t)lds, st, a);
+  return (ex.Is + pp - 1) / pp;
 }
 
 hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
@@ -401,21 +323,39 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
   const int nwg = nrg * a.ks_n;
   a.router_wgs = nwg;
   a.router_arrivals = nrg;
-  const int extra = (a.router && a.ex.Ws13) ? shared_up_tiles_host(a.ex, nw) : 0;
+  // the shared expert's gate/up rides a vector router launch (vector shape)
+  const int extra = (a.router && a.ex.Ws13 && a.variant != VAR_MFMA) ? shared_up_tiles_host(a.ex, nw) : 0;
   a.shared_tiles = extra;
   dim3 grid((unsigned)(nwg + extra)), block((unsigned)(64 * nw));
   const char* name = "?";
   if (a.variant == VAR_MFMA) {
     if (a.ks_n > 1 && (!a.part || !a.rg_counter)) return hipErrorInvalidValue;
     const int nt = (a.M + 15) / 16;
-    const size_t lds = extra ? (size_t)nw * nt * 256 * sizeof(float) : 0;   // the shared gate/up's reduction
+    const size_t lds = 0;
+    // router with finish: the product launch stores logits only, then the
+    // finish launch selects; with the profiling hook armed the product's
+    // dispatch records the start event and the finish's the stop event
+    const bool split = a.router && a.finish;
+    SkinnyLaunch p = a;
+    if (split) p.finish = 0;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const bool prof = a.router && profile_events_for(K_ROUTE, &e0, &e1);
+    auto go = [&](auto rk, auto pk) {
+      if (!a.router) launch(K_SKINNY, pk, grid, block, (uint32_t)lds, st, p);
+      else if (prof) hipExtLaunchKernelGGL(rk, grid, block, lds, st, e0, split ? nullptr : e1, 0u, p);
+      else hipLaunchKernelGGL(rk, grid, block, lds, st, p);
+    };
     switch (nt) {
-      case 1: launch_as(a, skinny_mfma_kernel<1, true>, skinny_mfma_kernel<1, false>, grid, block, lds, st); break;
-      case 2: launch_as(a, skinny_mfma_kernel<2, true>, skinny_mfma_kernel<2, false>, grid, block, lds, st); break;
-      case 3: launch_as(a, skinny_mfma_kernel<3, true>, skinny_mfma_kernel<3, false>, grid, block, lds, st); break;
-      default: launch_as(a, skinny_mfma_kernel<4, true>, skinny_mfma_kernel<4, false>, grid, block, lds, st); break;
+      case 1: go(skinny_mfma_kernel<1, true>, skinny_mfma_kernel<1, false>); break;
+      case 2: go(skinny_mfma_kernel<2, true>, skinny_mfma_kernel<2, false>); break;
+      case 3: go(skinny_mfma_kernel<3, true>, skinny_mfma_kernel<3, false>); break;
+      default: go(skinny_mfma_kernel<4, true>, skinny_mfma_kernel<4, false>); break;
     }
-    name = "mfma";
+    if (split) {
+      if (prof) hipExtLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishWaves * 64), 0, st, nullptr, e1, 0u, a);
+      else hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishWaves * 64), 0, st, a);
+    }
+    name = split ? "mfma + finish launch" : "mfma";
   } else if (a.router) {
     name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
     if (a.bf16) {
