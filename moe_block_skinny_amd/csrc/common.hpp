@@ -191,70 +191,6 @@ __device__ __forceinline__ void valu_dot(const T* const (&wr)[R], const T* const
     for (int t = 0; t < MB; ++t) acc[r][t] = group_sum<64>(acc[r][t]);
 }
 
-// ---- MFMA streaming core -----------------------------------------------------
-
-// One wave: a 16-row A tile (this lane's row pointer wr, real when wok;
-// lane l holds row l%16 and K elements 8*(l/16) .. +7 of every 32-wide step)
-// against NT 16-token B tiles (xr[nt], real when xok[nt]) with
-// v_mfma_f32_16x16x32_bf16.  The wave takes the SB-step blocks b0, b0 +
-// bstride, ... of the J steps (b0, bstride, J wave-uniform).  Two register
-// stages used in turn: the loads of the next block are issued before the
-// current one is multiplied, so a wave always has a block of loads in
-// flight.  Every load is issued unconditionally -- addresses are clamped
-// into range, and past the wave's last block the weight loads re-read an
-// activation row the caches hold -- and invalid operands are zeroed at use,
-// so the compiler never has to drain the loads in flight at a branch.
-template <int NT, int SB>
-__device__ __forceinline__ void mfma_kloop(const uint16_t* wr, bool wok, const uint16_t* const (&xr)[NT],
-                                           const bool (&xok)[NT], int kq, int J, int b0, int bstride,
-                                           f32x4 (&acc)[NT]) {
-  u32x4 a0[SB], x0[SB][NT], a1[SB], x1[SB][NT];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  J = __builtin_amdgcn_readfirstlane(J);
-  b0 = __builtin_amdgcn_readfirstlane(b0);
-  bstride = __builtin_amdgcn_readfirstlane(bstride);
-  auto load = [&](int blk, bool real, u32x4 (&av)[SB], u32x4 (&xv)[SB][NT]) {
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int j = blk * SB + u;
-      const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
-      av[u] = ld128_stream((real ? wr : xr[0]) + off);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) xv[u][nt] = ld128(xr[nt] + off);
-    }
-  };
-  auto mul = [&](int blk, const u32x4 (&av)[SB], const u32x4 (&xv)[SB][NT]) {
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const bool ok = blk * SB + u < J;
-      const u32x4 a = (ok && wok) ? av[u] : zero;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const u32x4 b = (ok && xok[nt]) ? xv[u][nt] : zero;
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          __builtin_bit_cast(bf16x8, b), acc[nt], 0, 0, 0);
-      }
-    }
-  };
-  int blk = b0;
-  if (blk * SB >= J) return;
-  load(blk, true, a0, x0);
-  for (;;) {
-    int nb = blk + bstride;
-    bool more = nb * SB < J;
-    load(more ? nb : blk, more, a1, x1);
-    mul(blk, a0, x0);
-    if (!more) break;
-    blk = nb;
-    nb = blk + bstride;
-    more = nb * SB < J;
-    load(more ? nb : blk, more, a0, x0);
-    mul(blk, a1, x1);
-    if (!more) break;
-    blk = nb;
-  }
-}
-
 // Lane `lane` picks acc[t == lane]: spreads MB results over the first lanes.
 template <int MB>
 __device__ __forceinline__ float pick_lane(const float (&v)[MB], int lane) {

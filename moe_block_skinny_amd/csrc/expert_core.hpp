@@ -257,11 +257,12 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
                                         unsigned char* s_x) {
   constexpr int PPT = MfmaX<NT>::kPerThread;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = lane & 15, kq = lane >> 4;
-  const int pair = p0 + 8 * wave + (row & 7);
+  // rows 0-7 of the wave: gate rows of its 8 pairs; rows 8-15: their up rows
+  const int pair = p0 + 8 * wave + mfma_row_a();
   const bool wok = pair < v.I;
   const bf16_t* W13 = reinterpret_cast<const bf16_t*>(v.W13);
-  const bf16_t* wr = W13 + (size_t)((row < 8 ? 0 : v.I) + (wok ? pair : 0)) * a.d + kq * 8;
+  const bf16_t* wa = W13 + (size_t)(wok ? pair : 0) * a.d + mfma_col_off();
+  const bf16_t* wb = W13 + (size_t)(v.I + (wok ? pair : 0)) * a.d + mfma_col_off();
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
   const bf16_t* xrow[PPT];
   bool xok[PPT];
@@ -276,7 +277,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows<NT, kUpMfmaChunks>(wr, wok, xrow, xok, 0, a.d / 32, s_x, acc);
+  mfma_rows<NT, kUpMfmaChunks>(wa, wok, wb, wok, xrow, xok, 0, a.d / 32, s_x, acc);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll

@@ -35,6 +35,12 @@ struct MfmaX {
   static constexpr int kLdsBytes = U * kBufBytes;                       // U chunks per iteration
 };
 
+// Weight rows of a wave, as mfma_rows takes them: this lane's row of rows
+// 0-7 (lane%8) and of rows 8-15, at element offset 8*(lane/8).
+__device__ __forceinline__ int mfma_row_a() { return threadIdx.x & 7; }
+__device__ __forceinline__ int mfma_row_b() { return 8 + (threadIdx.x & 7); }
+__device__ __forceinline__ int mfma_col_off() { return ((threadIdx.x & 63) >> 3) * 8; }
+
 // Token of this thread's i-th activation piece (pieces p = tid + 256 i of a
 // chunk: token p / (4 kChunk), piece p % (4 kChunk)).
 template <int NT>
@@ -43,31 +49,48 @@ __device__ __forceinline__ int mfma_piece_token(int i) {
 }
 
 // acc[nt] += W[16 rows of this wave] . X[tokens nt*16 .. +15]^T over steps
-// s0 .. s1-1 (s0 < s1).  wr: this lane's weight row (row lane%16 of the
-// wave's 16), already offset by (lane/16)*8 elements, read only when wok.
-// xrow[i]: activation row of this thread's i-th piece token, read only when
-// xok[i] (else zeros go to LDS).  X rows and W rows hold K = 32 * (steps of
-// the whole row) elements; steps index both.  s_x: MfmaX<NT, U>::kLdsBytes.
+// s0 .. s1-1 (s0 < s1).
+//
+// Weight loads move whole 128-byte lines: per pair of steps (64 elements)
+// one instruction loads rows 0-7 of the wave (lane l: row l%8, elements
+// 8*(l/8) .. +7 of the pair) and one rows 8-15.  The MFMA A operand wants
+// lane l = R + 16 g to hold row R; so the first step of the pair takes K
+// positions 16g .. 16g+7 of the 64 and the second 16g+8 .. 16g+15, which
+// lane l holds directly for rows R < 8 (first step) and R >= 8 (second
+// step), and lane l -+ 8 holds otherwise: a DPP row shift by 8.  The
+// activations in LDS are read with the same K positions.  (Loading 16 rows
+// x 64 bytes per instruction touched every line twice and cost ~3 us on the
+// dense product.)
+//
+// wa / wb: this lane's row (lane%8) of the wave's rows 0-7 / 8-15, already
+// offset by 8*(lane/8) elements; read only when oka / okb.  xrow[i]:
+// activation row of this thread's i-th piece token, read only when xok[i]
+// (else zeros go to LDS).  X rows and W rows hold K = 32 * (steps of the
+// whole row) elements; steps index both.  s_x: MfmaX<NT, U>::kLdsBytes.
 //
 // Each iteration requests the activations and then the weights of U chunks
 // before waiting for any of them, so a wave keeps U * 8 KB of weights in
-// flight, and leaves nothing in flight
-// across the loop's back edge (a load still in flight there made the
-// compiler copy its registers at the back edge and wait for every load).
-// Chunks past s1 hold zero activations (weight loads from a cached row), so
-// every chunk is multiplied whole, without a branch per step.
+// flight, and leaves nothing in flight across the loop's back edge (a load
+// still in flight there made the compiler copy its registers at the back
+// edge and wait for every load).  Steps past s1 hold zero activations and
+// zeroed weights (their loads read a cached activation row), so every chunk
+// is multiplied whole, without a branch per step.
 template <int NT, int U>
-__device__ __forceinline__ void mfma_rows(const bf16_t* wr, bool wok, const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread],
+__device__ __forceinline__ void mfma_rows(const bf16_t* wa, bool oka, const bf16_t* wb, bool okb,
+                                          const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread],
                                           const bool (&xok)[MfmaX<NT>::kPerThread], int s0, int s1,
                                           unsigned char* s_x, f32x4 (&acc)[NT]) {
   constexpr int PPT = MfmaX<NT>::kPerThread;
+  constexpr int NP = kChunk / 2;       // step pairs per chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
+  const bool low = row < 8;
+  const int hi_step = lane >> 5;       // lanes 32-63 hold the pair's second step
   const u32x4 zero = {0u, 0u, 0u, 0u};
   s0 = __builtin_amdgcn_readfirstlane(s0);
   s1 = __builtin_amdgcn_readfirstlane(s1);
   for (int c = s0; c < s1; c += U * kChunk) {
-    u32x4 xv[U][PPT], wv[U][kChunk];
+    u32x4 xv[U][PPT], va[U][NP], vb[U][NP];
     // activations of the iteration's chunks (clamped into range) ...
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -79,13 +102,15 @@ __device__ __forceinline__ void mfma_rows(const bf16_t* wr, bool wok, const bf16
         xv[u][i] = ld128(xrow[i] + (size_t)jc * 32 + (q & 3) * 8);
       }
     __builtin_amdgcn_sched_barrier(0);   // activations first: st_x waits only for them
-    // ... then the weights (steps past s1: a cached activation row)
+    // ... then the weights (a lane whose step is past s1 reads a cached row)
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int v = 0; v < kChunk; ++v) {
-        const int j = c + u * kChunk + v;
-        wv[u][v] = ld128_stream(j < s1 ? wr + (size_t)j * 32 : xrow[0]);
+      for (int p = 0; p < NP; ++p) {
+        const int j = c + u * kChunk + 2 * p;
+        const bool in = j + hi_step < s1;
+        va[u][p] = ld128_stream(in ? wa + (size_t)j * 32 : xrow[0]);
+        vb[u][p] = ld128_stream(in ? wb + (size_t)j * 32 : xrow[0]);
       }
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();              // the previous iteration's LDS reads are done
@@ -104,15 +129,27 @@ __device__ __forceinline__ void mfma_rows(const bf16_t* wr, bool wok, const bf16
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int v = 0; v < kChunk; ++v) {
-        const bool ok = wok && c + u * kChunk + v < s1;
-        const u32x4 av = ok ? wv[u][v] : zero;
+      for (int p = 0; p < NP; ++p) {
+        const bool in = c + u * kChunk + 2 * p + hi_step < s1;
+        const u32x4 a = (in && oka) ? va[u][p] : zero;
+        const u32x4 b = (in && okb) ? vb[u][p] : zero;
+        u32x4 ev, od;   // A operands of the pair's first and second step
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b[e], 0x118, 0xf, 0xf, false);  // row_shr:8
+          const uint32_t a_dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[e], 0x108, 0xf, 0xf, false);  // row_shl:8
+          ev[e] = low ? a[e] : b_up;
+          od[e] = low ? a_dn : b[e];
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(s_x + u * MfmaX<NT>::kBufBytes + (nt * 16 + row) * kXRow +
-                                                           (v * 4 + kq) * 16);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                            __builtin_bit_cast(bf16x8, bv), acc[nt], 0, 0, 0);
+          const unsigned char* xb = s_x + u * MfmaX<NT>::kBufBytes + (nt * 16 + row) * kXRow + p * 128 + kq * 32;
+          const u32x4 xe = *reinterpret_cast<const u32x4*>(xb);
+          const u32x4 xo = *reinterpret_cast<const u32x4*>(xb + 16);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ev),
+                                                            __builtin_bit_cast(bf16x8, xe), acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, od),
+                                                            __builtin_bit_cast(bf16x8, xo), acc[nt], 0, 0, 0);
         }
       }
   }

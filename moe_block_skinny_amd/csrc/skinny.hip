@@ -219,8 +219,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   const int s1 = s0 + a.ks_steps < J ? s0 + a.ks_steps : J;
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
-  const bool wok = n0 + row < a.N;
-  const bf16_t* wr = W + (size_t)(wok ? n0 + row : a.N - 1) * a.K + kq * 8;
+  const int ra = n0 + mfma_row_a(), rb = n0 + mfma_row_b();
+  const bool oka = ra < a.N, okb = rb < a.N;
+  const bf16_t* wa = W + (size_t)(oka ? ra : a.N - 1) * a.K + mfma_col_off();
+  const bf16_t* wb = W + (size_t)(okb ? rb : a.N - 1) * a.K + mfma_col_off();
   const bf16_t* xrow[PPT];
   bool xok[PPT];
 #pragma unroll
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows<NT, U>(wr, wok, xrow, xok, s0, s1, s_x, acc);
+  mfma_rows<NT, U>(wa, oka, wb, okb, xrow, xok, s0, s1, s_x, acc);
   if (a.ks_n == 1) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
