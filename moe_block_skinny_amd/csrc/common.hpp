@@ -248,6 +248,14 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Four consecutive floats (16-byte aligned) in one device-coherent vector
+// store: the same store as st_coherent, 16 bytes wide (each write-through
+// is a partial-line write at the memory side, so fewer, wider ones move
+// fewer bytes).  The compiler does not count this store in its own waits;
+// the arrival that publishes it drains every counter first (s_waitcnt 0).
+__device__ __forceinline__ void st_coherent4(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 
 // Grid-wide barrier in two halves, for a launch whose workgroups are all
 // resident at once.  Words in caller memory, zero before the first use: a

@@ -278,20 +278,24 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   mfma_rows<NT, kUpMfmaChunks>(wa, wok, wb, wok, xrow, xok, 0, a.d / 32, s_x, acc);
+  // lane l < 32: pairs i .. i+3 (i = p0 + 8w + 4(l/16), a multiple of 4,
+  // I a multiple of 32) of token nt*16 + l%16: one 16-byte store of h
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 hv;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float g = acc[nt][q];
       const float u = __shfl_xor(acc[nt][q], 32);
-      const int i = p0 + 8 * wave + 4 * (lane >> 4) + q;
-      const int t = nt * 16 + (lane & 15);
-      if (lane < 32 && i < v.I && t < v.m) {
-        int tok, sr;
-        token_of(a, slots, v, t, tok, sr);
-        st_coherent(&a.h[(size_t)sr * a.hld + i], silu(g) * u);
-      }
+      hv[q] = silu(acc[nt][q]) * u;
     }
+    const int i = p0 + 8 * wave + 4 * (lane >> 4);
+    const int t = nt * 16 + (lane & 15);
+    if (lane < 32 && i < v.I && t < v.m) {
+      int tok, sr;
+      token_of(a, slots, v, t, tok, sr);
+      st_coherent4(&a.h[(size_t)sr * a.hld + i], hv);
+    }
+  }
 }
 
 template <typename T>

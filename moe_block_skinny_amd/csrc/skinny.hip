@@ -244,33 +244,51 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
         if (n < a.N && t < a.M) finish_value(a, t, n, acc[nt][i]);
       }
   } else {
+    // partial sums [slice][M][N]: a lane's 4 values are 4 consecutive rows
+    // of one token, stored in one 16-byte device-coherent store
+    const bool vec = (a.N & 3) == 0;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 4 * kq, t = nt * 16 + row;
+      float* dst = &a.part[((size_t)ks * a.M + t) * a.N + n];
+      if (vec && t < a.M && n + 3 < a.N) {
+        st_coherent4(dst, acc[nt]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + 4 * kq + i, t = nt * 16 + row;
-        if (n < a.N && t < a.M) st_coherent(&a.part[((size_t)ks * a.M + t) * a.N + n], acc[nt][i]);
+        for (int i = 0; i < 4; ++i)
+          if (n + i < a.N && t < a.M) st_coherent(dst + i, acc[nt][i]);
       }
+    }
     __shared__ int s_last;
     if (!arrive_last(a.rg_counter + rgi, (uint32_t)a.ks_n, &s_last)) return;
-    // each thread: 4 consecutive rows of one token per pass, all slices'
-    // partials requested before any is added (one memory round trip)
+    // the last slice of the row group adds the partials in slice order:
+    // thread tid takes 4 consecutive rows of one token at positions tid,
+    // tid + 256, ... (NT of them: 64 rows x 16 NT tokens), and requests
+    // every slice's partials of all its positions before adding any (one
+    // memory round trip)
     const int nb = rgi * kMfmaRows;
-    for (int idx = tid * 4; idx < kMfmaRows * a.M; idx += blockDim.x * 4) {
+    f32x4 pv[NT][kMaxSlices];
+#pragma unroll
+    for (int p = 0; p < NT; ++p) {
+      const int idx = (tid + p * kMfmaWaves * 64) * 4;
       const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
-      const bool vec = (a.N & 3) == 0 && n + 4 <= a.N;   // else scalar below
-      const int nc = vec ? n : 0;
-      f32x4 pv[kMaxSlices];
+      const bool ok = vec && t < a.M && n + 3 < a.N;
 #pragma unroll
       for (int q = 0; q < kMaxSlices; ++q) {
         const int qc = q < a.ks_n ? q : 0;
-        pv[q] = *reinterpret_cast<const f32x4*>(&a.part[((size_t)qc * a.M + t) * a.N + nc]);
+        pv[p][q] = *reinterpret_cast<const f32x4*>(&a.part[((size_t)qc * a.M + (ok ? t : 0)) * a.N + (ok ? n : 0)]);
       }
-      if (vec) {
+    }
+#pragma unroll
+    for (int p = 0; p < NT; ++p) {
+      const int idx = (tid + p * kMfmaWaves * 64) * 4;
+      const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
+      if (t >= a.M || n >= a.N) continue;
+      if (vec && n + 3 < a.N) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < kMaxSlices; ++q)
-          if (q < a.ks_n) v += pv[q];
+          if (q < a.ks_n) v += pv[p][q];
 #pragma unroll
         for (int i = 0; i < 4; ++i) finish_value(a, t, n + i, v[i]);
       } else {
