@@ -256,6 +256,13 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
 __device__ __forceinline__ void st_coherent4(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
+// Eight bytes (8-byte aligned), the same way.
+__device__ __forceinline__ void st_coherent8(void* p, uint64_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_coherent16b(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Grid-wide barrier in two halves, for a launch whose workgroups are all
 // resident at once.  Words in caller memory, zero before the first use: a

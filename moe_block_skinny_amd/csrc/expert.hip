@@ -141,17 +141,53 @@ __global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a
 
 // ---- down projection -> Yslot ----------------------------------------------
 
+// Tasks (entry, 64-row tile of d), four waves of 16 rows.  A workgroup
+// takes a contiguous range of the task list (entry-major), so it stages an
+// entry's h once for all the tiles of that entry it holds.  MFMA entries
+// (m > 8): each wave requests its W2 rows (all K steps) first, then the
+// workgroup stages h (bf16 planes) in LDS and the waves multiply from it;
+// vector entries: down_valu with h from global.  Per-slot outputs go to
+// Yslot; combine_kernel adds them.
 template <typename T, int PATHS>
 __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
   __shared__ int32_t s_plan[kMaxPlanWords];
+  __shared__ __align__(16) unsigned char s_h[PATHS == kPathValu ? 16 : kHLdsBytes];
   const PlanView p = stage_plan(a, s_plan);
   const int tiles = (a.d + kDownRows - 1) / kDownRows;
   const int total = entries(a, p, true) * tiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = (total + gridDim.x - 1) / gridDim.x;
+  const int t0 = blockIdx.x * per, t1 = t0 + per < total ? t0 + per : total;
   const YSink sink = {a.Yslot, 0, 0, 0};
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
+  int staged = -1;   // entry whose h sits in s_h
+  for (int task = t0; task < t1; ++task) {
     const int e_idx = task / tiles, tile = task % tiles;
-    const ExpertView v = expert_view<T>(a, p, e_idx);
-    down_dispatch<T, PATHS>(a, p.slots, v, tile * kDownRows + (threadIdx.x >> 6) * 16, sink);
+    const ExpertView v = wave_uniform(expert_view<T>(a, p, e_idx));
+    const int r0 = tile * kDownRows + wave * 16;
+    if constexpr (PATHS != kPathValu && sizeof(T) == 2) {
+      if (use_mfma<PATHS>(v.m)) {
+        constexpr int JM = kMaxInter / 32;
+        const int J = v.I / 32;
+        const int row = lane & 15, kq = lane >> 4;
+        const bf16_t* wr = reinterpret_cast<const bf16_t*>(v.W2) + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
+        u32x4 wv[JM];
+#pragma unroll
+        for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
+        if (staged != e_idx) {
+          __syncthreads();   // the previous entry's h reads are done
+          stage_h_entry(a, p.slots, v, s_h);
+          staged = e_idx;
+        }
+        __syncthreads();
+        const int nt = (v.m + 15) / 16;
+        if (nt <= 1) down_mfma_lds<1>(a, p.slots, v, r0, wv, s_h);
+        else if (nt == 2) down_mfma_lds<2>(a, p.slots, v, r0, wv, s_h);
+        else if (nt == 3) down_mfma_lds<3>(a, p.slots, v, r0, wv, s_h);
+        else down_mfma_lds<4>(a, p.slots, v, r0, wv, s_h);
+        continue;
+      }
+    }
+    down_dispatch<T, kPathValu>(a, p.slots, v, r0, sink);
   }
 }
 
@@ -175,38 +211,31 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
   for (int i = threadIdx.x; i < a.B * a.k; i += blockDim.x) s_tw[i] = a.topk_w[i];
   if constexpr (PIPE) {
-    // h to LDS: fp32 as is, or for bf16 weights as bf16 hi/lo word rows
     const int nrows = a.B * a.k + a.B;
+    // h to LDS as stored (fp32, or for bf16 weights the hi and lo planes,
+    // which are the word rows down_valu_pipe reads)
     const int n4 = nrows * a.hld / 4;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-      const f32x4 x = reinterpret_cast<const f32x4*>(a.h)[i];
-      if constexpr (sizeof(T) == 2) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16x2(x.x, x.y, h0, l0);
-        split_bf16x2(x.z, x.w, h1, l1);
-        uint32_t* hw = reinterpret_cast<uint32_t*>(s_h);
-        hw[2 * i] = h0;
-        hw[2 * i + 1] = h1;
-        hw[(size_t)nrows * a.hld / 2 + 2 * i] = l0;
-        hw[(size_t)nrows * a.hld / 2 + 2 * i + 1] = l1;
-      } else {
-        reinterpret_cast<f32x4*>(s_h)[i] = x;
-      }
-    }
+    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+      reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
   }
-  __shared__ int s_order[PIPE ? kMaxB * kMaxK + kMaxB : 1];
+  __shared__ int s_order[kMaxB * kMaxK + kMaxB];
   const PlanView p = stage_plan(a, s_plan);   // its barrier also covers s_tw and s_h
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * rt;
   const YSink sink = {s_y, 1, r0, rt};
   const int ne = entries(a, p, true);
+  // entries by falling token count, dealt to the waves in snake order
+  // (w, 2nw-1-w, 2nw+w, ...) so their token totals come out close
+  if (wave == 0) order_entries(a, p, ne, s_order);
+  __syncthreads();
   if constexpr (PIPE) {
-    if (wave == 0) order_entries(a, p, ne, s_order);
-    __syncthreads();
     down_valu_pipe<T, RT>(a, p, ne, s_order, r0, rt, sink, s_h);
   } else {
-    for (int e_idx = wave; e_idx < ne; e_idx += nw)
-      down_dispatch<T, PATHS, RT>(a, p.slots, expert_view<T>(a, p, e_idx), r0, sink);
+    for (int j = 0;; ++j) {
+      const int pos = j * nw + ((j & 1) ? nw - 1 - wave : wave);
+      if (pos >= ne) break;
+      down_dispatch<T, PATHS, RT>(a, p.slots, expert_view<T>(a, p, s_order[pos]), r0, sink);
+    }
   }
   __syncthreads();
   const int has_shared = a.Ws13 ? 1 : 0;
@@ -277,16 +306,17 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
 }
 
 hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len) {
+  // two 4-wave workgroups per CU, each a contiguous range of the tasks
   const int tiles = (a.d + kDownRows - 1) / kDownRows;
   int g = max_entries(a) * tiles;
-  if (g > kMaxResidentWG) g = kMaxResidentWG;
+  if (g > 2 * kCUs) g = 2 * kCUs;
   if (g < 1) g = 1;
   const int paths = expert_paths(a.bf16, a.force, a.B);
   if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_kernel<float, kPathValu>), dim3(g), dim3(256), 0, st, a);
   else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathValu>), dim3(g), dim3(256), 0, st, a);
   else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathMfma>), dim3(g), dim3(256), 0, st, a);
   else launch(K_EXPERT_DOWN, (expert_down_kernel<bf16_t, kPathBoth>), dim3(g), dim3(256), 0, st, a);
-  if (desc) snprintf(desc, desc_len, "down grid=%d force=%d", g, a.force);
+  if (desc) snprintf(desc, desc_len, "down tasks grid=%d force=%d", g, a.force);
   return hipGetLastError();
 }
 

@@ -151,6 +151,48 @@ __device__ __forceinline__ void token_of(const ExpertLaunch& a, const int32_t* s
   }
 }
 
+// The SwiGLU output h of the slot rows (B*k routed slots, then B shared
+// tokens; row stride hld).  For fp32 weights h is fp32 [rows][hld].  For
+// bf16 weights every value v is kept as the pair hi = bf16(v), lo =
+// bf16(v - hi) (about 16 significant bits, the bf16 operand pair the down
+// products consume), in two planes of [rows][hld] bf16: hi at a.h, lo right
+// after it -- the same bytes as fp32, split once by the producer instead of
+// by every down workgroup.  Stored device-coherent (the fused block reads h
+// across workgroups of one launch).
+__device__ __forceinline__ int h_rows(const ExpertLaunch& a) { return a.B * a.k + a.B; }
+__device__ __forceinline__ uint16_t* h_hi(const ExpertLaunch& a) { return reinterpret_cast<uint16_t*>(a.h); }
+__device__ __forceinline__ uint16_t* h_lo(const ExpertLaunch& a) {
+  return reinterpret_cast<uint16_t*>(a.h) + (size_t)h_rows(a) * a.hld;
+}
+
+template <typename T>
+__device__ __forceinline__ void h_store(const ExpertLaunch& a, int sr, int i, float v) {
+  const size_t o = (size_t)sr * a.hld + i;
+  if constexpr (sizeof(T) == 2) {
+    const bf16_t hi = f32_to_bf16(v);
+    const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+    st_coherent16b(h_hi(a) + o, hi);
+    st_coherent16b(h_lo(a) + o, lo);
+  } else {
+    st_coherent(a.h + o, v);
+  }
+}
+
+// Values i .. i+3 (i a multiple of 4) of slot row sr.
+template <typename T>
+__device__ __forceinline__ void h_store4(const ExpertLaunch& a, int sr, int i, f32x4 v) {
+  const size_t o = (size_t)sr * a.hld + i;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t h0, l0, h1, l1;
+    split_bf16x2(v[0], v[1], h0, l0);
+    split_bf16x2(v[2], v[3], h1, l1);
+    st_coherent8(h_hi(a) + o, (uint64_t)h0 | ((uint64_t)h1 << 32));
+    st_coherent8(h_lo(a) + o, (uint64_t)l0 | ((uint64_t)l1 << 32));
+  } else {
+    st_coherent4(a.h + o, v);
+  }
+}
+
 // Kernel shape per entry.  PATHS is fixed per kernel instantiation: 1 = the
 // vector shape only (fp32, B <= 8 or forced), 2 = MFMA only (forced), 3 =
 // either, by token count (m > 8: MFMA).  Keeping unused shapes out of an
@@ -232,7 +274,7 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
 #pragma unroll
     for (int t = 0; t < MB; ++t)
       if (t == lane) sr = srow[t];
-    st_coherent(&a.h[(size_t)sr * a.hld + i], silu(g) * u);
+    h_store<T>(a, sr, i, silu(g) * u);
   }
 }
 
@@ -293,7 +335,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
     if (lane < 32 && i < v.I && t < v.m) {
       int tok, sr;
       token_of(a, slots, v, t, tok, sr);
-      st_coherent4(&a.h[(size_t)sr * a.hld + i], hv);
+      h_store4<bf16_t>(a, sr, i, hv);
     }
   }
 }
@@ -377,19 +419,18 @@ __device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* 
   for (int t = 0; t < v.m; ++t) {
     int tok, sr;
     token_of(a, slots, v, t, tok, sr);
-    float xs[VEC];
-    const float* hp = a.h + (size_t)sr * a.hld + (size_t)(cok ? c * VEC : 0);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) xs[e] = cok ? hp[e] : 0.f;
+    const size_t ho = (size_t)sr * a.hld + (size_t)(cok ? c * VEC : 0);
     float acc[R];
     if constexpr (sizeof(T) == 2) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split_bf16x2(xs[2 * q], xs[2 * q + 1], hi[q], lo[q]);
-      const u32x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 h4 = cok ? *reinterpret_cast<const u32x4*>(h_hi(a) + ho) : zero;
+      const u32x4 l4 = cok ? *reinterpret_cast<const u32x4*>(h_lo(a) + ho) : zero;
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_hilo(wv[r], h4, l4));
     } else {
+      float xs[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) xs[e] = cok ? a.h[ho + e] : 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_f32x(wv[r], xs, 0.f, T()));
     }
@@ -544,8 +585,8 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   const bf16_t* wr = W2 + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
   const int J = wave_uniform(v.I / 32);
   // all K steps of the wave's 16 rows requested at once (steps past J
-  // re-read the last one), then each token tile's h: one memory round trip
-  // per tile instead of one per step
+  // re-read the last one), then each token tile's h (bf16 hi and lo planes,
+  // split by the producer): one memory round trip per tile
   u32x4 wv[JM];
 #pragma unroll
   for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
@@ -555,37 +596,24 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
     int tok = 0, sr = 0;
     const bool ok = ti < v.m;
     if (ok) token_of(a, slots, v, ti, tok, sr);
-    const float* hr = a.h + (size_t)(ok ? sr : 0) * a.hld;
+    const uint16_t* hh = h_hi(a) + (size_t)(ok ? sr : 0) * a.hld;
+    const uint16_t* hl = h_lo(a) + (size_t)(ok ? sr : 0) * a.hld;
+    u32x4 hv[JM], lv[JM];
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+      hv[j] = *reinterpret_cast<const u32x4*>(hh + off);
+      lv[j] = *reinterpret_cast<const u32x4*>(hl + off);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // h in two halves of the steps (register pressure: two workgroups of
-    // eight waves share a CU)
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int jh = 0; jh < JM; jh += JM / 2) {
-      f32x4 h0[JM / 2], h1[JM / 2];
-#pragma unroll
-      for (int jj = 0; jj < JM / 2; ++jj) {
-        const int j = jh + jj;
-        const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
-        h0[jj] = *reinterpret_cast<const f32x4*>(hr + off);
-        h1[jj] = *reinterpret_cast<const f32x4*>(hr + off + 4);
-      }
-#pragma unroll
-      for (int jj = 0; jj < JM / 2; ++jj) {
-        const int j = jh + jj;
-        if (j < J) {
-          uint32_t hi[4], lo[4];
-          split_bf16x2(h0[jj].x, h0[jj].y, hi[0], lo[0]);
-          split_bf16x2(h0[jj].z, h0[jj].w, hi[1], lo[1]);
-          split_bf16x2(h1[jj].x, h1[jj].y, hi[2], lo[2]);
-          split_bf16x2(h1[jj].z, h1[jj].w, hi[3], lo[3]);
-          const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 hv4 = ok ? u32x4{hi[0], hi[1], hi[2], hi[3]} : zero;
-          const u32x4 lv4 = ok ? u32x4{lo[0], lo[1], lo[2], lo[3]} : zero;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
-                                                        __builtin_bit_cast(bf16x8, hv4), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
-                                                        __builtin_bit_cast(bf16x8, lv4), acc, 0, 0, 0);
-        }
+    for (int j = 0; j < JM; ++j) {
+      if (j < J) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                      __builtin_bit_cast(bf16x8, ok ? hv[j] : zero), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                      __builtin_bit_cast(bf16x8, ok ? lv[j] : zero), acc, 0, 0, 0);
       }
     }
     if (ok) {
@@ -593,6 +621,77 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 4 * kq + i;
         if (r < a.d) *sink.at(a, sr, r) = acc[i];
+      }
+    }
+  }
+}
+
+// ---- down projection as (entry, 64-row tile) tasks ------------------------
+
+// LDS image of one entry's h for the MFMA down: the token rows of the hi
+// plane (rows 0..63), then of the lo plane (rows 64..127), I bf16 each;
+// rows padded by 16 bytes so the 16 lanes reading one B operand (16 token
+// rows) spread over the LDS banks.
+constexpr int kHRowBytes = kMaxInter * 2 + 16;
+constexpr int kHLdsBytes = 2 * kMaxB * kHRowBytes;
+
+// Copy h of entry v's tokens (bf16 planes) into s_h with the whole workgroup.
+__device__ __forceinline__ void stage_h_entry(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                              unsigned char* s_h) {
+  const int per_row = v.I / 8;   // 16-byte pieces per plane row
+  const int n = v.m * 2 * per_row;
+  for (int pc = threadIdx.x; pc < n; pc += blockDim.x) {
+    const int t = pc / (2 * per_row), rem = pc % (2 * per_row);
+    const int plane = rem / per_row, q = rem % per_row;
+    int tok, sr;
+    token_of(a, slots, v, t, tok, sr);
+    const uint16_t* src = (plane ? h_lo(a) : h_hi(a)) + (size_t)sr * a.hld + q * 8;
+    *reinterpret_cast<u32x4*>(s_h + (plane * kMaxB + t) * kHRowBytes + q * 16) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+// Rows r0 .. r0+15 of entry v (m > 8) with one wave: the W2 rows (all K
+// steps, wv) were requested before h was staged; h from s_h.  Same products
+// in the same order as down_mfma, hence the same bits.  The per-slot outputs
+// (4 consecutive rows per lane) go to the global Yslot.
+template <int NT>
+__device__ __forceinline__ void down_mfma_lds(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
+                                              const u32x4 (&wv)[kMaxInter / 32], const unsigned char* s_h) {
+  constexpr int JM = kMaxInter / 32;
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const int J = wave_uniform(v.I / 32);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = nt * 16 + row;
+    const bool ok = t < v.m;
+    const unsigned char* hh = s_h + (size_t)(ok ? t : 0) * kHRowBytes + kq * 16;
+    const unsigned char* hl = hh + (size_t)kMaxB * kHRowBytes;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      if (j < J) {
+        const u32x4 hv = ok ? *reinterpret_cast<const u32x4*>(hh + j * 64) : zero;
+        const u32x4 lv = ok ? *reinterpret_cast<const u32x4*>(hl + j * 64) : zero;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                      __builtin_bit_cast(bf16x8, hv), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
+                                                      __builtin_bit_cast(bf16x8, lv), acc, 0, 0, 0);
+      }
+    }
+    if (ok) {
+      int tok, sr;
+      token_of(a, slots, v, t, tok, sr);
+      const YSink sink = {a.Yslot, 0, 0, 0};
+      const int r = r0 + 4 * kq;
+      float* dst = sink.at(a, sr, r);
+      if (r + 3 < a.d && (a.d & 3) == 0) {
+        *reinterpret_cast<f32x4*>(dst) = acc;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r + i < a.d) dst[i] = acc[i];
       }
     }
   }

@@ -114,23 +114,11 @@ __global__ __launch_bounds__(kBlockWaves * 64) void moe_block_kernel(BlockLaunch
   float* s_y = s_dyn;
   float* s_h = s_dyn + (size_t)nrows * rt;
   {
-    // h to LDS: fp32 as is, or for bf16 weights as bf16 hi/lo word rows
+    // h to LDS as stored (fp32, or for bf16 weights the hi and lo planes,
+    // which are the word rows down_valu_pipe reads)
     const int n4 = nrows * a.hld / 4;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-      const f32x4 x = reinterpret_cast<const f32x4*>(a.h)[i];
-      if constexpr (sizeof(T) == 2) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16x2(x.x, x.y, h0, l0);
-        split_bf16x2(x.z, x.w, h1, l1);
-        uint32_t* hw = reinterpret_cast<uint32_t*>(s_h);
-        hw[2 * i] = h0;
-        hw[2 * i + 1] = h1;
-        hw[(size_t)nrows * a.hld / 2 + 2 * i] = l0;
-        hw[(size_t)nrows * a.hld / 2 + 2 * i + 1] = l1;
-      } else {
-        reinterpret_cast<f32x4*>(s_h)[i] = x;
-      }
-    }
+    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+      reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
   }
   const int ne = p.n + (a.Ws13 ? 1 : 0);
   if (wave == 0) order_entries(a, p, ne, s_order);
