@@ -42,7 +42,10 @@
  *     SwiGLU intermediate, per-slot expert outputs and a completion counter.
  *     It must
  *     be zero-filled once before its first use (moe_workspace_init); every
- *     call leaves its counter words at zero again.  Two calls that run
+ *     call leaves its counter words at zero again.  The counter words sit at
+ *     the start of the workspace at offsets that do not depend on the sizes
+ *     (for N <= 63488), so one workspace large enough for the biggest call
+ *     may serve calls of different sizes in turn.  Two calls that run
  *     concurrently must not share a workspace.
  *   - Errors: every call validates all arguments on the host BEFORE any HIP
  *     call and returns MOE_EINVAL (null or misaligned pointer, bad dimension,

@@ -114,33 +114,37 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
   return MOE_OK;
 }
 
-// Skinny-product workspace: router logits fp32 [B][E] and its completion
-// counter (router only); with bf16 (where the MFMA shape may run) the fp32
-// partial sums of its K slices [slices][B][N] and one arrival counter per
-// 64-row group.
+// Skinny-product workspace.  First the counter words, at fixed offsets for
+// every shape (so one zero-filled workspace serves calls of any shape: each
+// call leaves its counters at zero, and no other call's data lands on
+// them): the router's completion counter (word 0) and one arrival counter
+// per 64-row group of the MFMA shape (words 32..); then the router logits
+// fp32 [B][E] (router only) and, with bf16 where the MFMA shape may run,
+// the fp32 partial sums of its K slices [slices][B][N].
+constexpr size_t kCounterBytes = 4096;   // fixed for N <= 64 * (1024 - 32)
+
 struct SkinnyWs {
   size_t logits, done, part, rg, total;
 };
 
 SkinnyWs skinny_ws(int B, int N, int K, int bf16, bool router) {
   SkinnyWs w;
-  size_t o = 0;
+  w.done = 0;
+  w.rg = 32 * 4;
+  size_t o = kCounterBytes;
+  const size_t rg_end = w.rg + (size_t)((N + 63) / 64) * 4;
+  if (rg_end > o) o = up(rg_end);
   w.logits = o;
   if (router) o = up(o + (size_t)B * N * 4);
-  w.done = o;
-  if (router) o = up(o + 4);
-  w.part = w.rg = o;
+  w.part = o;
+  bool sliced = false;
   if (bf16 && K >= 32) {
     int ks = 1, steps = 0;
     skinny_mfma_slices(B, N, K, &ks, &steps);
-    if (ks > 1) {
-      w.part = o;
-      o = up(o + (size_t)ks * B * N * 4);
-      w.rg = o;
-      o = up(o + (size_t)((N + 63) / 64) * 4);
-    }
+    sliced = ks > 1;
+    if (sliced) o = up(o + (size_t)ks * B * N * 4);
   }
-  w.total = o;
+  w.total = (router || sliced) ? o : 0;   // a plain vector-shape product needs none
   return w;
 }
 
@@ -168,6 +172,12 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   b.route = skinny_ws(B, E, d, bf16, true);
   b.ffn = expert_ws(B, k, I, Is);
   size_t o = 0;
+  // counter and flag words first, at offsets that do not depend on the
+  // shape: the fused kernel's barrier lines (2 count lines, 2 x
+  // kBlockMaxGrid flag lines, a status line), then the router's workspace,
+  // which starts with its own counters
+  b.sync = o;
+  o = up(o + (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4);
   b.route_off = o;
   o = up(o + b.route.total);
   b.ffn_off = o;
@@ -178,8 +188,6 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   o = up(o + (size_t)B * k * 4);
   b.plan = o;
   o = up(o + (size_t)moe_plan_words(B, k, E) * 4);
-  b.sync = o;   // fused kernel: 2 count lines, 2 x kBlockMaxGrid flag lines, a status line
-  o = up(o + (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4);
   b.total = o;
   return b;
 }

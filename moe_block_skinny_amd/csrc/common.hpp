@@ -8,11 +8,11 @@
 //   * only weights, which no kernel of the library ever writes, are read with
 //     plain or non-temporal loads;
 //   * anything produced inside the same launch by another workgroup (router
-//     logits, K-slice partial sums, h in the fused block) is stored
-//     device-coherent (st_coherent) and read only after the acquire fence of
-//     a completion counter or grid barrier (arrive_last, grid_wait), which
-//     the compiler cannot hoist a load above and which invalidates the
-//     non-coherent caches first.
+//     logits, K-slice partial sums, top-k ids, h in the fused block) is
+//     stored device-coherent (st_coherent*) and read with device-coherent
+//     loads (ld_coherent*) only after a completion counter or grid barrier
+//     (arrive_last, grid_wait) has seen every producer arrive; their
+//     acquire fence keeps the compiler from hoisting a load above the wait.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -248,20 +248,42 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Four consecutive floats (16-byte aligned) in one device-coherent vector
-// store: the same store as st_coherent, 16 bytes wide (each write-through
-// is a partial-line write at the memory side, so fewer, wider ones move
-// fewer bytes).  The compiler does not count this store in its own waits;
-// the arrival that publishes it drains every counter first (s_waitcnt 0).
-__device__ __forceinline__ void st_coherent4(float* p, f32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
-}
-// Eight bytes (8-byte aligned), the same way.
-__device__ __forceinline__ void st_coherent8(void* p, uint64_t v) {
-  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
-}
 __device__ __forceinline__ void st_coherent16b(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of values that other workgroups of the same launch stored with the
+// stores above.  Device-coherent loads (the same cache policy as a relaxed
+// agent-scope atomic load): a line this XCD's L2 still holds from before
+// the producers wrote it -- e.g. from an earlier launch over the same
+// workspace -- is not returned stale, which an acquire by one thread does
+// not guarantee for every line (observed: a stale K-slice partial).
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coherent_i32(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wide device-coherent loads and stores: raw buffer loads / stores with the
+// sc1 cache policy (the compiler tracks them like any memory access, waits
+// and hazards included), at a byte offset from the base of a buffer that
+// covers 2 GB (offsets past it read 0 and write nothing).  Each write-through
+// is a partial-line write at the memory side, so fewer, wider stores move
+// fewer bytes.
+typedef __amdgpu_buffer_rsrc_t coherent_rsrc_t;
+__device__ __forceinline__ coherent_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCachePolicySc1 = 16;   // sc1: coherent at device scope
+__device__ __forceinline__ u32x4 ld_coherent4(coherent_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1);
+}
+__device__ __forceinline__ void st_coherent4(coherent_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicySc1);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_coherent8(coherent_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCachePolicySc1);
 }
 
 // Grid-wide barrier in two halves, for a launch whose workgroups are all
@@ -324,11 +346,6 @@ __device__ __forceinline__ void grid_wait(const uint32_t* flags, uint32_t g0, in
   __syncthreads();
 }
 
-// Read of a value another workgroup of this launch produced, by the last
-// workgroup after arrive_last's acquire fence.  A plain load: the fence keeps
-// the compiler from moving it above the synchronisation and has invalidated
-// the caches it could be served stale from.
-__device__ __forceinline__ float ld_after_acquire(const float* p) { return *p; }
 
 // Orderable 32-bit key of a logit: larger key <=> larger value (finite
 // inputs; -0 is folded into +0 first), so equal keys are equal logits.

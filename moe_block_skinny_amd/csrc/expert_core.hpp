@@ -186,10 +186,11 @@ __device__ __forceinline__ void h_store4(const ExpertLaunch& a, int sr, int i, f
     uint32_t h0, l0, h1, l1;
     split_bf16x2(v[0], v[1], h0, l0);
     split_bf16x2(v[2], v[3], h1, l1);
-    st_coherent8(h_hi(a) + o, (uint64_t)h0 | ((uint64_t)h1 << 32));
-    st_coherent8(h_lo(a) + o, (uint64_t)l0 | ((uint64_t)l1 << 32));
+    const coherent_rsrc_t r = coherent_rsrc(a.h);
+    st_coherent8(r, (uint32_t)(o * 2), u32x2{h0, h1});
+    st_coherent8(r, (uint32_t)(((size_t)h_rows(a) * a.hld + o) * 2), u32x2{l0, l1});
   } else {
-    st_coherent4(a.h + o, v);
+    st_coherent4(coherent_rsrc(a.h), (uint32_t)(o * 4), __builtin_bit_cast(u32x4, v));
   }
 }
 

@@ -117,8 +117,9 @@ __global__ __launch_bounds__(kBlockWaves * 64) void moe_block_kernel(BlockLaunch
     // h to LDS as stored (fp32, or for bf16 weights the hi and lo planes,
     // which are the word rows down_valu_pipe reads)
     const int n4 = nrows * a.hld / 4;
+    const coherent_rsrc_t hrs = coherent_rsrc(a.h);   // written by other workgroups of this launch
     for (int i = threadIdx.x; i < n4; i += blockDim.x)
-      reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
+      reinterpret_cast<u32x4*>(s_h)[i] = ld_coherent4(hrs, (uint32_t)i * 16u);
   }
   const int ne = p.n + (a.Ws13 ? 1 : 0);
   if (wave == 0) order_entries(a, p, ne, s_order);

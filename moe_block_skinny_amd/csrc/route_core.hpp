@@ -49,7 +49,8 @@ __device__ __forceinline__ float sel_value(uint64_t c) { return key_value((uint3
 // Top-k of one token with the whole wave.  lv[i] is the logit of expert
 // lane + 64 i (ignored at or past E).  Writes the k ids in ascending order
 // and their weights exp(l - l_max) / sum over the selection to ids / w, and
-// also to ids2 / w2 when those are non-null.  Requires 1 <= k <= min(E, 16).
+// also to ids2 / w2 when those are non-null (device-coherent stores).
+// Requires 1 <= k <= min(E, 16).
 __device__ __forceinline__ void topk_wave(const float (&lv)[kNI], int E, int k, TopkScratch& sc, int32_t* ids,
                                           float* w, int32_t* ids2, float* w2) {
   const int lane = threadIdx.x & 63;
@@ -128,20 +129,22 @@ __device__ __forceinline__ void topk_wave(const float (&lv)[kNI], int E, int k, 
     const float wt = ex / z;
     ids[pos] = e;
     w[pos] = wt;
-    if (ids2) {
-      ids2[pos] = e;
-      w2[pos] = wt;
+    if (ids2) {   // read by other workgroups of the launch in the split finish
+      __hip_atomic_store(ids2 + pos, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(w2 + pos, wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Load the logits of token t (row t of [M][E]) as topk_wave expects them.
+// Load the logits of token t (row t of [M][E]) as topk_wave expects them;
+// device-coherent loads (other workgroups of the launch may have stored
+// them).
 __device__ __forceinline__ void load_logit_row(const float* logits, int t, int E, float (&lv)[kNI]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < kNI; ++i) {
     const int e = lane + 64 * i;
-    lv[i] = logits[(size_t)t * E + (e < E ? e : E - 1)];
+    lv[i] = ld_coherent(logits + (size_t)t * E + (e < E ? e : E - 1));
   }
 }
 

@@ -69,23 +69,18 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
   }
 }
 
-// NTK: waves that select (each holds a TopkScratch in LDS).
-template <int NTK>
-__device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
-  __shared__ int32_t s_ids[kMaxB * kMaxK];
-  __shared__ float s_w[kMaxB * kMaxK];
-  __shared__ TopkScratch s_tk[NTK];
+// The routing plan of all M*k slots from their expert ids (s_ids, LDS), by
+// the whole workgroup; sc: 128 ints of LDS scratch.
+__device__ __forceinline__ void route_plan(const SkinnyLaunch& a, const int32_t* s_ids, int* sc) {
   __shared__ unsigned long long s_mask[kMaxE];
   __shared__ int s_cnt[kMaxE];
   __shared__ int s_act[kMaxE];
   __shared__ int s_n;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int M = a.M, E = a.N, k = a.k, nslot = M * k;
-
-  topk_tokens<NTK>(a, s_tk, s_ids, s_w);
-  __syncthreads();
+  (void)M;
   if (nslot <= 64) {  // one wave sorts the slots
-    if (wave == 0) plan_wave(s_ids, nslot, E, reinterpret_cast<int*>(s_tk), a.plan, nullptr);
+    if (wave == 0) plan_wave(s_ids, nslot, E, sc, a.plan, nullptr);
     return;
   }
   for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
@@ -140,6 +135,18 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   }
 }
 
+// Top-k of every token and the plan, by one workgroup.  NTK: waves that
+// select (each holds a TopkScratch in LDS).
+template <int NTK>
+__device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
+  __shared__ int32_t s_ids[kMaxB * kMaxK];
+  __shared__ float s_w[kMaxB * kMaxK];
+  __shared__ TopkScratch s_tk[NTK];
+  topk_tokens<NTK>(a, s_tk, s_ids, s_w);
+  __syncthreads();
+  route_plan(a, s_ids, reinterpret_cast<int*>(s_tk));
+}
+
 // Router tail: every router workgroup arrives once; the last runs the finish.
 __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   __shared__ int s_flag;
@@ -148,12 +155,30 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   route_finish<kTopkWaves>(a);
 }
 
-// The finish as a launch of its own (one 16-wave workgroup, 16 selecting
-// waves), after a logits-only router launch whose workgroups have too few
-// waves to select many tokens quickly (the MFMA shape has 4).
+// The finish as a launch of its own, after a logits-only router launch
+// whose workgroups have too few waves to select many tokens quickly (the
+// MFMA shape has 4): ceil(M/16) workgroups of 16 waves, one token per wave;
+// each stores its tokens' ids and weights (device-coherent) and arrives;
+// the last one reads every token's ids and builds the plan.
 constexpr int kFinishWaves = 16;
 __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyLaunch a) {
-  route_finish<kFinishWaves>(a);
+  __shared__ TopkScratch s_tk[kFinishWaves];
+  __shared__ int32_t s_ids[kMaxB * kMaxK];
+  __shared__ float s_w[kMaxB * kMaxK];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kFinishWaves + wave;
+  const int E = a.N, k = a.k;
+  if (t < a.M) {
+    float lv[kNI];
+    load_logit_row(a.logits, t, E, lv);
+    topk_wave(lv, E, k, s_tk[wave], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
+              a.topk_w + (size_t)t * k);
+  }
+  if (!arrive_last(a.done_counter, gridDim.x, &s_last)) return;
+  for (int i = threadIdx.x; i < a.M * k; i += blockDim.x) s_ids[i] = ld_coherent_i32(a.topk_ids + i);
+  __syncthreads();
+  route_plan(a, s_ids, reinterpret_cast<int*>(s_tk));
 }
 
 // ---- vector-ALU kernels (gemv / splitk) ----------------------------------
@@ -187,16 +212,19 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
 // weights).  With several slices the workgroups store fp32 partial sums
 // [slice][M][N]; the last of a row group's slices to arrive adds them in
 // slice order (deterministic).
-constexpr int kMaxSlices = 8;
+constexpr int kMaxSlices = 32;
+constexpr int kSliceGroup = 8;   // partial sums requested together by the last slice
 
 void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
   (void)M;
   const int rg = (N + kMfmaRows - 1) / kMfmaRows;
   const int J = K / 32;
   const int nchunk = (J + kChunk - 1) / kChunk;
-  int ks = 256 / rg;                         // at most one workgroup per CU:
-  if (ks > kMaxSlices) ks = kMaxSlices;      // a second one would double the time;
+  int ks = 256 / rg;                         // one workgroup per CU (two per
+  if (ks > kMaxSlices) ks = kMaxSlices;      // CU measured slower);
                                              // the cap bounds the partial traffic
+                                             // (small N, e.g. the router: many
+                                             // slices, so every CU streams)
   if (ks > nchunk) ks = nchunk;
   if (ks < 1) ks = 1;
   const int chunks = (nchunk + ks - 1) / ks;
@@ -247,12 +275,13 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
     // partial sums [slice][M][N]: a lane's 4 values are 4 consecutive rows
     // of one token, stored in one 16-byte device-coherent store
     const bool vec = (a.N & 3) == 0;
+    const coherent_rsrc_t prs = coherent_rsrc(a.part);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = n0 + 4 * kq, t = nt * 16 + row;
       float* dst = &a.part[((size_t)ks * a.M + t) * a.N + n];
       if (vec && t < a.M && n + 3 < a.N) {
-        st_coherent4(dst, acc[nt]);
+        st_coherent4(prs, (uint32_t)((((size_t)ks * a.M + t) * a.N + n) * 4), __builtin_bit_cast(u32x4, acc[nt]));
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -263,21 +292,32 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
     if (!arrive_last(a.rg_counter + rgi, (uint32_t)a.ks_n, &s_last)) return;
     // the last slice of the row group adds the partials in slice order:
     // thread tid takes 4 consecutive rows of one token at positions tid,
-    // tid + 256, ... (NT of them: 64 rows x 16 NT tokens), and requests
-    // every slice's partials of all its positions before adding any (one
-    // memory round trip)
+    // tid + 256, ... (NT of them: 64 rows x 16 NT tokens); the partials of
+    // kSliceGroup slices for all its positions are requested before any is
+    // added (one memory round trip per group of slices)
     const int nb = rgi * kMfmaRows;
-    f32x4 pv[NT][kMaxSlices];
+    f32x4 sum[NT];
 #pragma unroll
-    for (int p = 0; p < NT; ++p) {
-      const int idx = (tid + p * kMfmaWaves * 64) * 4;
-      const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
-      const bool ok = vec && t < a.M && n + 3 < a.N;
+    for (int p = 0; p < NT; ++p) sum[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < a.ks_n; q0 += kSliceGroup) {
+      f32x4 pv[NT][kSliceGroup];
 #pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q) {
-        const int qc = q < a.ks_n ? q : 0;
-        pv[p][q] = *reinterpret_cast<const f32x4*>(&a.part[((size_t)qc * a.M + (ok ? t : 0)) * a.N + (ok ? n : 0)]);
+      for (int p = 0; p < NT; ++p) {
+        const int idx = (tid + p * kMfmaWaves * 64) * 4;
+        const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
+        const bool ok = vec && t < a.M && n + 3 < a.N;
+#pragma unroll
+        for (int q = 0; q < kSliceGroup; ++q) {
+          const int qc = q0 + q < a.ks_n ? q0 + q : 0;
+          pv[p][q] = __builtin_bit_cast(
+              f32x4, ld_coherent4(prs, (uint32_t)((((size_t)qc * a.M + (ok ? t : 0)) * a.N + (ok ? n : 0)) * 4)));
+        }
       }
+#pragma unroll
+      for (int p = 0; p < NT; ++p)
+#pragma unroll
+        for (int q = 0; q < kSliceGroup; ++q)
+          if (q0 + q < a.ks_n) sum[p] += pv[p][q];
     }
 #pragma unroll
     for (int p = 0; p < NT; ++p) {
@@ -285,16 +325,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
       const int t = idx / kMfmaRows, n = nb + idx % kMfmaRows;
       if (t >= a.M || n >= a.N) continue;
       if (vec && n + 3 < a.N) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < kMaxSlices; ++q)
-          if (q < a.ks_n) v += pv[p][q];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) finish_value(a, t, n + i, v[i]);
+        for (int i = 0; i < 4; ++i) finish_value(a, t, n + i, sum[p][i]);
       } else {
         for (int i = 0; i < 4 && n + i < a.N; ++i) {
           float v = 0.f;
-          for (int q = 0; q < a.ks_n; ++q) v += ld_after_acquire(&a.part[((size_t)q * a.M + t) * a.N + n + i]);
+          for (int q = 0; q < a.ks_n; ++q) v += ld_coherent(&a.part[((size_t)q * a.M + t) * a.N + n + i]);
           finish_value(a, t, n + i, v);
         }
       }
@@ -372,8 +408,9 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
       default: go(skinny_mfma_kernel<4, true>, skinny_mfma_kernel<4, false>); break;
     }
     if (split) {
-      if (prof) hipExtLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishWaves * 64), 0, st, nullptr, e1, 0u, a);
-      else hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kFinishWaves * 64), 0, st, a);
+      const dim3 fg((unsigned)((a.M + kFinishWaves - 1) / kFinishWaves));
+      if (prof) hipExtLaunchKernelGGL(route_finish_kernel, fg, dim3(kFinishWaves * 64), 0, st, nullptr, e1, 0u, a);
+      else hipLaunchKernelGGL(route_finish_kernel, fg, dim3(kFinishWaves * 64), 0, st, a);
     }
     name = split ? "mfma + finish launch" : "mfma";
   } else if (a.router) {

@@ -93,6 +93,29 @@ def test_skinny_gemm_dense_workload(B):
         assert np.all(err16 <= bound + 2.0 ** -8 * np.abs(ref)), (var, B)
 
 
+def test_skinny_gemm_workspace_reuse():
+    """Back-to-back MFMA products with K slices over ONE workspace, with
+    different inputs and batch sizes: every call's partial sums must be read
+    as that call wrote them, never as an earlier call left them in a cache."""
+    N, K = 3072, 7168
+    Wh = synth.dense_w()
+    W = dev(Wh)
+    ws = ws_for(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=64, N=N, K=K)
+    outs = []
+    with variant("mfma"):
+        for i, B in enumerate((64, 32, 17, 64, 16, 48, 33, 64)):
+            Xh = synth.to_bf16_bits(np.random.default_rng(100 + i).standard_normal((B, K)).astype(np.float32))
+            Y = torch.empty((B, N), device="cuda")
+            mb.skinny_gemm(dev(Xh), W, Y, ws)
+            outs.append((Xh, Y))
+    torch.cuda.synchronize()
+    for i, (Xh, Y) in enumerate(outs):
+        ref = orc.skinny_gemm(Xh, Wh)
+        bound = fp32_sum_bound(widen(Xh), widen(Wh))
+        err = np.abs(host(Y) - ref)
+        assert np.all(err <= bound), (i, Xh.shape[0], float(err.max()))
+
+
 def test_skinny_gemm_fp32():
     rng = np.random.default_rng(3)
     for B, N, K in [(1, 70, 1024), (2, 33, 260), (7, 129, 516)]:
