@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a
       __shared__ TopkScratch s_tk[kUpWaves];
       __shared__ int32_t s_ids[64];
       __shared__ float s_w[64];
-      p = route_here(a, s_plan, s_tk, s_ids, s_w);
+      p = route_here<false>(a, s_plan, s_tk, s_ids, s_w);
     } else {
       p = stage_plan(a, s_plan);
     }

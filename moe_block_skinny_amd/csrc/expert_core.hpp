@@ -67,7 +67,8 @@ __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s
 // router's finishing workgroup.  s_tk: one TopkScratch per selecting wave
 // (at most kTopkWaves).  The last workgroup of the grid also stores
 // ids, weights and plan for the down launch and the caller.  Ends with a
-// barrier.
+// barrier.  SAME_LAUNCH: the logits were stored in this launch (fused block).
+template <bool SAME_LAUNCH>
 __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s_plan, TopkScratch* s_tk,
                                                int32_t* s_ids, float* s_w) {
   constexpr int QB = 2;
@@ -80,7 +81,7 @@ __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int t = t0 + nw * q;
-      load_logit_row(a.logits, t < B ? t : B - 1, E, lv[q]);
+      load_logit_row<SAME_LAUNCH>(a.logits, t < B ? t : B - 1, E, lv[q]);
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlockWaves * 64) void moe_block_kernel(BlockLaunch
 
   // 2. top-k and plan of all tokens, in this workgroup's LDS
   grid_wait(f.flags_r, g_r, f.spin_limit, f.status);
-  const PlanView p = route_here(a, s_plan, reinterpret_cast<TopkScratch*>(s_dyn), s_ids, s_w);
+  const PlanView p = route_here<true>(a, s_plan, reinterpret_cast<TopkScratch*>(s_dyn), s_ids, s_w);
 
   // 3. routed gate/up + SwiGLU
   {

@@ -136,15 +136,17 @@ __device__ __forceinline__ void topk_wave(const float (&lv)[kNI], int E, int k, 
   }
 }
 
-// Load the logits of token t (row t of [M][E]) as topk_wave expects them;
-// device-coherent loads (other workgroups of the launch may have stored
-// them).
+// Load the logits of token t (row t of [M][E]) as topk_wave expects them:
+// device-coherent loads when other workgroups of the same launch stored them
+// (SAME_LAUNCH), plain loads when an earlier launch did.
+template <bool SAME_LAUNCH>
 __device__ __forceinline__ void load_logit_row(const float* logits, int t, int E, float (&lv)[kNI]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < kNI; ++i) {
     const int e = lane + 64 * i;
-    lv[i] = ld_coherent(logits + (size_t)t * E + (e < E ? e : E - 1));
+    const float* p = logits + (size_t)t * E + (e < E ? e : E - 1);
+    lv[i] = SAME_LAUNCH ? ld_coherent(p) : *p;
   }
 }
 

@@ -57,7 +57,7 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int t = t0 + nw * q;
-      load_logit_row(a.logits, t < M ? t : M - 1, E, lv[q]);
+      load_logit_row<true>(a.logits, t < M ? t : M - 1, E, lv[q]);
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
   const int E = a.N, k = a.k;
   if (t < a.M) {
     float lv[kNI];
-    load_logit_row(a.logits, t, E, lv);
+    load_logit_row<false>(a.logits, t, E, lv);
     topk_wave(lv, E, k, s_tk[wave], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
               a.topk_w + (size_t)t * k);
   }
