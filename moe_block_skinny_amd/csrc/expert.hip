@@ -55,6 +55,7 @@ __device__ __forceinline__ int entries(const ExpertLaunch& a, const PlanView& p,
 // pairs as above; every workgroup lists the tasks per entry in LDS (a
 // prefix over the plan) and walks them.
 constexpr int kUpWaves = 4;
+constexpr int kUpAllMfmaTasks = 256;   // one 64-row task per compute unit
 constexpr int kUpPairsValu = 2;
 
 template <typename T, int PATHS>
@@ -101,6 +102,15 @@ __global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a
     const int ne = p.n + (tiles_s > 0 ? 1 : 0);   // routed entries, then the shared one
     const int tiles_m = (a.I + kUpPairsMfma - 1) / kUpPairsMfma;
     const int tiles_ms = (a.Is + kUpPairsMfma - 1) / kUpPairsMfma;
+    // Every entry takes the matrix shape once the routed entries alone make
+    // a 64-row task per compute unit: the vector shape re-reads the entry's
+    // activations (m rows of d) for every 4 weight rows, so at up to 8
+    // tokens it moves up to twice its weight bytes again and streams at
+    // about 2/3 the matrix shape's rate per workgroup (batch 64: ~34 such
+    // entries made ~4300 vector tasks, 120 us); below that count the small
+    // vector tasks are needed to spread the entries over the compute units.
+    const bool all_mfma = PATHS == kPathBoth && p.n * tiles_m >= kUpAllMfmaTasks;
+    auto mfma_entry = [&](int m) { return all_mfma || use_mfma<PATHS>(m); };
     // s_tstart[e]: first task of entry e (one wave, 64 entries per pass)
     if (wave == 0) {
       const int lane = threadIdx.x & 63;
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a
         if (e < ne) {
           const bool sh = e >= p.n;
           const int m = sh ? a.B : p.offs[e + 1] - p.offs[e];
-          n = use_mfma<PATHS>(m) ? (sh ? tiles_ms : tiles_m) : (sh ? tiles_s : tiles_r);
+          n = mfma_entry(m) ? (sh ? tiles_ms : tiles_m) : (sh ? tiles_s : tiles_r);
         }
         const int incl = wave_incl_scan(n);
         if (e < ne) s_tstart[e] = base + incl - n;
@@ -132,7 +142,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a
       const int e = wave_uniform(lo);
       const ExpertView v = e < p.n ? expert_view<T>(a, p, e) : shared_view(a);
       const int tile = task - s_tstart[e];
-      if (use_mfma<PATHS>(v.m)) up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x);
+      if (mfma_entry(v.m)) up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x);
       else up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
       __syncthreads();  // s_red / s_x are reused by the next task
     }

@@ -66,92 +66,185 @@ __device__ __forceinline__ int mfma_piece_token(int i) {
 // offset by 8*(lane/8) elements; read only when oka / okb.  xrow[i]:
 // activation row of this thread's i-th piece token, read only when xok[i]
 // (else zeros go to LDS).  X rows and W rows hold K = 32 * (steps of the
-// whole row) elements; steps index both.  s_x: MfmaX<NT, U>::kLdsBytes.
+// whole row) elements; steps index both.
 //
-// Each iteration requests the activations and then the weights of U chunks
-// before waiting for any of them, so a wave keeps U * 8 KB of weights in
-// flight, and leaves nothing in flight across the loop's back edge (a load
-// still in flight there made the compiler copy its registers at the back
-// edge and wait for every load).  Steps past s1 hold zero activations and
-// zeroed weights (their loads read a cached activation row), so every chunk
-// is multiplied whole, without a branch per step.
+// The work is cut in stages of U chunks (U * kChunk steps).  A stage's
+// loads are issued unconditionally: steps past s1 read a cached activation
+// row (weights) or the last step again (activations), and hold zero
+// weights and activations when multiplied, so every chunk is multiplied
+// whole, without a branch per step.
+
+// Activations of the stage at step c (clamped into range).
+template <int NT, int U>
+__device__ __forceinline__ void mfma_issue_x(const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread], int c, int s1,
+                                             u32x4 (&xv)[U][MfmaX<NT>::kPerThread]) {
+  constexpr int PPT = MfmaX<NT>::kPerThread;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int q = (tid + i * kMfmaWaves * 64) % (4 * kChunk);
+      const int j = c + u * kChunk + q / 4;
+      const int jc = j < s1 ? j : s1 - 1;
+      xv[u][i] = ld128(xrow[i] + (size_t)jc * 32 + (q & 3) * 8);
+    }
+}
+
+// Weights of the stage at step c (a lane whose step is past s1 reads the
+// cached row `spare`).
+template <int U>
+__device__ __forceinline__ void mfma_issue_w(const bf16_t* wa, const bf16_t* wb, const bf16_t* spare, int c, int s1,
+                                             u32x4 (&va)[U][kChunk / 2], u32x4 (&vb)[U][kChunk / 2]) {
+  const int hi_step = (threadIdx.x & 63) >> 5;   // lanes 32-63 hold the pair's second step
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int p = 0; p < kChunk / 2; ++p) {
+      const int j = c + u * kChunk + 2 * p;
+      const bool in = j + hi_step < s1;
+      va[u][p] = ld128_stream(in ? wa + (size_t)j * 32 : spare);
+      vb[u][p] = ld128_stream(in ? wb + (size_t)j * 32 : spare);
+    }
+}
+
+// The stage's activations into the LDS buffer `buf` (U chunks); zeros for
+// tokens past the batch and steps past s1.
+template <int NT, int U>
+__device__ __forceinline__ void mfma_store_x(const u32x4 (&xv)[U][MfmaX<NT>::kPerThread],
+                                             const bool (&xok)[MfmaX<NT>::kPerThread], int c, int s1,
+                                             unsigned char* buf) {
+  constexpr int PPT = MfmaX<NT>::kPerThread;
+  const int tid = threadIdx.x;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + i * kMfmaWaves * 64;
+      const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
+      const bool ok = xok[i] && c + u * kChunk + q / 4 < s1;
+      *reinterpret_cast<u32x4*>(buf + u * MfmaX<NT>::kBufBytes + t * kXRow + q * 16) = ok ? xv[u][i] : zero;
+    }
+}
+
+// The stage's products: weights in registers, activations from `buf`.
+template <int NT, int U>
+__device__ __forceinline__ void mfma_compute(const u32x4 (&va)[U][kChunk / 2], const u32x4 (&vb)[U][kChunk / 2],
+                                             bool oka, bool okb, int c, int s1, const unsigned char* buf,
+                                             f32x4 (&acc)[NT]) {
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const bool low = row < 8;
+  const int hi_step = lane >> 5;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int p = 0; p < kChunk / 2; ++p) {
+      const bool in = c + u * kChunk + 2 * p + hi_step < s1;
+      const u32x4 a = (in && oka) ? va[u][p] : zero;
+      const u32x4 b = (in && okb) ? vb[u][p] : zero;
+      u32x4 ev, od;   // A operands of the pair's first and second step
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b[e], 0x118, 0xf, 0xf, false);  // row_shr:8
+        const uint32_t a_dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[e], 0x108, 0xf, 0xf, false);  // row_shl:8
+        ev[e] = low ? a[e] : b_up;
+        od[e] = low ? a_dn : b[e];
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const unsigned char* xb = buf + u * MfmaX<NT>::kBufBytes + (nt * 16 + row) * kXRow + p * 128 + kq * 32;
+        const u32x4 xe = *reinterpret_cast<const u32x4*>(xb);
+        const u32x4 xo = *reinterpret_cast<const u32x4*>(xb + 16);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ev),
+                                                          __builtin_bit_cast(bf16x8, xe), acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, od),
+                                                          __builtin_bit_cast(bf16x8, xo), acc[nt], 0, 0, 0);
+      }
+    }
+}
+
+// One stage in flight at a time: each iteration requests the activations
+// and then the weights of its stage before waiting for any of them, and
+// leaves nothing in flight across the loop's back edge (a load still in
+// flight there made the compiler copy its registers at the back edge and
+// wait for every load).  s_x: MfmaX<NT, U>::kLdsBytes.
 template <int NT, int U>
 __device__ __forceinline__ void mfma_rows(const bf16_t* wa, bool oka, const bf16_t* wb, bool okb,
                                           const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread],
                                           const bool (&xok)[MfmaX<NT>::kPerThread], int s0, int s1,
                                           unsigned char* s_x, f32x4 (&acc)[NT]) {
   constexpr int PPT = MfmaX<NT>::kPerThread;
-  constexpr int NP = kChunk / 2;       // step pairs per chunk
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int row = lane & 15, kq = lane >> 4;
-  const bool low = row < 8;
-  const int hi_step = lane >> 5;       // lanes 32-63 hold the pair's second step
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  constexpr int NP = kChunk / 2;
   s0 = __builtin_amdgcn_readfirstlane(s0);
   s1 = __builtin_amdgcn_readfirstlane(s1);
   for (int c = s0; c < s1; c += U * kChunk) {
     u32x4 xv[U][PPT], va[U][NP], vb[U][NP];
-    // activations of the iteration's chunks (clamped into range) ...
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int q = (tid + i * kMfmaWaves * 64) % (4 * kChunk);
-        const int j = c + u * kChunk + q / 4;
-        const int jc = j < s1 ? j : s1 - 1;
-        xv[u][i] = ld128(xrow[i] + (size_t)jc * 32 + (q & 3) * 8);
-      }
-    __builtin_amdgcn_sched_barrier(0);   // activations first: st_x waits only for them
-    // ... then the weights (a lane whose step is past s1 reads a cached row)
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int j = c + u * kChunk + 2 * p;
-        const bool in = j + hi_step < s1;
-        va[u][p] = ld128_stream(in ? wa + (size_t)j * 32 : xrow[0]);
-        vb[u][p] = ld128_stream(in ? wb + (size_t)j * 32 : xrow[0]);
-      }
+    mfma_issue_x<NT, U>(xrow, c, s1, xv);
+    __builtin_amdgcn_sched_barrier(0);   // activations first: the LDS stores wait only for them
+    mfma_issue_w<U>(wa, wb, xrow[0], c, s1, va, vb);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();              // the previous iteration's LDS reads are done
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * kMfmaWaves * 64;
-        const int t = pc / (4 * kChunk), q = pc % (4 * kChunk);
-        const bool ok = xok[i] && c + u * kChunk + q / 4 < s1;
-        *reinterpret_cast<u32x4*>(s_x + u * MfmaX<NT>::kBufBytes + t * kXRow + q * 16) = ok ? xv[u][i] : zero;
-      }
+    mfma_store_x<NT, U>(xv, xok, c, s1, s_x);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);   // no weight use above the barrier (it would wait there)
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const bool in = c + u * kChunk + 2 * p + hi_step < s1;
-        const u32x4 a = (in && oka) ? va[u][p] : zero;
-        const u32x4 b = (in && okb) ? vb[u][p] : zero;
-        u32x4 ev, od;   // A operands of the pair's first and second step
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t b_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b[e], 0x118, 0xf, 0xf, false);  // row_shr:8
-          const uint32_t a_dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[e], 0x108, 0xf, 0xf, false);  // row_shl:8
-          ev[e] = low ? a[e] : b_up;
-          od[e] = low ? a_dn : b[e];
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const unsigned char* xb = s_x + u * MfmaX<NT>::kBufBytes + (nt * 16 + row) * kXRow + p * 128 + kq * 32;
-          const u32x4 xe = *reinterpret_cast<const u32x4*>(xb);
-          const u32x4 xo = *reinterpret_cast<const u32x4*>(xb + 16);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ev),
-                                                            __builtin_bit_cast(bf16x8, xe), acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, od),
-                                                            __builtin_bit_cast(bf16x8, xo), acc[nt], 0, 0, 0);
-        }
-      }
+    mfma_compute<NT, U>(va, vb, oka, okb, c, s1, s_x, acc);
+  }
+}
+
+// Two stages in flight: the loads of stage i+1 are requested before the
+// products of stage i, whose weights sit in the other register set and
+// whose activations sit in the other LDS buffer.  Unrolled by two so each
+// register set keeps its registers across the back edge (the set in
+// flight there is the one the next iteration multiplies first).  One
+// barrier per stage: it publishes the stage's activations and retires the
+// reads of the buffer the next stores overwrite.
+// s_x: 2 * MfmaX<NT, U>::kLdsBytes.
+template <int NT, int U>
+__device__ __forceinline__ void mfma_rows_db(const bf16_t* wa, bool oka, const bf16_t* wb, bool okb,
+                                             const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread],
+                                             const bool (&xok)[MfmaX<NT>::kPerThread], int s0, int s1,
+                                             unsigned char* s_x, f32x4 (&acc)[NT]) {
+  constexpr int PPT = MfmaX<NT>::kPerThread;
+  constexpr int NP = kChunk / 2;
+  constexpr int G = U * kChunk;
+  s0 = __builtin_amdgcn_readfirstlane(s0);
+  s1 = __builtin_amdgcn_readfirstlane(s1);
+  unsigned char* buf0 = s_x;
+  unsigned char* buf1 = s_x + MfmaX<NT, U>::kLdsBytes;
+  u32x4 xv[U][PPT], va0[U][NP], vb0[U][NP], va1[U][NP], vb1[U][NP];
+  mfma_issue_x<NT, U>(xrow, s0, s1, xv);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_issue_w<U>(wa, wb, xrow[0], s0, s1, va0, vb0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_store_x<NT, U>(xv, xok, s0, s1, buf0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = s0;; c += 2 * G) {
+    mfma_issue_x<NT, U>(xrow, c + G, s1, xv);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_issue_w<U>(wa, wb, xrow[0], c + G, s1, va1, vb1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_compute<NT, U>(va0, vb0, oka, okb, c, s1, buf0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_store_x<NT, U>(xv, xok, c + G, s1, buf1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + G >= s1) break;
+    mfma_issue_x<NT, U>(xrow, c + 2 * G, s1, xv);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_issue_w<U>(wa, wb, xrow[0], c + 2 * G, s1, va0, vb0);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_compute<NT, U>(va1, vb1, oka, okb, c + G, s1, buf1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_store_x<NT, U>(xv, xok, c + 2 * G, s1, buf0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 2 * G >= s1) break;
   }
 }
 

@@ -234,9 +234,8 @@ void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
 
 template <int NT, bool ROUTER>
 __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaunch a) {
-  // two chunks (16 KB of weights per wave) in flight (four measured slower)
-  constexpr int U = 2;
-  __shared__ __align__(16) unsigned char s_x[MfmaX<NT, U>::kLdsBytes];
+  constexpr int U = 1;
+  __shared__ __align__(16) unsigned char s_x[2 * MfmaX<NT, U>::kLdsBytes];
   constexpr int PPT = MfmaX<NT>::kPerThread;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
@@ -262,7 +261,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows<NT, U>(wa, oka, wb, okb, xrow, xok, s0, s1, s_x, acc);
+  mfma_rows_db<NT, U>(wa, oka, wb, okb, xrow, xok, s0, s1, s_x, acc);
   if (a.ks_n == 1) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
