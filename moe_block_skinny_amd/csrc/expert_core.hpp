@@ -26,6 +26,7 @@
 namespace moe {
 
 constexpr int kMaxPlanWords = 2 + 2 * 512 + 64 * 16;
+constexpr int kDownTokGroup = 4; // tokens whose h the vector down requests together
 constexpr int kUpPairsMfma = 32;  // gate/up pairs per MFMA up task (64 weight rows)
 constexpr int kUpMfmaChunks = 2;  // chunks in flight per wave (two workgroups per CU)
 
@@ -418,29 +419,53 @@ __device__ __forceinline__ void down_valu(const ExpertLaunch& a, const int32_t* 
     const int row = rbase + P * r;
     wv[r] = (cok && row < a.d) ? ld128_stream(W2 + (size_t)row * v.I + (size_t)c * VEC) : zero;
   }
-  for (int t = 0; t < v.m; ++t) {
-    int tok, sr;
-    token_of(a, slots, v, t, tok, sr);
-    const size_t ho = (size_t)sr * a.hld + (size_t)(cok ? c * VEC : 0);
-    float acc[R];
-    if constexpr (sizeof(T) == 2) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      const u32x4 h4 = cok ? *reinterpret_cast<const u32x4*>(h_hi(a) + ho) : zero;
-      const u32x4 l4 = cok ? *reinterpret_cast<const u32x4*>(h_lo(a) + ho) : zero;
+  if constexpr (sizeof(T) == 2) {
+    // h of kDownTokGroup tokens requested before any is used (one memory
+    // round trip per group, not per token); a token past m re-reads the last
+    const size_t co = (size_t)(cok ? c * VEC : 0);
+    for (int t0 = 0; t0 < v.m; t0 += kDownTokGroup) {
+      u32x4 h4[kDownTokGroup], l4[kDownTokGroup];
+      int srs[kDownTokGroup];
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_hilo(wv[r], h4, l4));
-    } else {
-      float xs[VEC];
+      for (int q = 0; q < kDownTokGroup; ++q) {
+        const int t = t0 + q < v.m ? t0 + q : v.m - 1;
+        int tok;
+        token_of(a, slots, v, t, tok, srs[q]);
+        const size_t ho = (size_t)srs[q] * a.hld + co;
+        h4[q] = cok ? *reinterpret_cast<const u32x4*>(h_hi(a) + ho) : zero;
+        l4[q] = cok ? *reinterpret_cast<const u32x4*>(h_lo(a) + ho) : zero;
+      }
+#pragma unroll
+      for (int q = 0; q < kDownTokGroup; ++q) {
+        if (t0 + q >= v.m) break;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_hilo(wv[r], h4[q], l4[q]));
+        if (c == 0) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int row = rbase + P * r;
+            if (row < a.d) *sink.at(a, srs[q], row) = acc[r];
+          }
+        }
+      }
+    }
+  } else {
+    for (int t = 0; t < v.m; ++t) {
+      int tok, sr;
+      token_of(a, slots, v, t, tok, sr);
+      const size_t ho = (size_t)sr * a.hld + (size_t)(cok ? c * VEC : 0);
+      float xs[VEC], acc[R];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) xs[e] = cok ? a.h[ho + e] : 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(dot_chunk_f32x(wv[r], xs, 0.f, T()));
-    }
-    if (c == 0) {
+      if (c == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = rbase + P * r;
-        if (row < a.d) *sink.at(a, sr, row) = acc[r];
+        for (int r = 0; r < R; ++r) {
+          const int row = rbase + P * r;
+          if (row < a.d) *sink.at(a, sr, row) = acc[r];
+        }
       }
     }
   }
@@ -592,7 +617,9 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   u32x4 wv[JM];
 #pragma unroll
   for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
-#pragma unroll
+  // one token tile's h in registers at a time (two overlapped tiles took
+  // 64 more registers than the 4-waves-per-SIMD budget and spilled)
+#pragma unroll 1
   for (int nt = 0; nt < NT; ++nt) {
     const int ti = nt * 16 + row;
     int tok = 0, sr = 0;

@@ -214,9 +214,9 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
 // slice order (deterministic).
 constexpr int kMaxSlices = 32;
 constexpr int kSliceGroup = 8;   // partial sums requested together by the last slice
+constexpr int kMaxPartialBytes = 128 * 1024;   // partials one last slice reads
 
 void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
-  (void)M;
   const int rg = (N + kMfmaRows - 1) / kMfmaRows;
   const int J = K / 32;
   const int nchunk = (J + kChunk - 1) / kChunk;
@@ -226,6 +226,13 @@ void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
                                              // (small N, e.g. the router: many
                                              // slices, so every CU streams)
   if (ks > nchunk) ks = nchunk;
+  // the last slice of a row group reads every slice's partial tile (64 rows
+  // x 16 NT tokens x 4 bytes): at most kMaxPartialBytes, so the reduction
+  // tail stays one or two memory round trips (the 384-row router at batch
+  // 64 with 28 slices spent ~10 us reading 458 KB in one workgroup)
+  const int nt = (M + 15) / 16;
+  const int ks_cap = kMaxPartialBytes / (kMfmaRows * 16 * nt * 4);
+  if (ks > ks_cap) ks = ks_cap;
   if (ks < 1) ks = 1;
   const int chunks = (nchunk + ks - 1) / ks;
   *ks_steps = chunks * kChunk;
