@@ -356,8 +356,12 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, ch
   else if (!a.bf16) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<float, kPathValu, 16, false>), grid, block, lds, st, a);
   else if (pipe) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 28, true>), grid, block, lds, st, a);
   else if (paths == kPathValu) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathValu, 16, false>), grid, block, lds, st, a);
-  else if (paths == kPathMfma) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16, false>), grid, block, lds, st, a);
-  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathBoth, 16, false>), grid, block, lds, st, a);
+  // with the matrix shape allowed, every entry takes it, also one of one
+  // token: an entry's W2 rows cost one round trip either way, the matrix
+  // shape was no slower per entry at batch 64 (~6 us against ~7 us for 1-2
+  // tokens, ~10-16 us for 3-8 on the vector shape), and the kernel holding
+  // both shapes spilled 35 registers to scratch
+  else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16, false>), grid, block, lds, st, a);
   if (desc)
     snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d%s force=%d", g, rt, nw,
              pipe ? " prefetch" : "", a.force);
