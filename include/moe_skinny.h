@@ -42,10 +42,11 @@
  *     SwiGLU intermediate, per-slot expert outputs and a completion counter.
  *     It must
  *     be zero-filled once before its first use (moe_workspace_init); every
- *     call leaves its counter words at zero again.  The counter words sit at
- *     the start of the workspace at offsets that do not depend on the sizes
- *     (for N <= 63488), so one workspace large enough for the biggest call
- *     may serve calls of different sizes in turn.  Two calls that run
+ *     call leaves its counter words at zero again.  The counter words sit in
+ *     a header at the start of the workspace, at offsets that depend neither
+ *     on the op nor on the sizes (for N <= 63488), and every call's data
+ *     follows that header, so one workspace large enough for the biggest
+ *     call may serve calls of any op and size in turn.  Two calls that run
  *     concurrently must not share a workspace.
  *   - Errors: every call validates all arguments on the host BEFORE any HIP
  *     call and returns MOE_EINVAL (null or misaligned pointer, bad dimension,

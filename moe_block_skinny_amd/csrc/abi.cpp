@@ -114,15 +114,23 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
   return MOE_OK;
 }
 
-// Skinny-product workspace.  First the counter words, at fixed offsets for
-// every shape (so one zero-filled workspace serves calls of any shape: each
-// call leaves its counters at zero, and no other call's data lands on
-// them): the router's completion counter (word 0) and one arrival counter
-// per 64-row group of the MFMA shape (words 32..); then the router logits
-// fp32 [B][E] (router only) and, with bf16 where the MFMA shape may run,
-// the fp32 partial sums of its K slices [slices][B][N].
-constexpr size_t kCounterBytes = 4096;   // fixed for N <= 64 * (1024 - 32)
+// Workspace layout.  Every call's workspace starts with the same header of
+// counter and flag words at fixed offsets, whatever the op and the sizes, and
+// every call's data follows the header, so one zero-filled workspace large
+// enough for the biggest call can serve calls of any op and size in turn:
+// each call leaves its counters at zero, and no call's data ever lands on a
+// counter.  The header holds the router's completion counter (word 0), one
+// arrival counter per 64-row group of the MFMA product (words 32.., for
+// N <= 63488), then the fused block's barrier lines (2 count lines, 2 x
+// kBlockMaxGrid flag lines, a status line).
+constexpr size_t kCounterBytes = 4096;
+constexpr size_t kSyncOff = kCounterBytes;
+constexpr size_t kSyncBytes = (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4;
+constexpr size_t kHeaderBytes = (kSyncOff + kSyncBytes + kAlign - 1) / kAlign * kAlign;
 
+// Skinny product / router: after the header, the router logits fp32 [B][N]
+// (router only) and, where the MFMA shape may run with K slices (bf16), the
+// fp32 partial sums of its slices [slices][B][N].
 struct SkinnyWs {
   size_t logits, done, part, rg, total;
 };
@@ -131,7 +139,7 @@ SkinnyWs skinny_ws(int B, int N, int K, int bf16, bool router) {
   SkinnyWs w;
   w.done = 0;
   w.rg = 32 * 4;
-  size_t o = kCounterBytes;
+  size_t o = kHeaderBytes;
   const size_t rg_end = w.rg + (size_t)((N + 63) / 64) * 4;
   if (rg_end > o) o = up(rg_end);
   w.logits = o;
@@ -140,14 +148,22 @@ SkinnyWs skinny_ws(int B, int N, int K, int bf16, bool router) {
   bool sliced = false;
   if (bf16 && K >= 32) {
     int ks = 1, steps = 0;
-    skinny_mfma_slices(B, N, K, &ks, &steps);
-    sliced = ks > 1;
+    if (router) {
+      // the MFMA router (any B when forced) stores the partial sums of
+      // every K slice, one slice included, for its finish launch
+      router_mfma_slices(B, N, K, &ks, &steps);
+      sliced = true;
+    } else {
+      skinny_mfma_slices(B, N, K, &ks, &steps);
+      sliced = ks > 1;
+    }
     if (sliced) o = up(o + (size_t)ks * B * N * 4);
   }
   w.total = (router || sliced) ? o : 0;   // a plain vector-shape product needs none
   return w;
 }
 
+// Experts: after the header, the SwiGLU intermediate h.
 struct ExpertWs {
   size_t h, total;
   int hld;
@@ -156,32 +172,28 @@ struct ExpertWs {
 ExpertWs expert_ws(int B, int k, int I, int Is) {
   ExpertWs w;
   w.hld = I > Is ? I : Is;
-  w.h = 0;
-  w.total = up((size_t)(B * k + B) * w.hld * 4);
+  w.h = kHeaderBytes;
+  w.total = up(w.h + (size_t)(B * k + B) * w.hld * 4);
   return w;
 }
 
+// Block: the router's layout at offset 0 (its counters are the header's),
+// the fused barrier lines in the header, then h, ids, weights and plan.
 struct BlockWs {
   SkinnyWs route;
-  ExpertWs ffn;
-  size_t route_off, ffn_off, ids, w, plan, sync, total;
+  size_t route_off, ffn_h, ids, w, plan, sync, total;
+  int hld;
 };
 
 BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   BlockWs b;
   b.route = skinny_ws(B, E, d, bf16, true);
-  b.ffn = expert_ws(B, k, I, Is);
-  size_t o = 0;
-  // counter and flag words first, at offsets that do not depend on the
-  // shape: the fused kernel's barrier lines (2 count lines, 2 x
-  // kBlockMaxGrid flag lines, a status line), then the router's workspace,
-  // which starts with its own counters
-  b.sync = o;
-  o = up(o + (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4);
-  b.route_off = o;
-  o = up(o + b.route.total);
-  b.ffn_off = o;
-  o = up(o + b.ffn.total);
+  b.route_off = 0;
+  b.sync = kSyncOff;
+  b.hld = I > Is ? I : Is;
+  size_t o = up(b.route.total);
+  b.ffn_h = o;
+  o = up(o + (size_t)(B * k + B) * b.hld * 4);
   b.ids = o;
   o = up(o + (size_t)B * k * 4);
   b.w = o;
@@ -301,7 +313,7 @@ ExpertLaunch expert_launch(int dt, int B, int d, int E, int k, int I, const void
   a.W2 = W2;
   a.Ws13 = Ws13;
   a.Ws2 = Ws2;
-  a.h = reinterpret_cast<float*>(ws + L.h);
+  a.h = ws ? reinterpret_cast<float*>(ws + L.h) : nullptr;
   a.hld = L.hld;
   a.force = force;
   return a;
@@ -555,7 +567,8 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(w + L.ids);
   float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.w);
   int32_t* plan = reinterpret_cast<int32_t*>(w + L.plan);
-  ExpertLaunch ex = expert_launch(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, w + L.ffn_off, force);
+  ExpertLaunch ex = expert_launch(dtype, B, d, E, k, I, X, plan, W13, W2, Is, Ws13, Ws2, nullptr, force);
+  ex.h = reinterpret_cast<float*>(w + L.ffn_h);
   ex.topk_w = tw;
   ex.out = out;
   ex.out_bf16 = bf16;

@@ -59,7 +59,7 @@ constexpr int kUpAllMfmaTasks = 256;   // one 64-row task per compute unit
 constexpr int kUpPairsValu = 2;
 
 template <typename T, int PATHS>
-__global__ __launch_bounds__(kUpWaves * 64) void expert_up_kernel(ExpertLaunch a) {
+__global__ __launch_bounds__(kUpWaves * 64, 2) void expert_up_kernel(ExpertLaunch a) {
   constexpr int PPT = kUpPairsValu;
   __shared__ int32_t s_plan[kMaxPlanWords];
   __shared__ float s_red[PPT * 2 * kPartStride];

@@ -322,7 +322,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows<NT, kUpMfmaChunks>(wa, wok, wb, wok, xrow, xok, 0, a.d / 32, s_x, acc);
+  mfma_rows_db<NT, kUpMfmaChunks / 2>(wa, wok, wb, wok, xrow, xok, 0, a.d / 32, s_x, acc);
   // lane l < 32: pairs i .. i+3 (i = p0 + 8w + 4(l/16), a multiple of 4,
   // I a multiple of 32) of token nt*16 + l%16: one 16-byte store of h
 #pragma unroll

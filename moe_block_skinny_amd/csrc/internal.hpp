@@ -80,6 +80,9 @@ struct SkinnyLaunch {
   int ks_n, ks_steps;
   float* part;
   uint32_t* rg_counter;
+  // router on the MFMA shape with its finish launch: every K slice stores
+  // its partial sums and the finish launch adds them (defer = 1)
+  int defer;
 };
 
 // The whole block in one launch (fused kernel, small batch on the vector
@@ -147,6 +150,7 @@ int skinny_rows_per_block(int variant, int router);
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router);
 // K slices of the MFMA shape (also sizes the partial-sum workspace)
 void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps);
+void router_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps);
 int shared_up_tiles_host(const ExpertLaunch& ex, int nw);
 
 }  // namespace moe

@@ -155,28 +155,101 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
   route_finish<kTopkWaves>(a);
 }
 
-// The finish as a launch of its own, after a logits-only router launch
-// whose workgroups have too few waves to select many tokens quickly (the
-// MFMA shape has 4): ceil(M/16) workgroups of 16 waves, one token per wave;
-// each stores its tokens' ids and weights (device-coherent) and arrives;
-// the last one reads every token's ids and builds the plan.
-constexpr int kFinishWaves = 16;
+// The finish as a launch of its own, after the MFMA router product, whose
+// workgroups store the partial sums of their K slices: one wave per token
+// adds its token's partials in slice order (the same order in every run),
+// adds the bias, selects the top-k and stores ids and weights
+// (device-coherent) and arrives; the last workgroup to arrive reads every
+// token's ids and builds the plan.  The partials of up to kFinishSlices
+// slices are requested at once (16-byte loads, 4 experts per lane), so a
+// token costs one or two memory round trips however many slices there are.
+constexpr int kFinishWaves = 4;
+constexpr int kFinishSlices = 16;
 __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyLaunch a) {
   __shared__ TopkScratch s_tk[kFinishWaves];
   __shared__ int32_t s_ids[kMaxB * kMaxK];
   __shared__ float s_w[kMaxB * kMaxK];
+  __shared__ __align__(16) float s_lg[kFinishWaves][kMaxE];
   __shared__ int s_last;
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * kFinishWaves + wave;
   const int E = a.N, k = a.k;
   if (t < a.M) {
     float lv[kNI];
-    load_logit_row<false>(a.logits, t, E, lv);
+    if ((E & 3) == 0) {
+      // lane l sums experts 4l .. 4l+3 and 256 + 4l .. +3
+      constexpr int NV = kMaxE / 256;
+      const int nv4 = E >> 2;
+      f32x4 sum[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < a.ks_n; q0 += kFinishSlices) {
+        f32x4 pv[kFinishSlices][NV];
+#pragma unroll
+        for (int q = 0; q < kFinishSlices; ++q) {
+          const int qc = q0 + q < a.ks_n ? q0 + q : a.ks_n - 1;
+          const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * E);
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const int j = lane + 64 * v;
+            pv[q][v] = row[j < nv4 ? j : nv4 - 1];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kFinishSlices; ++q)
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (q0 + q < a.ks_n) sum[v] += pv[q][v];
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int j = lane + 64 * v;
+        if (j < nv4) *reinterpret_cast<f32x4*>(&s_lg[wave][4 * j]) = sum[v];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < kNI; ++i) {
+        const int e = lane + 64 * i;
+        lv[i] = s_lg[wave][e < E ? e : E - 1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kNI; ++i) lv[i] = 0.f;
+      for (int q = 0; q < a.ks_n; ++q)
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+          const int e = lane + 64 * i;
+          lv[i] += a.part[((size_t)q * a.M + t) * E + (e < E ? e : E - 1)];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        if (a.bias) lv[i] += a.bias[(size_t)t * a.bias_ld + e];
+        a.logits[(size_t)t * E + e] = lv[i];
+        if (a.logits_out) a.logits_out[(size_t)t * E + e] = lv[i];
+      }
+    }
     topk_wave(lv, E, k, s_tk[wave], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
               a.topk_w + (size_t)t * k);
   }
   if (!arrive_last(a.done_counter, gridDim.x, &s_last)) return;
-  for (int i = threadIdx.x; i < a.M * k; i += blockDim.x) s_ids[i] = ld_coherent_i32(a.topk_ids + i);
+  {
+    // every token's ids, all requested before any is stored
+    constexpr int PER = kMaxB * kMaxK / (kFinishWaves * 64);
+    int32_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = threadIdx.x + j * kFinishWaves * 64;
+      v[j] = ld_coherent_i32(a.topk_ids + (i < a.M * k ? i : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = threadIdx.x + j * kFinishWaves * 64;
+      if (i < a.M * k) s_ids[i] = v[j];
+    }
+  }
   __syncthreads();
   route_plan(a, s_ids, reinterpret_cast<int*>(s_tk));
 }
@@ -239,6 +312,25 @@ void skinny_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
   *ks_n = (J + *ks_steps - 1) / *ks_steps;
 }
 
+// K slices of the MFMA router: enough 64-row x K-slice workgroups to put
+// one on most compute units, one LDS chunk (8 steps) each at E = 384, d =
+// 7168; nothing is reduced inside the launch (the finish launch adds the
+// slices), so the partial traffic only has to stay below the weight bytes:
+// [slices][M][N] fp32 against N x K bf16, i.e. slices x M x 2 < K.
+void router_mfma_slices(int M, int N, int K, int* ks_n, int* ks_steps) {
+  const int rg = (N + kMfmaRows - 1) / kMfmaRows;
+  const int J = K / 32;
+  const int nchunk = (J + kChunk - 1) / kChunk;
+  int ks = 256 / rg;
+  if (ks > nchunk) ks = nchunk;
+  const int cap = K / (2 * (M > 0 ? M : 1));
+  if (ks > cap) ks = cap;
+  if (ks < 1) ks = 1;
+  const int chunks = (nchunk + ks - 1) / ks;
+  *ks_steps = chunks * kChunk;
+  *ks_n = (J + *ks_steps - 1) / *ks_steps;
+}
+
 template <int NT, bool ROUTER>
 __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaunch a) {
   constexpr int U = 1;
@@ -269,6 +361,23 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   mfma_rows_db<NT, U>(wa, oka, wb, okb, xrow, xok, s0, s1, s_x, acc);
+  if (ROUTER && a.defer) {
+    // partial sums [slice][M][N] for the finish launch (a later launch: plain
+    // stores); a lane's 4 values are 4 consecutive rows of one token
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 4 * kq, t = nt * 16 + row;
+      float* dst = &a.part[((size_t)ks * a.M + t) * a.N + n];
+      if ((a.N & 3) == 0 && t < a.M && n + 3 < a.N) {
+        *reinterpret_cast<f32x4*>(dst) = acc[nt];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < a.N && t < a.M) dst[i] = acc[nt][i];
+      }
+    }
+    return;
+  }
   if (a.ks_n == 1) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -377,7 +486,8 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
   const int nrg = (a.N + rows - 1) / rows;
   const int nw = a.S;
   if (a.variant == VAR_MFMA) {
-    skinny_mfma_slices(a.M, a.N, a.K, &a.ks_n, &a.ks_steps);
+    if (a.router && a.finish) router_mfma_slices(a.M, a.N, a.K, &a.ks_n, &a.ks_steps);
+    else skinny_mfma_slices(a.M, a.N, a.K, &a.ks_n, &a.ks_steps);
   } else {
     a.ks_n = 1;
     a.ks_steps = 0;
@@ -391,7 +501,7 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
   dim3 grid((unsigned)(nwg + extra)), block((unsigned)(64 * nw));
   const char* name = "?";
   if (a.variant == VAR_MFMA) {
-    if (a.ks_n > 1 && (!a.part || !a.rg_counter)) return hipErrorInvalidValue;
+    if ((a.ks_n > 1 || (a.router && a.finish)) && (!a.part || !a.rg_counter)) return hipErrorInvalidValue;
     const int nt = (a.M + 15) / 16;
     const size_t lds = 0;
     // router with finish: the product launch stores logits only, then the
@@ -399,7 +509,10 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
     // dispatch records the start event and the finish's the stop event
     const bool split = a.router && a.finish;
     SkinnyLaunch p = a;
-    if (split) p.finish = 0;
+    if (split) {
+      p.finish = 0;
+      p.defer = 1;
+    }
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool prof = a.router && profile_events_for(K_ROUTE, &e0, &e1);
     auto go = [&](auto rk, auto pk) {

@@ -314,14 +314,15 @@ def test_combine(dt, B, d, k, shared):
 
 # ---------------------------------------------------------------- whole block
 
-def run_block(c, W13, W2, Ws13, Ws2):
+def run_block(c, W13, W2, Ws13, Ws2, ws=None):
     cfg = c.cfg
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     dt = mb.DT_BF16 if cfg.dtype == "bf16" else mb.DT_F32
     out = torch.full((cfg.B, cfg.d), float("nan"), dtype=tdt, device="cuda")
     ids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
     w = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
-    ws = ws_for(mb.OP_BLOCK, dt, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is)
+    if ws is None:
+        ws = ws_for(mb.OP_BLOCK, dt, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is)
     bias = None if c.bias is None else dev(c.bias)
     mb.moe_block(dev(c.X), dev(c.Wr), cfg.k, W13, W2, out, ws, Ws13, Ws2, bias, c.bias_ld, ids, w)
     torch.cuda.synchronize()
@@ -388,3 +389,43 @@ def test_block_batch_invariance_on_gpu():
         out1, ids1, _ = run_block(sub, W13, W2, Ws13, Ws2)
         assert np.array_equal(host(ids1)[0], host(ids8)[t])
         assert np.max(np.abs(host(out1)[0] - g8[t])) <= 2e-2 * rms(g8[t])
+
+
+def test_one_workspace_serves_every_op_in_turn():
+    """One zero-filled workspace, sized for the biggest call, used in turn by
+    a sliced MFMA product, the standalone router, experts and combine, and the
+    block at two batch sizes: no call's data may land on another call's
+    counters, so every block result equals the one on a fresh workspace."""
+    cases = {n: case_and_weights(n) for n in ("tp8_b64", "tp16_b1")}
+    nbytes = 0
+    for c, _ in cases.values():
+        cfg = c.cfg
+        kw = dict(B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is)
+        nbytes = max(nbytes, mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, **kw),
+                     mb.workspace_bytes(mb.OP_ROUTE, mb.DT_BF16, **kw),
+                     mb.workspace_bytes(mb.OP_EXPERT_FFN, mb.DT_BF16, **kw))
+    nbytes = max(nbytes, mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=64, N=3072, K=7168))
+    ws = mb.workspace(nbytes)
+    fresh = {n: run_block(c, *w)[0] for n, (c, w) in cases.items()}
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    X = torch.randn((64, 7168), generator=gen, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((3072, 7168), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    Y = torch.empty((64, 3072), dtype=torch.bfloat16, device="cuda")
+    for name in ("tp8_b64", "tp16_b1", "tp8_b64"):
+        c, (W13, W2, Ws13, Ws2) = cases[name]
+        cfg = c.cfg
+        mb.skinny_gemm(X, W, Y, ws)
+        ids = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((cfg.B, cfg.k), device="cuda")
+        plan = torch.empty((mb.plan_words(cfg.B, cfg.k, cfg.E),), dtype=torch.int32, device="cuda")
+        bias = None if c.bias is None else dev(c.bias)
+        mb.moe_route(dev(c.X), dev(c.Wr), cfg.k, ids, tw, plan, ws, bias=bias, bias_ld=c.bias_ld)
+        Ys = torch.empty((cfg.B, cfg.k + 1, cfg.d), device="cuda")
+        mb.moe_expert_ffn(dev(c.X), plan, W13, W2, cfg.k, Ys, ws, Ws13, Ws2)
+        out = torch.empty((cfg.B, cfg.d), dtype=torch.bfloat16, device="cuda")
+        mb.moe_combine(Ys, tw, True, out)
+        got, got_ids, _ = run_block(c, W13, W2, Ws13, Ws2, ws=ws)
+        say("shared workspace", name)
+        assert np.array_equal(host(ids), c.ids)
+        assert np.array_equal(host(got_ids), c.ids)
+        assert torch.equal(got.view(torch.int16), fresh[name].view(torch.int16))
