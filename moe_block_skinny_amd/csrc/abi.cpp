@@ -285,11 +285,13 @@ SkinnyLaunch route_launch(int dt, int v, int B, int d, int E, int k, const void*
 moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const void* Wr,
                        const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
                        float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
-                       const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr) {
+                       const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr,
+                       int plan_by_consumer = 0) {
   int v;
   moe_status_t s = resolve_skinny(dt == MOE_DT_BF16, B, d, &v);
   if (s) return s;
   SkinnyLaunch a = route_launch(dt, v, B, d, E, k, X, Wr, bias, bias_ld, ids, w, plan, logits_out, ws, finish);
+  a.plan_by_consumer = plan_by_consumer && v == VAR_MFMA;
   if (shared) a.ex = *shared;
   if (logits) *logits = a.logits;
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
@@ -620,15 +622,25 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
     // the vector router launch carries the shared expert's vector gate/up;
     // otherwise it is a task of the gate/up launch
     ex.skip_shared = Ws13 && paths == kPathValu && v != VAR_MFMA;
+    // after the MFMA router the finish launch stores ids and weights only,
+    // and every gate/up workgroup builds the plan from the ids (the gate/up
+    // kernel then has the matrix shape, whose LDS holds the plan scratch)
+    const bool consumer_plan = v == VAR_MFMA && paths != kPathValu;
+    if (consumer_plan) {
+      ex.ids_in = ids;
+      ex.plan_out = plan;
+    }
     if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off,
-                       st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr)))
+                       st, d1, sizeof d1, ex.skip_shared ? &ex : nullptr, 1, nullptr, consumer_plan ? 1 : 0)))
       return s;
   }
   {
     if ((s = hip_status(launch_expert_up(ex, st, d2, sizeof d2), "expert gate/up launch"))) return s;
   }
   {
-    if ((s = hip_status(launch_expert_down_combine(ex, st, d3, sizeof d3), "expert down+combine launch")))
+    ExpertLaunch exd = ex;
+    exd.ids_in = nullptr;   // the down launch reads the plan the gate/up launch stored
+    if ((s = hip_status(launch_expert_down_combine(exd, st, d3, sizeof d3), "expert down+combine launch")))
       return s;
   }
   char desc[480];

@@ -59,7 +59,7 @@ constexpr int kUpAllMfmaTasks = 256;   // one 64-row task per compute unit
 constexpr int kUpPairsValu = 2;
 
 template <typename T, int PATHS>
-__global__ __launch_bounds__(kUpWaves * 64, 2) void expert_up_kernel(ExpertLaunch a) {
+__global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void expert_up_kernel(ExpertLaunch a) {
   constexpr int PPT = kUpPairsValu;
   __shared__ int32_t s_plan[kMaxPlanWords];
   __shared__ float s_red[PPT * 2 * kPartStride];
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kUpWaves * 64, 2) void expert_up_kernel(ExpertLaunc
   } else {
     __shared__ __align__(16) unsigned char s_x[MfmaX<4, kUpMfmaChunks>::kLdsBytes];
     __shared__ int s_tstart[kMaxE + 2];
-    const PlanView p = stage_plan(a, s_plan);
+    static_assert(sizeof(s_x) >= kPlanFromIdsBytes, "plan scratch fits the activation buffer");
+    const PlanView p = a.ids_in ? plan_from_ids(a, s_plan, s_x) : stage_plan(a, s_plan);
     const int ne = p.n + (tiles_s > 0 ? 1 : 0);   // routed entries, then the shared one
     const int tiles_m = (a.I + kUpPairsMfma - 1) / kUpPairsMfma;
     const int tiles_ms = (a.Is + kUpPairsMfma - 1) / kUpPairsMfma;

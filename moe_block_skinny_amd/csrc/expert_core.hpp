@@ -62,6 +62,23 @@ __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s
   return plan_view(a, s_plan);
 }
 
+// The plan built in this workgroup's LDS from the ids [B][k] stored by the
+// router's finish launch (an earlier launch); the last workgroup of the grid
+// also stores it (plan_out) for the down launch.  scratch: LDS free until
+// the call returns, at least kPlanFromIdsBytes.  Ends with a barrier.
+constexpr int kPlanFromIdsBytes = kMaxB * kMaxK * 4 + (int)sizeof(PlanScratch);
+__device__ __forceinline__ PlanView plan_from_ids(const ExpertLaunch& a, int32_t* s_plan, unsigned char* scratch) {
+  const int nslot = a.B * a.k;
+  int32_t* s_ids = reinterpret_cast<int32_t*>(scratch);
+  PlanScratch& ps = *reinterpret_cast<PlanScratch*>(scratch + kMaxB * kMaxK * 4);
+  for (int i = threadIdx.x; i < nslot; i += blockDim.x) s_ids[i] = a.ids_in[i];
+  __syncthreads();
+  const bool writer = blockIdx.x == gridDim.x - 1;
+  plan_block(s_ids, nslot, a.k, a.E, s_plan, writer ? a.plan_out : nullptr, ps);
+  __syncthreads();
+  return plan_view(a, s_plan);
+}
+
 // Routing inside the gate/up launch (B*k <= 64): the workgroup selects the
 // top-k of all B tokens from the router's logits [B][E] (bias included) and
 // builds the plan in LDS -- the same functions, hence the same bits, as the
@@ -227,11 +244,14 @@ __host__ __device__ __forceinline__ int expert_paths(int bf16, int force, int B)
 // barrier; with NH = 1 a wave works alone.  Waves whose pair is past I still
 // reach the barrier.
 constexpr int kPartStride = 8;
-template <typename T, int MB, int NH>
+// U1: chunks per lane in flight at one token (7, all of a 7168-wide half row
+// at once, measured slower at batch 1 than 4).  The number in flight does not
+// change any lane's order of accumulation.
+template <typename T, int MB, int NH, int U1>
 __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int i,
                                         int half, int ps, float* s_part) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int U = MB <= 1 ? 8 / NH : (MB <= 2 ? 4 : (MB <= 4 ? 2 : 1));
+  constexpr int U = MB <= 1 ? U1 : (MB <= 2 ? 4 : (MB <= 4 ? 2 : 1));
   const int lane = threadIdx.x & 63;
   const bool live = i < v.I;
   const T* W13 = reinterpret_cast<const T*>(v.W13);
@@ -281,13 +301,13 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
   }
 }
 
-template <typename T, int NH>
+template <typename T, int NH, int U1 = 8 / NH>
 __device__ __forceinline__ void up_valu_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
                                                  int i, int half, int ps, float* s_part) {
-  if (v.m <= 1) up_valu<T, 1, NH>(a, slots, v, i, half, ps, s_part);
-  else if (v.m <= 2) up_valu<T, 2, NH>(a, slots, v, i, half, ps, s_part);
-  else if (v.m <= 4) up_valu<T, 4, NH>(a, slots, v, i, half, ps, s_part);
-  else up_valu<T, 8, NH>(a, slots, v, i, half, ps, s_part);
+  if (v.m <= 1) up_valu<T, 1, NH, U1>(a, slots, v, i, half, ps, s_part);
+  else if (v.m <= 2) up_valu<T, 2, NH, U1>(a, slots, v, i, half, ps, s_part);
+  else if (v.m <= 4) up_valu<T, 4, NH, U1>(a, slots, v, i, half, ps, s_part);
+  else up_valu<T, 8, NH, U1>(a, slots, v, i, half, ps, s_part);
 }
 
 // Pairs p0 .. p0+31 of entry v (m > 8 tokens) over all of d with the four

@@ -39,6 +39,9 @@ struct ExpertLaunch {
   int32_t* ids_out;
   float* w_out;
   int32_t* plan_out;
+  // gate/up launch after a router finish that stored only ids [B][k]: every
+  // workgroup builds the plan from them; the last also stores it (plan_out)
+  const int32_t* ids_in;
   int down_rows;            // rows per workgroup of the prefetching down+combine
 };
 
@@ -81,8 +84,11 @@ struct SkinnyLaunch {
   float* part;
   uint32_t* rg_counter;
   // router on the MFMA shape with its finish launch: every K slice stores
-  // its partial sums and the finish launch adds them (defer = 1)
+  // its partial sums and the finish launch adds them (defer = 1); with
+  // plan_by_consumer the finish stores ids and weights only and the gate/up
+  // launch builds the plan from the ids
   int defer;
+  int plan_by_consumer;
 };
 
 // The whole block in one launch (fused kernel, small batch on the vector

@@ -194,4 +194,84 @@ __device__ __forceinline__ void plan_wave(const int32_t* ids, int nslot, int E, 
   }
 }
 
+// LDS scratch of plan_block.
+struct PlanScratch {
+  unsigned long long mask[kMaxE];   // bit t: token t chose expert e
+  int cnt[kMaxE];                   // first plan slot of expert e
+  int act[kMaxE];                   // rank of expert e among the active ones
+  int incl[kMaxE];
+  int wtot[kMaxE / 64];
+  int n;
+  int sc[128];                      // plan_wave's scratch
+};
+
+// The routing plan of nslot = B*k slots (slot s = t*k + j chose expert
+// ids[s], ids in LDS) with the whole workgroup, into P and, when non-null,
+// P2 (same layout as plan_wave; either may be LDS or global memory).  Up to
+// 64 slots one wave sorts them (plan_wave); beyond, per-expert token masks
+// and a scan over experts.  Ends after the last write, without a barrier.
+__device__ __forceinline__ void plan_block(const int32_t* ids, int nslot, int k, int E, int32_t* P, int32_t* P2,
+                                           PlanScratch& ps) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (nslot <= 64) {
+    if (wave == 0) plan_wave(ids, nslot, E, ps.sc, P, P2);
+    return;
+  }
+  for (int e = tid; e < E; e += blockDim.x) ps.mask[e] = 0ull;
+  __syncthreads();
+  // bit t of mask[e] is set when token t selected expert e (B <= 64)
+  for (int s = tid; s < nslot; s += blockDim.x) atomicOr(&ps.mask[ids[s]], 1ull << (s / k));
+  __syncthreads();
+  // exclusive prefix sums over experts of slot counts and of "is active",
+  // packed in one int (counts <= 1024 in the low half, actives <= 512 in
+  // the high half): a DPP scan per 64-expert group (waves take groups in
+  // turn, so any workgroup size works), group totals through LDS.
+  const int nwv = (E + 63) >> 6, nw = blockDim.x >> 6;
+  for (int grp = wave; grp < nwv; grp += nw) {
+    const int e = grp * 64 + lane;
+    const int c = e < E ? __popcll(ps.mask[e]) : 0;
+    const int packed = c | ((c > 0 ? 1 : 0) << 16);
+    const int incl = wave_incl_scan(packed);
+    ps.incl[e] = incl - packed;   // exclusive within the group
+    if (lane == 63) ps.wtot[grp] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int grp = e >> 6;
+    int base = 0;
+    for (int g = 0; g < grp; ++g) base += ps.wtot[g];
+    const int ex = base + ps.incl[e];
+    ps.cnt[e] = ex & 0xffff;
+    ps.act[e] = ex >> 16;
+  }
+  if (tid == 0) {
+    int tot = 0;
+    for (int g = 0; g < nwv; ++g) tot += ps.wtot[g];
+    ps.n = tot >> 16;
+  }
+  __syncthreads();
+  const int n = ps.n;
+  const int maxa = nslot < E ? nslot : E;
+  for (int q = 0; q < 2; ++q) {
+    int32_t* D = q ? P2 : P;
+    if (!D) continue;
+    int32_t* active = D + 1;
+    int32_t* offs = D + 1 + maxa;
+    int32_t* slots = D + 2 + 2 * maxa;
+    if (tid == 0) D[0] = n;
+    for (int e = tid; e < E; e += blockDim.x)
+      if (ps.mask[e]) {
+        active[ps.act[e]] = e;
+        offs[ps.act[e]] = ps.cnt[e];
+      }
+    for (int i = n + tid; i < maxa; i += blockDim.x) active[i] = -1;
+    for (int i = n + tid; i <= maxa; i += blockDim.x) offs[i] = nslot;
+    for (int s = tid; s < nslot; s += blockDim.x) {
+      const int e = ids[s], t = s / k;
+      const unsigned long long below = (t == 0) ? 0ull : (ps.mask[e] & ((1ull << t) - 1ull));
+      slots[ps.cnt[e] + __popcll(below)] = s;
+    }
+  }
+}
+
 }  // namespace moe

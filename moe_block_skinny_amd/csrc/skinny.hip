@@ -70,69 +70,10 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
 }
 
 // The routing plan of all M*k slots from their expert ids (s_ids, LDS), by
-// the whole workgroup; sc: 128 ints of LDS scratch.
-__device__ __forceinline__ void route_plan(const SkinnyLaunch& a, const int32_t* s_ids, int* sc) {
-  __shared__ unsigned long long s_mask[kMaxE];
-  __shared__ int s_cnt[kMaxE];
-  __shared__ int s_act[kMaxE];
-  __shared__ int s_n;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int M = a.M, E = a.N, k = a.k, nslot = M * k;
-  (void)M;
-  if (nslot <= 64) {  // one wave sorts the slots
-    if (wave == 0) plan_wave(s_ids, nslot, E, sc, a.plan, nullptr);
-    return;
-  }
-  for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
-  __syncthreads();
-  // bit t of s_mask[e] is set when token t selected expert e (B <= 64)
-  for (int s = tid; s < nslot; s += blockDim.x) atomicOr(&s_mask[s_ids[s]], 1ull << (s / k));
-  __syncthreads();
-  // exclusive prefix sums over experts of slot counts and of "is active",
-  // packed in one int (counts <= 1024 in the low half, actives <= 512 in
-  // the high half): a DPP scan per 64-expert group (waves take groups in
-  // turn, so any workgroup size works), group totals through LDS.
-  __shared__ int s_wtot[kMaxE / 64];
-  __shared__ int s_incl[kMaxE];
-  const int nwv = (E + 63) >> 6, nw = blockDim.x >> 6;
-  for (int grp = wave; grp < nwv; grp += nw) {
-    const int e = grp * 64 + lane;
-    const int c = e < E ? __popcll(s_mask[e]) : 0;
-    const int packed = c | ((c > 0 ? 1 : 0) << 16);
-    const int incl = wave_incl_scan(packed);
-    s_incl[e] = incl - packed;   // exclusive within the group
-    if (lane == 63) s_wtot[grp] = incl;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    const int grp = e >> 6;
-    int base = 0;
-    for (int g = 0; g < grp; ++g) base += s_wtot[g];
-    const int ex = base + s_incl[e];
-    s_cnt[e] = ex & 0xffff;
-    s_act[e] = ex >> 16;
-  }
-  if (tid == 0) {
-    int tot = 0;
-    for (int g = 0; g < nwv; ++g) tot += s_wtot[g];
-    s_n = tot >> 16;
-  }
-  __syncthreads();
-  const int n = s_n;
-  const int maxa = nslot < E ? nslot : E;
-  int32_t* active = a.plan + 1;
-  int32_t* offs = a.plan + 1 + maxa;
-  int32_t* slots = a.plan + 2 + 2 * maxa;
-  if (tid == 0) a.plan[0] = n;
-  for (int e = tid; e < E; e += blockDim.x)
-    if (s_mask[e]) { active[s_act[e]] = e; offs[s_act[e]] = s_cnt[e]; }
-  for (int i = n + tid; i < maxa; i += blockDim.x) active[i] = -1;
-  for (int i = n + tid; i <= maxa; i += blockDim.x) offs[i] = nslot;
-  for (int s = tid; s < nslot; s += blockDim.x) {
-    int e = s_ids[s], t = s / k;
-    unsigned long long below = (t == 0) ? 0ull : (s_mask[e] & ((1ull << t) - 1ull));
-    slots[s_cnt[e] + __popcll(below)] = s;
-  }
+// the whole workgroup, into a.plan.
+__device__ __forceinline__ void route_plan(const SkinnyLaunch& a, const int32_t* s_ids) {
+  __shared__ PlanScratch s_ps;
+  plan_block(s_ids, a.M * a.k, a.k, a.N, a.plan, nullptr, s_ps);
 }
 
 // Top-k of every token and the plan, by one workgroup.  NTK: waves that
@@ -144,7 +85,7 @@ __device__ __forceinline__ void route_finish(const SkinnyLaunch& a) {
   __shared__ TopkScratch s_tk[NTK];
   topk_tokens<NTK>(a, s_tk, s_ids, s_w);
   __syncthreads();
-  route_plan(a, s_ids, reinterpret_cast<int*>(s_tk));
+  route_plan(a, s_ids);
 }
 
 // Router tail: every router workgroup arrives once; the last runs the finish.
@@ -156,72 +97,80 @@ __device__ __forceinline__ void router_tail(const SkinnyLaunch& a) {
 }
 
 // The finish as a launch of its own, after the MFMA router product, whose
-// workgroups store the partial sums of their K slices: one wave per token
-// adds its token's partials in slice order (the same order in every run),
-// adds the bias, selects the top-k and stores ids and weights
-// (device-coherent) and arrives; the last workgroup to arrive reads every
-// token's ids and builds the plan.  The partials of up to kFinishSlices
-// slices are requested at once (16-byte loads, 4 experts per lane), so a
-// token costs one or two memory round trips however many slices there are.
+// workgroups store the partial sums of their K slices: one workgroup per
+// token; its four waves each add a quarter of the slices (all of a wave's
+// partials requested at once, 16-byte loads, 4 experts per lane), wave 0 adds
+// the four quarters in wave order (the same order in every run), adds the
+// bias, selects the top-k and stores ids and weights (device-coherent).
+// Unless the gate/up launch builds the plan, every workgroup then arrives
+// and the last one reads every token's ids and builds the plan.
 constexpr int kFinishWaves = 4;
-constexpr int kFinishSlices = 16;
+constexpr int kFinishSlices = 8;   // partials per wave requested together
 __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyLaunch a) {
-  __shared__ TopkScratch s_tk[kFinishWaves];
+  __shared__ TopkScratch s_tk[1];
   __shared__ int32_t s_ids[kMaxB * kMaxK];
   __shared__ float s_w[kMaxB * kMaxK];
   __shared__ __align__(16) float s_lg[kFinishWaves][kMaxE];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kFinishWaves + wave;
+  const int t = blockIdx.x;
   const int E = a.N, k = a.k;
-  if (t < a.M) {
-    float lv[kNI];
-    if ((E & 3) == 0) {
-      // lane l sums experts 4l .. 4l+3 and 256 + 4l .. +3
-      constexpr int NV = kMaxE / 256;
-      const int nv4 = E >> 2;
-      f32x4 sum[NV];
+  float lv[kNI];
+  if ((E & 3) == 0) {
+    // wave w: slices [q0, q1); lane l: experts 4l .. 4l+3 and 256 + 4l .. +3
+    constexpr int NV = kMaxE / 256;
+    const int per = (a.ks_n + kFinishWaves - 1) / kFinishWaves;
+    const int q0 = wave * per, q1 = q0 + per < a.ks_n ? q0 + per : a.ks_n;
+    const int nv4 = E >> 2;
+    f32x4 sum[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int q0 = 0; q0 < a.ks_n; q0 += kFinishSlices) {
-        f32x4 pv[kFinishSlices][NV];
+    for (int v = 0; v < NV; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = q0; qb < q1; qb += kFinishSlices) {
+      f32x4 pv[kFinishSlices][NV];
 #pragma unroll
-        for (int q = 0; q < kFinishSlices; ++q) {
-          const int qc = q0 + q < a.ks_n ? q0 + q : a.ks_n - 1;
-          const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * E);
+      for (int q = 0; q < kFinishSlices; ++q) {
+        const int qc = qb + q < q1 ? qb + q : q1 - 1;
+        const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * E);
 #pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            const int j = lane + 64 * v;
-            pv[q][v] = row[j < nv4 ? j : nv4 - 1];
-          }
+        for (int v = 0; v < NV; ++v) {
+          const int j = lane + 64 * v;
+          pv[q][v] = row[j < nv4 ? j : nv4 - 1];
         }
-#pragma unroll
-        for (int q = 0; q < kFinishSlices; ++q)
-#pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (q0 + q < a.ks_n) sum[v] += pv[q][v];
       }
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int j = lane + 64 * v;
-        if (j < nv4) *reinterpret_cast<f32x4*>(&s_lg[wave][4 * j]) = sum[v];
-      }
-      wave_lds_sync();
+      for (int q = 0; q < kFinishSlices; ++q)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (qb + q < q1) sum[v] += pv[q][v];
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int j = lane + 64 * v;
+      if (j < nv4) *reinterpret_cast<f32x4*>(&s_lg[wave][4 * j]) = sum[v];
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
       for (int i = 0; i < kNI; ++i) {
         const int e = lane + 64 * i;
-        lv[i] = s_lg[wave][e < E ? e : E - 1];
+        const int ec = e < E ? e : E - 1;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFinishWaves; ++w) v += s_lg[w][ec];
+        lv[i] = v;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kNI; ++i) lv[i] = 0.f;
-      for (int q = 0; q < a.ks_n; ++q)
-#pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-          const int e = lane + 64 * i;
-          lv[i] += a.part[((size_t)q * a.M + t) * E + (e < E ? e : E - 1)];
-        }
     }
+  } else if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) lv[i] = 0.f;
+    for (int q = 0; q < a.ks_n; ++q)
+#pragma unroll
+      for (int i = 0; i < kNI; ++i) {
+        const int e = lane + 64 * i;
+        lv[i] += a.part[((size_t)q * a.M + t) * E + (e < E ? e : E - 1)];
+      }
+  }
+  if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int e = lane + 64 * i;
@@ -231,9 +180,10 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
         if (a.logits_out) a.logits_out[(size_t)t * E + e] = lv[i];
       }
     }
-    topk_wave(lv, E, k, s_tk[wave], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
+    topk_wave(lv, E, k, s_tk[0], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
               a.topk_w + (size_t)t * k);
   }
+  if (a.plan_by_consumer) return;   // the gate/up launch builds the plan from the ids
   if (!arrive_last(a.done_counter, gridDim.x, &s_last)) return;
   {
     // every token's ids, all requested before any is stored
@@ -251,7 +201,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
     }
   }
   __syncthreads();
-  route_plan(a, s_ids, reinterpret_cast<int*>(s_tk));
+  route_plan(a, s_ids);
 }
 
 // ---- vector-ALU kernels (gemv / splitk) ----------------------------------
@@ -527,7 +477,7 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
       default: go(skinny_mfma_kernel<4, true>, skinny_mfma_kernel<4, false>); break;
     }
     if (split) {
-      const dim3 fg((unsigned)((a.M + kFinishWaves - 1) / kFinishWaves));
+      const dim3 fg((unsigned)a.M);   // one workgroup per token
       if (prof) hipExtLaunchKernelGGL(route_finish_kernel, fg, dim3(kFinishWaves * 64), 0, st, nullptr, e1, 0u, a);
       else hipLaunchKernelGGL(route_finish_kernel, fg, dim3(kFinishWaves * 64), 0, st, a);
     }
