@@ -647,15 +647,22 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
     if (ok) token_of(a, slots, v, ti, tok, sr);
     const uint16_t* hh = h_hi(a) + (size_t)(ok ? sr : 0) * a.hld;
     const uint16_t* hl = h_lo(a) + (size_t)(ok ? sr : 0) * a.hld;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     u32x4 hv[JM], lv[JM];
+    // only the lanes of real tokens load (an entry of one token moves one
+    // row of h, not sixteen, through the vector memory path)
+    if (ok) {
 #pragma unroll
-    for (int j = 0; j < JM; ++j) {
-      const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
-      hv[j] = *reinterpret_cast<const u32x4*>(hh + off);
-      lv[j] = *reinterpret_cast<const u32x4*>(hl + off);
+      for (int j = 0; j < JM; ++j) {
+        const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+        hv[j] = *reinterpret_cast<const u32x4*>(hh + off);
+        lv[j] = *reinterpret_cast<const u32x4*>(hl + off);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < JM; ++j) hv[j] = lv[j] = zero;
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
       if (j < J) {
