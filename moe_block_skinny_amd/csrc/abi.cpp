@@ -102,10 +102,22 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // ---- kernel shape of the skinny product --------------------------------------
 
-moe_status_t resolve_skinny(int bf16, int B, int K, int* variant) {
+// Automatic shapes: the small-matrix (gemv) shape at B <= 2, split-K above.
+// The dense product takes the matrix shape from B = 6 (bf16, K % 32 == 0):
+// measured at N = 3072, K = 7168 the split-K shape grows by ~0.9 us per
+// token (11.5 us at B = 4, 15.1 at 8) while the matrix shape stays at
+// ~13.4 us.  The router keeps split-K up to B = 8, where the gate/up launch
+// selects from its logits.
+constexpr int kDenseSplitkMaxB = 5;
+
+moe_status_t resolve_skinny(int bf16, int B, int K, int* variant, bool router = true) {
   const int f = forced();
   int v = f;
-  if (f == MOE_VARIANT_AUTO) v = B <= 2 ? VAR_GEMV : (B <= 8 ? VAR_SPLITK : VAR_MFMA);
+  if (f == MOE_VARIANT_AUTO) {
+    const bool mfma_ok = bf16 && K % 32 == 0;
+    const int splitk_max = (router || !mfma_ok) ? 8 : kDenseSplitkMaxB;
+    v = B <= 2 ? VAR_GEMV : (B <= splitk_max ? VAR_SPLITK : VAR_MFMA);
+  }
   if (v == VAR_GEMV && B > 2) return fail(MOE_EUNSUPPORTED, "gemv shape supports B <= 2 (B=%d)", B);
   if (v == VAR_SPLITK && B > 8) return fail(MOE_EUNSUPPORTED, "splitk shape supports B <= 8 (B=%d)", B);
   if (v == VAR_MFMA && !bf16) return fail(MOE_EUNSUPPORTED, "mfma shape needs bf16 (fp32 supports B <= 8)");
@@ -439,7 +451,7 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   if (K % (dtype == MOE_DT_BF16 ? 8 : 4)) return fail(MOE_EUNSUPPORTED, "K=%d not a multiple of the vector width", K);
   const int bf16 = dtype == MOE_DT_BF16;
   int v;
-  s = resolve_skinny(bf16, B, K, &v);
+  s = resolve_skinny(bf16, B, K, &v, false);
   if (s) return s;
   const SkinnyWs L = skinny_ws(B, N, K, bf16, false);
   if (L.total && !aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");

@@ -417,7 +417,11 @@ int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router
   if (router) return 16;
   const int rows = skinny_rows_per_block(variant, router);
   const int nwg = (N + rows - 1) / rows;
-  int nw = (1536 + nwg - 1) / nwg;
+  // waves per launch: ~12 per CU for the small-matrix shape (two per
+  // workgroup at N = 3072: 9.4 -> 8.9 us at B = 1), ~6 for split-K (more
+  // made it slower: its activation loads already match the weight loads)
+  const int target = variant == VAR_GEMV ? 3072 : 1536;
+  int nw = (target + nwg - 1) / nwg;
   int maxw = (K / (bf16 ? 8 : 4)) / 64;
   if (maxw > 16) maxw = 16;
   if (maxw < 1) maxw = 1;
