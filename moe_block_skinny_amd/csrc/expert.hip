@@ -208,16 +208,21 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
 // (I, Is <= 16 chunks: 8 loads per lane per entry, so the whole grid is
 // resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays
 // within 36 KB at B=64).
+// PAIRED (matrix shape, RT > 16): a.down_rows (17..32) rows per workgroup,
+// 16 waves; each entry goes to a pair of waves, one per 16-row half, so h of
+// an entry crosses from L2 once per pair of row tiles (per 16 rows it was
+// the larger part of the launch's L2 traffic at batch 64).
 template <typename T, int PATHS, int RT, bool PIPE>
-__global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512, PATHS == kPathValu ? 1 : 4)
+__global__ __launch_bounds__((PATHS == kPathValu || RT > 16) ? 1024 : 512, (PATHS == kPathValu || RT > 16) ? 1 : 4)
 void expert_down_combine_kernel(ExpertLaunch a) {
+  constexpr bool PAIRED = !PIPE && RT > 16 && PATHS != kPathValu;
   // PIPE (vector shape, short rows, h fits in LDS): h is staged in LDS with
   // the plan and each wave prefetches its next entry's W2 rows
   // (down_valu_pipe)
   __shared__ int32_t s_plan[kMaxPlanWords];
   __shared__ float s_tw[kMaxB * kMaxK];
   extern __shared__ float s_dyn[];   // s_y [B*k + B][rt], then (PIPE) h [B*k + B][hld]
-  const int rt = PIPE ? a.down_rows : RT;
+  const int rt = (PIPE || PAIRED) ? a.down_rows : RT;
   float* s_y = s_dyn;
   float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
   for (int i = threadIdx.x; i < a.B * a.k; i += blockDim.x) s_tw[i] = a.topk_w[i];
@@ -241,6 +246,14 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   __syncthreads();
   if constexpr (PIPE) {
     down_valu_pipe<T, RT>(a, p, ne, s_order, r0, rt, sink, s_h);
+  } else if constexpr (PAIRED) {
+    const int half = wave & 1, pw = wave >> 1, np = nw >> 1;
+    const int r_end = r0 + rt < a.d ? r0 + rt : a.d;
+    for (int j = 0;; ++j) {
+      const int pos = j * np + ((j & 1) ? np - 1 - pw : pw);
+      if (pos >= ne) break;
+      down_dispatch<T, PATHS, 16>(a, p.slots, expert_view<T>(a, p, s_order[pos]), r0 + 16 * half, sink, r_end);
+    }
   } else {
     for (int j = 0;; ++j) {
       const int pos = j * nw + ((j & 1) ? nw - 1 - wave : wave);
@@ -346,9 +359,16 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, ch
     rt = rt_pipe;
     a.down_rows = rt;
   }
+  // matrix shape: rows split evenly over the compute units in multiples of
+  // 4; above 16 a pair of waves takes each entry (one per 16-row half)
+  const bool paired = !pipe && paths != kPathValu && a.bf16 && rt_pipe > 16 && rt_pipe <= 32;
+  if (paired) {
+    rt = rt_pipe;
+    a.down_rows = rt;
+  }
   const int g = (a.d + rt - 1) / rt;
-  int nw = max_entries(a);
-  const int maxw = paths == kPathValu ? 16 : 8;
+  int nw = max_entries(a) * (paired ? 2 : 1);
+  const int maxw = (paths == kPathValu || paired) ? 16 : 8;
   if (nw > maxw) nw = maxw;
   if (nw < 1) nw = 1;
   const size_t lds = (size_t)(a.B * a.k + a.B) * rt * sizeof(float) + (pipe ? h_bytes : 0);
@@ -362,10 +382,11 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, ch
   // shape was no slower per entry at batch 64 (~6 us against ~7 us for 1-2
   // tokens, ~10-16 us for 3-8 on the vector shape), and the kernel holding
   // both shapes spilled 35 registers to scratch
+  else if (paired) launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 32, false>), grid, block, lds, st, a);
   else launch(K_EXPERT_DOWN, (expert_down_combine_kernel<bf16_t, kPathMfma, 16, false>), grid, block, lds, st, a);
   if (desc)
     snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d%s force=%d", g, rt, nw,
-             pipe ? " prefetch" : "", a.force);
+             pipe ? " prefetch" : (paired ? " paired" : ""), a.force);
   return hipGetLastError();
 }
 

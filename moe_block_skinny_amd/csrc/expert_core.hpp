@@ -624,12 +624,14 @@ __device__ __forceinline__ void order_entries(const ExpertLaunch& a, const PlanV
 
 template <int NT>
 __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int r0,
-                          const YSink& sink) {
+                          const YSink& sink, int r_end) {
   constexpr int JM = kMaxInter / 32;   // K steps of the longest row
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
   const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
-  const bf16_t* wr = W2 + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
+  // rows from r_end on (past d, or another workgroup's tile) re-read the
+  // last row of the range (cached) and are not stored
+  const bf16_t* wr = W2 + (size_t)(r0 + row < r_end ? r0 + row : r_end - 1) * v.I;
   const int J = wave_uniform(v.I / 32);
   // all K steps of the wave's 16 rows requested at once (steps past J
   // re-read the last one), then each token tile's h (bf16 hi and lo planes,
@@ -676,7 +678,7 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 4 * kq + i;
-        if (r < a.d) *sink.at(a, sr, r) = acc[i];
+        if (r < r_end) *sink.at(a, sr, r) = acc[i];
       }
     }
   }
@@ -756,15 +758,16 @@ __device__ __forceinline__ void down_mfma_lds(const ExpertLaunch& a, const int32
 // Rows r0..r0+ROWS-1 of entry v with one wave (the MFMA shape covers 16).
 template <typename T, int PATHS, int ROWS = 16>
 __device__ __forceinline__ void down_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
-                                              int r0, const YSink& sink) {
+                                              int r0, const YSink& sink, int r_end = -1) {
   static_assert(ROWS == 16 || PATHS == kPathValu, "the MFMA down shape covers 16 rows");
+  if (r_end < 0) r_end = a.d;
   if (use_mfma<PATHS>(v.m)) {
     if constexpr (sizeof(T) == 2) {
       const int nt = (v.m + 15) / 16;
-      if (nt <= 1) down_mfma<1>(a, slots, v, r0, sink);
-      else if (nt == 2) down_mfma<2>(a, slots, v, r0, sink);
-      else if (nt == 3) down_mfma<3>(a, slots, v, r0, sink);
-      else down_mfma<4>(a, slots, v, r0, sink);
+      if (nt <= 1) down_mfma<1>(a, slots, v, r0, sink, r_end);
+      else if (nt == 2) down_mfma<2>(a, slots, v, r0, sink, r_end);
+      else if (nt == 3) down_mfma<3>(a, slots, v, r0, sink, r_end);
+      else down_mfma<4>(a, slots, v, r0, sink, r_end);
     }
   } else {
     constexpr int VEC = Elem<T>::VEC;
