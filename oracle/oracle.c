@@ -9,7 +9,9 @@
  * Sources (web pages on the Kimi K3 specialised decode path):
  *   [WRITEUP] "vLLM 如何用智能体辅助优化 Kimi K3 解码性能" -- Chinese
  *             translation of the vLLM write-up.  Part 1 §1 (tuning shapes to
- *             the workload), Part 1 §3 (MoE scheduling: router scores, routed
+ *             the workload), Part 1 §2 (overlapping computation and
+ *             communication: the attention output projection fused with its
+ *             all-reduce and the residual), Part 1 §3 (MoE scheduling: router scores, routed
  *             experts, shared expert), Part 2 §3 (correctness).
  *   [AREX]    "vLLM 宣布 Kimi K3 在 GB300 NVL72 上实现 batch 1 解码 842
  *             tokens/s" -- section "每层从 23 个内核减到 13 个" (MoE schedule).
@@ -31,6 +33,8 @@
  *   - combine: out[t] = sum_j w[t][j] * y[t][j] (ascending expert id)
  *     + y_shared[t].
  *   - dense skinny GEMM: Y[b][n] = sum_c X[b][c] * W[n][c].
+ *   - attention output projection with residual (Part 1 §2, without its
+ *     all-reduce): Y[b][n] = sum_c X[b][c] * W[n][c] + R[b][n].
  *
  * Everything is computed token by token and slot by slot -- never grouped by
  * expert -- in fp64, with bf16 inputs widened exactly.  Inputs must be finite.
@@ -75,6 +79,19 @@ void oracle_skinny_gemm(int dt, int B, int N, int K, const void *X,
     for (int n = 0; n < N; ++n)
       Y[(size_t)b * N + n] =
           dot(X, (size_t)b * K, W, (size_t)n * K, dt, K);
+}
+
+/* Attention output projection with the residual added ([WRITEUP] part 1
+ * §2: the output projection fused with its all-reduce and the following
+ * residual; on one GPU the all-reduce is absent):
+ * Y[b][n] = sum_c X[b][c] W[n][c] + R[b][n]; X [B][K], W [N][K], R [B][N]. */
+void oracle_skinny_gemm_residual(int dt, int B, int N, int K, const void *X,
+                                 const void *W, const void *R, double *Y) {
+  for (int b = 0; b < B; ++b)
+    for (int n = 0; n < N; ++n)
+      Y[(size_t)b * N + n] =
+          dot(X, (size_t)b * K, W, (size_t)n * K, dt, K) +
+          elem(R, dt, (size_t)b * N + n);
 }
 
 /* Router logits: l[t][e] = sum_c x[t][c] Wr[e][c] + bias(t, e).

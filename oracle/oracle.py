@@ -51,6 +51,7 @@ def _load():
             lib.oracle_silu.restype = ctypes.c_double
             lib.oracle_silu.argtypes = [ctypes.c_double]
             lib.oracle_skinny_gemm.argtypes = [I, I, I, I, P, P, P]
+            lib.oracle_skinny_gemm_residual.argtypes = [I, I, I, I, P, P, P, P]
             lib.oracle_router_logits.argtypes = [I, I, I, I, P, P, P, I, P]
             lib.oracle_topk.argtypes = [I, I, P, P, P]
             lib.oracle_plan_words.restype = I
@@ -99,6 +100,17 @@ def skinny_gemm(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     assert W.shape[1] == K and _dt(X) == _dt(W)
     Y = np.empty((B, N), np.float64)
     _load().oracle_skinny_gemm(_dt(X), B, N, K, _p(X), _p(W), _p(Y))
+    return Y
+
+
+def skinny_gemm_residual(X: np.ndarray, W: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """Y[b][n] = sum_c X[b][c] W[n][c] + R[b][n] in fp64 (R of X's dtype)."""
+    X, W, R = _c(X), _c(W), _c(R)
+    B, K = X.shape
+    N = W.shape[0]
+    assert W.shape[1] == K and R.shape == (B, N) and _dt(X) == _dt(W) == _dt(R)
+    Y = np.empty((B, N), np.float64)
+    _load().oracle_skinny_gemm_residual(_dt(X), B, N, K, _p(X), _p(W), _p(R), _p(Y))
     return Y
 
 

@@ -71,6 +71,33 @@ def test_gemm_integer_exact_and_split_k(splits):
     assert np.array_equal(parts, Y)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_gemm_residual_pins(dt):
+    """Output projection with residual: numpy's float64 X W^T + R; a zero
+    residual gives the plain product bit for bit; zero weights give R itself;
+    integer inputs are exact (int64 product plus residual); a residual with
+    rows swapped moves only those rows (R is indexed [b][n], not [n][b])."""
+    rng = np.random.default_rng(11)
+    B, N, K = 4, 37, 96
+    X = rng.standard_normal((B, K)).astype(np.float32)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    R = rng.standard_normal((B, N)).astype(np.float32)
+    if dt == "bf16":
+        X, W, R = synth.to_bf16_bits(X), synth.to_bf16_bits(W), synth.to_bf16_bits(R)
+    Y = orc.skinny_gemm_residual(X, W, R)
+    ref = widen(X) @ widen(W).T + widen(R)
+    bound = 2 * K * 2.0 ** -53 * (np.abs(widen(X)) @ np.abs(widen(W)).T + np.abs(widen(R))) + 1e-300
+    assert np.all(np.abs(Y - ref) <= bound)
+    assert np.array_equal(orc.skinny_gemm_residual(X, W, np.zeros_like(R)), orc.skinny_gemm(X, W))
+    assert np.array_equal(orc.skinny_gemm_residual(X, np.zeros_like(W), R), widen(R))
+    Rs = np.ascontiguousarray(R[::-1])
+    Ys = orc.skinny_gemm_residual(X, W, Rs)
+    assert np.allclose(Ys - orc.skinny_gemm(X, W), widen(Rs), rtol=0, atol=1e-12)
+    Xi, Wi, Ri = rng.integers(-3, 4, (B, K)), rng.integers(-3, 4, (N, K)), rng.integers(-50, 51, (B, N))
+    f = (lambda a: synth.to_bf16_bits(a.astype(np.float32))) if dt == "bf16" else (lambda a: a.astype(np.float32))
+    assert np.array_equal(orc.skinny_gemm_residual(f(Xi), f(Wi), f(Ri)), (Xi @ Wi.T + Ri).astype(np.float64))
+
+
 @pytest.mark.parametrize("bias_mode", ["none", "row", "per_token"])
 def test_router_logits(bias_mode):
     rng = np.random.default_rng(7)
