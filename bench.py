@@ -8,7 +8,8 @@ plan, routed and shared expert gate/up + SwiGLU + down, weighted combine)
 over one batch of synthetic bf16 input, through the C ABI (moe_block).
 Default workload: one TP16 weight shard at batch 1 (d=7168, E=384, top-8,
 I=Is=128).  Other workloads: tp16_b8, tp8_b64, tiny, dense (the attention
-input projection, --batch B).
+input projection, --batch B), oproj (the attention output projection with
+the residual added, --batch B).
 
 Weights are random (seeded torch generator on the GPU) in R rotating full
 sets so that the bytes touched between two uses of a set exceed twice the
@@ -51,8 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="tp16_b1",
-                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "copy"])
-    ap.add_argument("--batch", type=int, default=1, help="dense workload batch")
+                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "oproj", "copy"])
+    ap.add_argument("--batch", type=int, default=1, help="dense / oproj workload batch")
     ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: enough to defeat caches)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-steps", type=int, default=100)
@@ -232,6 +233,47 @@ def run_dense(args, torch, mb, synth):
     return us, ms, "bf16", config, roof, cpu
 
 
+# ---------------------------------------------------------------- oproj
+
+def run_oproj(args, torch, mb, synth):
+    """Attention output projection with the residual added:
+    Y = X . W^T + R, X [B][3072], W [7168][3072], R and Y [B][7168], bf16."""
+    B, N, K = args.batch, synth.OPROJ_N, synth.OPROJ_K
+    wbytes = N * K * 2
+    R_sets = args.rotate or rotations(wbytes, cap_sets=64)
+    sets = []
+    for r in range(R_sets):
+        g = torch.Generator(device="cuda").manual_seed(args.seed * 1000003 + r)
+        sets.append(dict(X=torch.randn((B, K), generator=g, device="cuda", dtype=torch.bfloat16),
+                         W=(torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * K ** -0.5).to(torch.bfloat16),
+                         R=torch.randn((B, N), generator=g, device="cuda", dtype=torch.bfloat16),
+                         Y=torch.empty((B, N), device="cuda", dtype=torch.bfloat16)))
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K))
+
+    def step(i):
+        s = sets[i % R_sets]
+        mb.skinny_gemm_residual(s["X"], s["W"], s["R"], s["Y"], ws)
+
+    ms = timed_loop(step, args, torch)
+    nbytes = wbytes + B * K * 2 + 2 * B * N * 2
+    durs = kernel_times(step, mb.KERNEL_SKINNY, args, torch, mb)
+    achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=stored_traffic("oproj_b%d" % B, "skinny_gemm"),
+                kernel="skinny_valu_kernel / skinny_mfma_kernel",
+                bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
+    us = ms * 1e3
+    config = dict(workload="attention output projection + residual: Y[%d x %d] = X[%d x %d] . W[%d x %d]^T "
+                           "+ R, bf16" % (B, N, B, K, N, K),
+                  B=B, N=N, K=K, rotate=R_sets, algorithmic_bytes=nbytes,
+                  gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                  hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  variant=mb.last_variant())
+    cpu = None if args.no_cpu_baseline else cpu_baseline_oproj(B, args)
+    return us, ms, "bf16", config, roof, cpu
+
+
 # ---------------------------------------------------------------- copy
 
 def run_copy(args, torch):
@@ -355,6 +397,23 @@ def cpu_baseline_dense(B, N, K, args):
                 host_cpus=os.cpu_count())
 
 
+def cpu_baseline_oproj(B, args):
+    from moe_block_skinny_amd import synth
+    from oracle import oracle as orc
+
+    X, W, R = synth.oproj_x(B), synth.oproj_w(), synth.oproj_r(B)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.skinny_gemm_residual(X, W, R)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
+                sample="%d output projections with residual at B=%d, fp64 C oracle, one thread, %.1f s"
+                       % (n, B, el), host_cpus=os.cpu_count())
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -373,6 +432,8 @@ def main():
         us, ms, dtype, config, roof, cpu = run_copy(args, torch)
     elif args.workload == "dense":
         us, ms, dtype, config, roof, cpu = run_dense(args, torch, mb, synth)
+    elif args.workload == "oproj":
+        us, ms, dtype, config, roof, cpu = run_oproj(args, torch, mb, synth)
     else:
         us, ms, dtype, config, roof, cpu = run_moe(args, torch, mb, synth)
     line = dict(metric=METRIC, value=round(us, 3), unit="µs", n_gpus=1, steps=args.steps,

@@ -178,6 +178,19 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
                          int y_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* Attention output projection with the residual added (WRITEUP part 1 §2:
+ * the output projection fused with its all-reduce and the following
+ * residual; on one GPU the all-reduce is absent):
+ *   Y[b][n] = sum_c X[b][c] * W[n][c] + R[b][n], accumulated in fp32, the
+ *   residual added once after the sum, then rounded to y_dtype.
+ *   R [B][N] of dtype, caller-owned device memory, 16-byte aligned; Y may be
+ *   R itself (an in-place residual update: each element is read and
+ *   written by the same thread) but must not otherwise overlap it.  Every
+ *   other argument, the kernel shapes, the workspace and the errors are
+ *   those of skinny_gemm; a null R is MOE_EINVAL. */
+moe_status_t skinny_gemm_residual(int dtype, int B, int N, int K, const void* X, const void* W, const void* R,
+                                  void* Y, int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* Router (WRITEUP part 1 §3; selection and weights are the standard top-k
  * softmax the block's workload definitions name):
  *   logits[t][e] = sum_c X[t][c] * Wr[e][c] + bias(t, e), accumulated in fp32;

@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_workspace_init": (_I, [_P, _Z, _P]),
     "moe_profile_events": (_I, [_I, _P, _P]),
     "skinny_gemm": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _Z, _P]),
+    "skinny_gemm_residual": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "moe_route": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_I, _I, _I, _I, _P, _P, _I, _P, _P]),
@@ -141,6 +142,13 @@ def skinny_gemm(X, W, Y, ws=None, stream=None):
     N = W.shape[0]
     _check(lib.skinny_gemm(_dt(X), B, N, K, _ptr(X), _ptr(W), _ptr(Y), _dt(Y), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def skinny_gemm_residual(X, W, R, Y, ws=None, stream=None):
+    B, K = X.shape
+    N = W.shape[0]
+    _check(lib.skinny_gemm_residual(_dt(X), B, N, K, _ptr(X), _ptr(W), _ptr(R), _ptr(Y), _dt(Y), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def moe_route(X, Wr, k, topk_ids, topk_w, plan, ws, bias=None, bias_ld=0, logits_out=None,

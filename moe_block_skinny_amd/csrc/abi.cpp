@@ -439,8 +439,13 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
                     "workspace fill");
 }
 
-moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
-                         int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// skinny_gemm and skinny_gemm_residual: the product, plus R when non-null.
+moe_status_t run_skinny_gemm(const char* op, int dtype, int B, int N, int K, const void* X, const void* W,
+                             const void* R, void* Y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   moe_status_t s = check_dtype(dtype);
   if (s) return s;
@@ -469,13 +474,30 @@ moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const vo
   a.S = skinny_default_splits(v, bf16, B, N, K, 0);
   a.Y = Y;
   a.y_bf16 = y_dtype == MOE_DT_BF16;
+  a.R = R;
   char desc[160];
   {
     s = hip_status(launch_skinny(a, reinterpret_cast<hipStream_t>(stream), desc, sizeof desc),
                    "skinny_gemm launch");
   }
-  if (!s) record("skinny_gemm", B, desc);
+  if (!s) record(op, B, desc);
   return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t skinny_gemm(int dtype, int B, int N, int K, const void* X, const void* W, void* Y,
+                         int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return run_skinny_gemm("skinny_gemm", dtype, B, N, K, X, W, nullptr, Y, y_dtype, ws, ws_bytes, stream);
+}
+
+moe_status_t skinny_gemm_residual(int dtype, int B, int N, int K, const void* X, const void* W, const void* R,
+                                  void* Y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!aligned(R)) return fail(MOE_EINVAL, "R null or not 16-byte aligned");
+  return run_skinny_gemm("skinny_gemm_residual", dtype, B, N, K, X, W, R, Y, y_dtype, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, const void* Wr,

@@ -59,6 +59,7 @@ struct SkinnyLaunch {
   // store mode
   void* Y;
   int y_bf16;
+  const void* R;            // residual [M][N] of the element type, added to Y (nullable)
   // router mode (router != 0); finish = 0: logits only (no top-k, no plan)
   int router;
   int finish;

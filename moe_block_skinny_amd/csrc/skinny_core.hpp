@@ -21,10 +21,13 @@ __device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n
     if (a.bias) v += a.bias[(size_t)t * a.bias_ld + n];
     st_coherent(&a.logits[(size_t)t * a.N + n], v);   // read by other workgroups of the launch
     if (a.logits_out) a.logits_out[(size_t)t * a.N + n] = v;
-  } else if (a.y_bf16) {
-    reinterpret_cast<bf16_t*>(a.Y)[(size_t)t * a.N + n] = f32_to_bf16(v);
   } else {
-    reinterpret_cast<float*>(a.Y)[(size_t)t * a.N + n] = v;
+    const size_t o = (size_t)t * a.N + n;
+    // the residual is read and the result stored by the same thread, so Y
+    // may be R itself (an in-place residual update)
+    if (a.R) v += a.bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.R)[o]) : reinterpret_cast<const float*>(a.R)[o];
+    if (a.y_bf16) reinterpret_cast<bf16_t*>(a.Y)[o] = f32_to_bf16(v);
+    else reinterpret_cast<float*>(a.Y)[o] = v;
   }
 }
 

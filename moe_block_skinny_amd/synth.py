@@ -31,6 +31,7 @@ import numpy as np
 # stream tags
 _T_X, _T_WR, _T_W13, _T_W2, _T_WS13, _T_WS2, _T_GUMBEL, _T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 _T_DX, _T_DW = 9, 10
+_T_OX, _T_OW, _T_OR = 11, 12, 13
 
 
 @dataclass(frozen=True)
@@ -60,6 +61,10 @@ CONFIGS = {
 DENSE_N = 3072
 DENSE_K = 7168
 DENSE_BATCHES = (1, 2, 4, 8, 16, 32, 64)
+# attention output projection with residual: back from one rank's attention
+# width (taken equal to the input projection's share, 3072) to d = 7168
+OPROJ_N = 7168
+OPROJ_K = 3072
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -171,3 +176,16 @@ def dense_x(B: int, K: int = DENSE_K, seed: int = 0) -> np.ndarray:
 
 def dense_w(N: int = DENSE_N, K: int = DENSE_K, seed: int = 0) -> np.ndarray:
     return to_bf16_bits(_normal(_rng(seed, _T_DW), (N, K), K ** -0.5))
+
+
+def oproj_x(B: int, K: int = OPROJ_K, seed: int = 0) -> np.ndarray:
+    return to_bf16_bits(_normal(_rng(seed, _T_OX, B), (B, K), 1.0))
+
+
+def oproj_w(N: int = OPROJ_N, K: int = OPROJ_K, seed: int = 0) -> np.ndarray:
+    return to_bf16_bits(_normal(_rng(seed, _T_OW), (N, K), K ** -0.5))
+
+
+def oproj_r(B: int, N: int = OPROJ_N, seed: int = 0) -> np.ndarray:
+    """The residual stream entering the output projection: N(0, 1)."""
+    return to_bf16_bits(_normal(_rng(seed, _T_OR, B), (B, N), 1.0))

@@ -84,6 +84,26 @@ def test_skinny_gemm_validation(kw, status):
     assert lib.moe_last_error() != b""
 
 
+def gemm_residual(**kw):
+    a = dict(dt=mb.DT_BF16, B=4, N=64, K=256, X=A, W=A, R=A, Y=A, ydt=mb.DT_BF16, ws=A, wsb=BIG)
+    a.update(kw)
+    return lib.skinny_gemm_residual(a["dt"], a["B"], a["N"], a["K"], a["X"], a["W"], a["R"], a["Y"],
+                                    a["ydt"], a["ws"], a["wsb"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=None), mb.EINVAL),
+    (dict(R=MIS), mb.EINVAL),
+    (dict(dt=7), mb.EINVAL),
+    (dict(X=None), mb.EINVAL),
+    (dict(B=65), mb.EUNSUPPORTED),
+    (dict(K=252), mb.EUNSUPPORTED),
+])
+def test_skinny_gemm_residual_validation(kw, status):
+    assert gemm_residual(**kw) == status
+    assert lib.moe_last_error() != b""
+
+
 def route(**kw):
     a = dict(dt=mb.DT_BF16, B=8, d=7168, E=384, k=8, X=A, Wr=A, bias=None, ld=0, ids=A, w=A,
              plan=A, lo=None, ws=A, wsb=BIG)

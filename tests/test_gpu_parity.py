@@ -93,6 +93,52 @@ def test_skinny_gemm_dense_workload(B):
         assert np.all(err16 <= bound + 2.0 ** -8 * np.abs(ref)), (var, B)
 
 
+@pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma"])
+@pytest.mark.parametrize("K", [3072, 1056])
+def test_skinny_gemm_residual_integer_exact(var, K):
+    """Output projection with residual on small integers: every sum is exact
+    in fp32, so every kernel shape must give X W^T + R bit for bit."""
+    rng = np.random.default_rng(K)
+    N = synth.OPROJ_N
+    Wi = rng.integers(-3, 4, (N, K))
+    W = dev(bf16_of_ints(Wi))
+    for B in SHAPES[var][:4] + ([64] if var in ("auto", "mfma") else []):
+        Xi = rng.integers(-3, 4, (B, K))
+        Ri = rng.integers(-50, 51, (B, N))
+        ref = (Xi @ Wi.T + Ri).astype(np.float64)
+        Y = torch.full((B, N), float("nan"), device="cuda")
+        ws = ws_for(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K)
+        with variant(var):
+            mb.skinny_gemm_residual(dev(bf16_of_ints(Xi)), W, dev(bf16_of_ints(Ri)), Y, ws)
+        torch.cuda.synchronize()
+        say("skinny_gemm_residual integer", var, "B", B, "K", K)
+        assert np.array_equal(host(Y), ref), (var, B)
+
+
+@pytest.mark.parametrize("B", [1, 2, 8, 64])
+def test_skinny_gemm_residual_workload(B):
+    """Output projection workload (N = 7168, K = 3072, bf16) against the
+    oracle; the in-place form (Y is R) gives the same bits."""
+    Xh, Wh, Rh = synth.oproj_x(B), synth.oproj_w(), synth.oproj_r(B)
+    ref = orc.skinny_gemm_residual(Xh, Wh, Rh)
+    bound = fp32_sum_bound(widen(Xh), widen(Wh)) + 2.0 ** -23 * np.abs(widen(Rh))
+    N, K = Wh.shape
+    X, W, R = dev(Xh), dev(Wh), dev(Rh)
+    ws = ws_for(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K)
+    Y32 = torch.empty((B, N), device="cuda")
+    Y16 = torch.empty((B, N), device="cuda", dtype=torch.bfloat16)
+    mb.skinny_gemm_residual(X, W, R, Y32, ws)
+    mb.skinny_gemm_residual(X, W, R, Y16, ws)
+    Rin = R.clone()
+    mb.skinny_gemm_residual(X, W, Rin, Rin, ws)
+    torch.cuda.synchronize()
+    say("skinny_gemm_residual workload B", B, mb.last_variant())
+    err = np.abs(host(Y32) - ref)
+    assert np.all(err <= bound), float(err.max())
+    assert np.all(np.abs(host(Y16) - ref) <= bound + 2.0 ** -8 * np.abs(ref))
+    assert torch.equal(Rin.view(torch.int16), Y16.view(torch.int16))
+
+
 def test_skinny_gemm_workspace_reuse():
     """Back-to-back MFMA products with K slices over ONE workspace, with
     different inputs and batch sizes: every call's partial sums must be read
