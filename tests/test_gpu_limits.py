@@ -1,0 +1,76 @@
+"""The block at the edges of its scope, against the CPU oracle (needs an
+MI355X): the largest routing problem the ABI accepts (B = 64 tokens, E = 512
+experts, top-16: 1024 slots), every expert chosen by every token (k = E),
+top-1, and the smallest batch that takes the matrix shapes (B = 9).  Expert
+ids and the plan bit-exact; the block output within 2^-8 |ref| + 1e-3 rms
+per element (fp32 internals plus one bf16 rounding).  The stated bar
+max|err| <= 2e-2 * rms is not asserted here: these synthetic outputs reach
+six times their rms, where rounding the exact result to bf16 alone moves it
+by up to 2^-8 * 6 rms = 0.024 rms (the max-scope case measures 0.0225 for
+the rounded oracle, and the same for the GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from moe_block_skinny_amd import binding as mb
+from moe_block_skinny_amd import synth
+from tests import inputs
+from tests.gpu_util import dev, host, rms, say
+
+pytestmark = pytest.mark.gpu
+
+LIMITS = {
+    "max_scope": synth.MoEConfig("max_scope", 64, 1024, 512, 16, 32, 32, "bf16", "plain"),
+    "all_experts": synth.MoEConfig("all_experts", 5, 1024, 8, 8, 64, 0, "bf16", "plain"),
+    "top1": synth.MoEConfig("top1", 64, 1024, 64, 1, 64, 64, "bf16", "zipf"),
+    "first_matrix_b9": synth.MoEConfig("first_matrix_b9", 9, 2048, 32, 4, 64, 64, "bf16", "gumbel"),
+}
+
+
+def weights(c):
+    cfg = c.cfg
+    W13 = torch.full((cfg.E, 2 * cfg.I, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.full((cfg.E, cfg.d, cfg.I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for e in c.touched:
+        W13[e] = dev(c.W13[e])
+        W2[e] = dev(c.W2[e])
+    Ws13 = None if c.Ws13 is None else dev(c.Ws13)
+    Ws2 = None if c.Ws2 is None else dev(c.Ws2)
+    return W13, W2, Ws13, Ws2
+
+
+@pytest.mark.parametrize("name", sorted(LIMITS))
+def test_block_and_route_at_scope_limits(name):
+    c = inputs.Case(LIMITS[name], seed=7)
+    cfg = c.cfg
+    say("limits", name, "distinct experts", len(c.touched), "redraws", c.redraws)
+    W13, W2, Ws13, Ws2 = weights(c)
+    bias = None if c.bias is None else dev(c.bias)
+    X, Wr = dev(c.X), dev(c.Wr)
+    # the block
+    out = torch.full((cfg.B, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                         I=cfg.I, Is=cfg.Is))
+    mb.moe_block(X, Wr, cfg.k, W13, W2, out, ws, Ws13, Ws2, bias, c.bias_ld, ids, w)
+    torch.cuda.synchronize()
+    say("  variant", mb.last_variant())
+    ref = c.oracle_block()["out"]
+    g = host(out)
+    assert np.array_equal(host(ids), c.ids)
+    assert np.max(np.abs(host(w) - c.w)) <= 1e-5
+    scale = rms(ref)
+    err = np.abs(g - ref)
+    say("  max|err|/rms", float(err.max() / scale))
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
+    # the router alone: ids, weights and the plan it builds itself
+    rids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
+    rw = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
+    plan = torch.full((mb.plan_words(cfg.B, cfg.k, cfg.E),), -7, dtype=torch.int32, device="cuda")
+    wsr = mb.workspace(mb.workspace_bytes(mb.OP_ROUTE, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k))
+    mb.moe_route(X, Wr, cfg.k, rids, rw, plan, wsr, bias=bias, bias_ld=c.bias_ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rids), c.ids)
+    assert np.array_equal(host(plan), c.plan)
+    assert np.max(np.abs(host(rw) - c.w)) <= 1e-5
