@@ -633,47 +633,39 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   // last row of the range (cached) and are not stored
   const bf16_t* wr = W2 + (size_t)(r0 + row < r_end ? r0 + row : r_end - 1) * v.I;
   const int J = wave_uniform(v.I / 32);
-  // all K steps of the wave's 16 rows requested at once (steps past J
-  // re-read the last one), then each token tile's h (bf16 hi and lo planes,
-  // split by the producer): one memory round trip per tile
-  u32x4 wv[JM];
-#pragma unroll
-  for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
-  // one token tile's h in registers at a time (two overlapped tiles took
-  // 64 more registers than the 4-waves-per-SIMD budget and spilled)
-#pragma unroll 1
-  for (int nt = 0; nt < NT; ++nt) {
-    const int ti = nt * 16 + row;
-    int tok = 0, sr = 0;
-    const bool ok = ti < v.m;
-    if (ok) token_of(a, slots, v, ti, tok, sr);
-    const uint16_t* hh = h_hi(a) + (size_t)(ok ? sr : 0) * a.hld;
-    const uint16_t* hl = h_lo(a) + (size_t)(ok ? sr : 0) * a.hld;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 hv[JM], lv[JM];
-    // only the lanes of real tokens load (an entry of one token moves one
-    // row of h, not sixteen, through the vector memory path)
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  constexpr int JH = JM / 2;
+  // h of one token tile in two halves of K: 32 registers of h at a time keep
+  // the wave within its register budget.  Only the lanes of real tokens load
+  // (an entry of one token moves one row of h, not sixteen, through the
+  // vector memory path); the others neither load nor zero their registers
+  // (the products take zero for them): writing a register that a load might
+  // still own makes the compiler wait for every load in flight.
+  auto load_half = [&](bool ok, const uint16_t* hh, const uint16_t* hl, int half, u32x4 (&hv)[JH], u32x4 (&lv)[JH]) {
     if (ok) {
 #pragma unroll
-      for (int j = 0; j < JM; ++j) {
+      for (int jj = 0; jj < JH; ++jj) {
+        const int j = half * JH + jj;
         const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
-        hv[j] = *reinterpret_cast<const u32x4*>(hh + off);
-        lv[j] = *reinterpret_cast<const u32x4*>(hl + off);
+        hv[jj] = *reinterpret_cast<const u32x4*>(hh + off);
+        lv[jj] = *reinterpret_cast<const u32x4*>(hl + off);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < JM; ++j) hv[j] = lv[j] = zero;
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  };
+  auto mul_half = [&](bool ok, int half, const u32x4 (&wv)[JM], const u32x4 (&hv)[JH], const u32x4 (&lv)[JH],
+                      f32x4& acc) {
 #pragma unroll
-    for (int j = 0; j < JM; ++j) {
+    for (int jj = 0; jj < JH; ++jj) {
+      const int j = half * JH + jj;
       if (j < J) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
-                                                      __builtin_bit_cast(bf16x8, ok ? hv[j] : zero), acc, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8, ok ? hv[jj] : zero), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
-                                                      __builtin_bit_cast(bf16x8, ok ? lv[j] : zero), acc, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8, ok ? lv[jj] : zero), acc, 0, 0, 0);
       }
     }
+  };
+  auto store = [&](bool ok, int sr, const f32x4& acc) {
     if (ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -681,6 +673,47 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
         if (r < r_end) *sink.at(a, sr, r) = acc[i];
       }
     }
+  };
+  // token tile 0: the first half of its h is requested before the weights
+  // (all K steps of the wave's 16 rows at once, steps past J re-reading the
+  // last one), so waiting for the weights never delays the request for h
+  int tok0 = 0, sr0 = 0;
+  const bool ok0 = row < v.m;
+  if (ok0) token_of(a, slots, v, row, tok0, sr0);
+  const uint16_t* hh0 = h_hi(a) + (size_t)(ok0 ? sr0 : 0) * a.hld;
+  const uint16_t* hl0 = h_lo(a) + (size_t)(ok0 ? sr0 : 0) * a.hld;
+  u32x4 wv[JM];
+  {
+    u32x4 hv[JH], lv[JH];
+    load_half(ok0, hh0, hl0, 0, hv, lv);
+#pragma unroll
+    for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mul_half(ok0, 0, wv, hv, lv, acc);
+    if (JH < J) {
+      load_half(ok0, hh0, hl0, 1, hv, lv);
+      mul_half(ok0, 1, wv, hv, lv, acc);
+    }
+    store(ok0, sr0, acc);
+  }
+  // the other token tiles, one at a time
+#pragma unroll 1
+  for (int nt = 1; nt < NT; ++nt) {
+    const int ti = nt * 16 + row;
+    int tok = 0, sr = 0;
+    const bool ok = ti < v.m;
+    if (ok) token_of(a, slots, v, ti, tok, sr);
+    const uint16_t* hh = h_hi(a) + (size_t)(ok ? sr : 0) * a.hld;
+    const uint16_t* hl = h_lo(a) + (size_t)(ok ? sr : 0) * a.hld;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half * JH >= J) break;
+      u32x4 hv[JH], lv[JH];
+      load_half(ok, hh, hl, half, hv, lv);
+      mul_half(ok, half, wv, hv, lv, acc);
+    }
+    store(ok, sr, acc);
   }
 }
 
