@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused"],
                     help="moe_block schedule: one fused launch where it applies, or three launches")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs (one captured block per weight set) instead of plain "
+                         "launches; every replay is first checked against the plain launch's bits")
     return ap.parse_args()
 
 
@@ -118,7 +121,10 @@ def run_moe(args, torch, mb, synth):
                      s["bias"], s["bias_ld"], topk_ids=s["ids"])
 
     mb.set_block_schedule(args.schedule)
-    ms = timed_loop(step, args, torch)
+    if args.graph:
+        ms = graph_loop(step, R, args, torch, [s["out"] for s in sets])
+    else:
+        ms = timed_loop(step, args, torch)
     fused = "fused" in mb.last_variant()
     route_in_up = "top-k/plan" in mb.last_variant()
     # algorithmic bytes per set: every selected expert's weights once, the
@@ -160,6 +166,7 @@ def run_moe(args, torch, mb, synth):
                   distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
                   gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                   kernels=per_kernel,
+                  launch="graph replay" if args.graph else "plain launches",
                   variant=mb.last_variant())
     cpu = None if args.no_cpu_baseline else cpu_baseline_moe(cfg, args)
     return us, ms, cfg.dtype, config, roof, cpu
@@ -329,6 +336,41 @@ def timed_loop(step, args, torch):
     e0.record()
     for i in range(args.steps):
         step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
+def graph_loop(step, R, args, torch, outs):
+    """Per-step time of graph replays: one graph per weight set, each holding
+    one step captured on a side stream.  Before timing, every graph is
+    replayed three times with plain launches of the other sets in between,
+    and each replay must reproduce the plain launch's output bits."""
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for r in range(R):
+            outs[r].fill_(0)
+            graphs[r].replay()
+            step(r + 1)               # plain launches between the replays
+            torch.cuda.synchronize()
+            if not torch.equal(outs[r].view(torch.int16), ref[r].view(torch.int16)):
+                raise RuntimeError("graph replay %d of set %d differs from the plain launch" % (rep, r))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / args.steps
