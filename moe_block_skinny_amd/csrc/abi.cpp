@@ -193,7 +193,7 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 // the fused barrier lines in the header, then h, ids, weights and plan.
 struct BlockWs {
   SkinnyWs route;
-  size_t route_off, ffn_h, ids, w, plan, sync, total;
+  size_t route_off, ffn_h, ids, w, plan, sync, up_part, total;
   int hld;
 };
 
@@ -212,6 +212,14 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   o = up(o + (size_t)B * k * 4);
   b.plan = o;
   o = up(o + (size_t)moe_plan_words(B, k, E) * 4);
+  // the gate/up launch's K-slice partial sums (matrix shape, B > 8): at most
+  // one task per workgroup of its grid (512) when tiles are cut, so at most
+  // 256 cut tiles of 2 slices x 4 token tiles x 4 KB
+  b.up_part = 0;
+  if (bf16 && B > 8) {
+    b.up_part = o;
+    o = up(o + (size_t)256 * 2 * 4 * 4096);
+  }
   b.total = o;
   return b;
 }
@@ -608,6 +616,10 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   ex.topk_w = tw;
   ex.out = out;
   ex.out_bf16 = bf16;
+  if (L.up_part) {
+    ex.up_part = reinterpret_cast<float*>(w + L.up_part);
+    ex.up_counter = reinterpret_cast<uint32_t*>(w + 32 * 4);   // the header's arrival words
+  }
   // Two schedules.  Small batch on the vector shape (B*k <= 64): the router
   // launch only scores; the gate/up launch selects the top-k and builds the
   // plan in every workgroup (no cross-workgroup handshake) and runs the

@@ -112,26 +112,65 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     // vector tasks are needed to spread the entries over the compute units.
     const bool all_mfma = PATHS == kPathBoth && p.n * tiles_m >= kUpAllMfmaTasks;
     auto mfma_entry = [&](int m) { return all_mfma || use_mfma<PATHS>(m); };
-    // s_tstart[e]: first task of entry e (one wave, 64 entries per pass)
+    // Tiles of entries with more than 16 tokens take longest (their
+    // activations are staged in several 16-token tiles per K step): when the
+    // grid still gives every task a workgroup of its own, each such tile is
+    // cut in two K slices on two workgroups, the later of which adds the
+    // halves and applies SwiGLU.  s_tstart[e]: first task of entry e;
+    // s_pbase[e] / s_cbase[e]: its first partial block (4 KB units) and tile
+    // counter (split entries); one wave, 64 entries per pass.
+    constexpr int kSplit = 2;
+    __shared__ unsigned short s_pbase[kMaxE + 2];
+    __shared__ unsigned short s_cbase[kMaxE + 2];
+    __shared__ int s_use_split;
+    auto entry_tasks = [&](int e, bool split, int& pn, int& cn) {
+      const bool sh = e >= p.n;
+      const int m = sh ? a.B : p.offs[e + 1] - p.offs[e];
+      pn = cn = 0;
+      if (!mfma_entry(m)) return sh ? tiles_s : tiles_r;
+      const int tiles = sh ? tiles_ms : tiles_m;
+      if (split && m > 16) {
+        cn = tiles;
+        pn = tiles * kSplit * ((m + 15) / 16);
+        return tiles * kSplit;
+      }
+      return tiles;
+    };
     if (wave == 0) {
       const int lane = threadIdx.x & 63;
-      int base = 0;
+      int total2 = 0;
+      if (a.up_part) {
+        for (int e0 = 0; e0 < ne; e0 += 64) {
+          int pn, cn;
+          const int n = e0 + lane < ne ? entry_tasks(e0 + lane, true, pn, cn) : 0;
+          total2 += __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
+        }
+      }
+      const bool split = a.up_part && total2 <= (int)gridDim.x;
+      int base = 0, pb = 0, cb = 0;
       for (int e0 = 0; e0 < ne; e0 += 64) {
         const int e = e0 + lane;
-        int n = 0;
+        int pn = 0, cn = 0;
+        const int n = e < ne ? entry_tasks(e, split, pn, cn) : 0;
+        const int incl = wave_incl_scan(n), pincl = wave_incl_scan(pn), cincl = wave_incl_scan(cn);
         if (e < ne) {
-          const bool sh = e >= p.n;
-          const int m = sh ? a.B : p.offs[e + 1] - p.offs[e];
-          n = mfma_entry(m) ? (sh ? tiles_ms : tiles_m) : (sh ? tiles_s : tiles_r);
+          s_tstart[e] = base + incl - n;
+          s_pbase[e] = (unsigned short)(pb + pincl - pn);
+          s_cbase[e] = (unsigned short)(cb + cincl - cn);
         }
-        const int incl = wave_incl_scan(n);
-        if (e < ne) s_tstart[e] = base + incl - n;
         base += __builtin_amdgcn_readlane(incl, 63);
+        pb += __builtin_amdgcn_readlane(pincl, 63);
+        cb += __builtin_amdgcn_readlane(cincl, 63);
       }
-      if (lane == 0) s_tstart[ne] = base;
+      if (lane == 0) {
+        s_tstart[ne] = base;
+        s_use_split = split ? 1 : 0;
+      }
     }
     __syncthreads();
     const int total = s_tstart[ne];
+    const bool use_split = s_use_split != 0;
+    const int J = a.d / 32, nch = (J + kChunk - 1) / kChunk;
     for (int task = blockIdx.x; task < total; task += gridDim.x) {
       // entry of the task: the last e with s_tstart[e] <= task
       int lo = 0, hi = ne - 1;
@@ -142,9 +181,25 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       }
       const int e = wave_uniform(lo);
       const ExpertView v = e < p.n ? expert_view<T>(a, p, e) : shared_view(a);
-      const int tile = task - s_tstart[e];
-      if (mfma_entry(v.m)) up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x);
-      else up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+      const int local = task - s_tstart[e];
+      if (mfma_entry(v.m)) {
+        UpSlice sl = {0, J, 0, 1, nullptr, nullptr};
+        int tile = local;
+        if (use_split && v.m > 16) {
+          const int q = local % kSplit, nt = (v.m + 15) / 16;
+          tile = local / kSplit;
+          sl.s0 = (q * nch / kSplit) * kChunk;
+          sl.s1 = ((q + 1) * nch / kSplit) * kChunk;
+          if (sl.s1 > J) sl.s1 = J;
+          sl.slice = q;
+          sl.split = kSplit;
+          sl.part = a.up_part + (size_t)(s_pbase[e] + tile * kSplit * nt) * (kMfmaWaves * 64 * 4);
+          sl.counter = a.up_counter + s_cbase[e] + tile;
+        }
+        up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x, sl);
+      } else {
+        up_valu_dispatch<T, 2>(a, p.slots, v, local * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+      }
       __syncthreads();  // s_red / s_x are reused by the next task
     }
   }

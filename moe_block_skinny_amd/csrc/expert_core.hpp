@@ -317,9 +317,19 @@ __device__ __forceinline__ void up_valu_dispatch(const ExpertLaunch& a, const in
 // + q (q = 0..3) for token nt*16 + l%16 and lane l + 32 the matching up
 // sums; SwiGLU pairs them across the two lane halves.  The entry's token
 // rows are gathered into LDS (s_x).
+// K range of an MFMA gate/up task: all of d, or one of `split` slices of it
+// whose fp32 sums go to `part` (this tile's block: split x 4 waves x NT x 64
+// lanes of f32x4); the tile's last slice to arrive on `counter` adds the
+// slices in slice order and applies SwiGLU.
+struct UpSlice {
+  int s0, s1, slice, split;
+  float* part;
+  uint32_t* counter;
+};
+
 template <int NT>
 __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v, int p0,
-                                        unsigned char* s_x) {
+                                        unsigned char* s_x, const UpSlice& sl) {
   constexpr int PPT = MfmaX<NT>::kPerThread;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // rows 0-7 of the wave: gate rows of its 8 pairs; rows 8-15: their up rows
@@ -342,7 +352,30 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows_db<NT, kUpMfmaChunks / 2>(wa, wok, wb, wok, xrow, xok, 0, a.d / 32, s_x, acc);
+  mfma_rows_db<NT, kUpMfmaChunks / 2>(wa, wok, wb, wok, xrow, xok, sl.s0, sl.s1, s_x, acc);
+  if (sl.split > 1) {
+    // one K slice: store its sums (device-coherent: the tile's last slice,
+    // another workgroup of this launch, reads them) and arrive
+    const coherent_rsrc_t prs = coherent_rsrc(sl.part);
+    auto off = [&](int q, int nt) { return (uint32_t)((((q * kMfmaWaves + wave) * NT + nt) * 64 + lane) * 16); };
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) st_coherent4(prs, off(sl.slice, nt), __builtin_bit_cast(u32x4, acc[nt]));
+    __shared__ int s_last;
+    if (!arrive_last(sl.counter, (uint32_t)sl.split, &s_last)) return;
+    constexpr int kMaxSplit = 2;
+    u32x4 pv[kMaxSplit][NT];
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pv[q][nt] = ld_coherent4(prs, off(q < sl.split ? q : 0, nt));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[nt] = __builtin_bit_cast(f32x4, pv[0][nt]);
+#pragma unroll
+      for (int q = 1; q < kMaxSplit; ++q)
+        if (q < sl.split) acc[nt] += __builtin_bit_cast(f32x4, pv[q][nt]);
+    }
+  }
   // lane l < 32: pairs i .. i+3 (i = p0 + 8w + 4(l/16), a multiple of 4,
   // I a multiple of 32) of token nt*16 + l%16: one 16-byte store of h
 #pragma unroll
@@ -365,13 +398,13 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
 
 template <typename T>
 __device__ __forceinline__ void up_mfma_dispatch(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
-                                                 int p0, unsigned char* s_x) {
+                                                 int p0, unsigned char* s_x, const UpSlice& sl) {
   if constexpr (sizeof(T) == 2) {
     const int nt = (v.m + 15) / 16;
-    if (nt <= 1) up_mfma<1>(a, slots, v, p0, s_x);
-    else if (nt == 2) up_mfma<2>(a, slots, v, p0, s_x);
-    else if (nt == 3) up_mfma<3>(a, slots, v, p0, s_x);
-    else up_mfma<4>(a, slots, v, p0, s_x);
+    if (nt <= 1) up_mfma<1>(a, slots, v, p0, s_x, sl);
+    else if (nt == 2) up_mfma<2>(a, slots, v, p0, s_x, sl);
+    else if (nt == 3) up_mfma<3>(a, slots, v, p0, s_x, sl);
+    else up_mfma<4>(a, slots, v, p0, s_x, sl);
   }
 }
 

@@ -43,6 +43,11 @@ struct ExpertLaunch {
   // workgroup builds the plan from them; the last also stores it (plan_out)
   const int32_t* ids_in;
   int down_rows;            // rows per workgroup of the prefetching down+combine
+  // gate/up on the matrix shape: the K-slice partial sums of tiles cut in
+  // two (up_part, null: none are cut) and one arrival counter per such tile
+  // (up_counter, zero on entry and left at zero)
+  float* up_part;
+  uint32_t* up_counter;
 };
 
 // Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
