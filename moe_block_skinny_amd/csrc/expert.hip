@@ -297,17 +297,29 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   const int ne = entries(a, p, true);
   // entries by falling token count, dealt to the waves in snake order
   // (w, 2nw-1-w, 2nw+w, ...) so their token totals come out close
-  if (wave == 0) order_entries(a, p, ne, s_order);
+  __shared__ int s_next;
+  if (wave == 0) {
+    if constexpr (PAIRED) order_entries_by_tiles(a, p, ne, s_order);
+    else order_entries(a, p, ne, s_order);
+    if ((threadIdx.x & 63) == 0) s_next = nw;
+  }
   __syncthreads();
   if constexpr (PIPE) {
     down_valu_pipe<T, RT>(a, p, ne, s_order, r0, rt, sink, s_h);
   } else if constexpr (PAIRED) {
-    const int half = wave & 1, pw = wave >> 1, np = nw >> 1;
+    // units (entry in order, 16-row half of the tile): wave w starts with
+    // unit w and then claims the next free unit from an LDS counter, so the
+    // waves finish together whatever each entry costs (a fixed deal of the
+    // entries left the last waves ~20 us behind the first at batch 64).  A
+    // unit's outputs go to its own rows of s_y, so the result does not depend
+    // on which wave takes which unit.
     const int r_end = r0 + rt < a.d ? r0 + rt : a.d;
-    for (int j = 0;; ++j) {
-      const int pos = j * np + ((j & 1) ? np - 1 - pw : pw);
-      if (pos >= ne) break;
-      down_dispatch<T, PATHS, 16>(a, p.slots, expert_view<T>(a, p, s_order[pos]), r0 + 16 * half, sink, r_end);
+    for (int u = wave;;) {
+      if (u >= 2 * ne) break;
+      down_dispatch<T, PATHS, 16>(a, p.slots, expert_view<T>(a, p, s_order[u >> 1]), r0 + 16 * (u & 1), sink, r_end);
+      int nx = 0;
+      if ((threadIdx.x & 63) == 0) nx = atomicAdd(&s_next, 1);
+      u = __builtin_amdgcn_readfirstlane(nx);
     }
   } else {
     for (int j = 0;; ++j) {
