@@ -193,7 +193,7 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 // the fused barrier lines in the header, then h, ids, weights and plan.
 struct BlockWs {
   SkinnyWs route;
-  size_t route_off, ffn_h, ids, w, plan, sync, up_part, total;
+  size_t route_off, ffn_h, ids, w, plan, sync, up_part, ht, total;
   int hld;
 };
 
@@ -219,6 +219,12 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   if (bf16 && B > 8) {
     b.up_part = o;
     o = up(o + (size_t)256 * 2 * 4 * 4096);
+  }
+  // the tiled copy of h read by the matrix-shape down (bf16): two planes
+  b.ht = 0;
+  if (bf16) {
+    b.ht = o;
+    o = up(o + (size_t)2 * ht_rows(B, k, E) * b.hld * 2);
   }
   b.total = o;
   return b;
@@ -628,6 +634,10 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   // router launch when both take the same kernel family (the vector router
   // kernel carries only the vector gate/up, the MFMA one only the MFMA one).
   const int paths = expert_paths(bf16, force, B);
+  if (paths != kPathValu) {
+    ex.ht_hi = reinterpret_cast<uint16_t*>(w + L.ht);
+    ex.ht_lo = ex.ht_hi + (size_t)ht_rows(B, k, E) * L.hld;
+  }
   const bool route_in_up = paths == kPathValu && v != VAR_MFMA && B * k <= 64;
   const int sched = schedule();
   // AUTO takes the three launches: on MI355X each grid-wide barrier of the

@@ -414,6 +414,8 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
 hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
   ExpertLaunch a = a0;
   const int paths = expert_paths(a.bf16, a.force, a.B);
+  // the matrix-shape down reads h from the tiled copy the gate/up launch wrote
+  if (paths != kPathValu && (!a.ht_hi || !a.ht_lo)) return hipErrorInvalidValue;
   const int vec = a.bf16 ? 8 : 4;
   const bool short_rows = a.I <= 16 * vec && (!a.Ws13 || a.Is <= 16 * vec);
   const size_t h_bytes = (size_t)(a.B * a.k + a.B) * a.hld * sizeof(float);

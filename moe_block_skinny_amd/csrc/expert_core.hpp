@@ -122,7 +122,16 @@ struct ExpertView {
   const void* W13;    // [2I][d]
   const void* W2;     // [d][I]
   int slot0;          // first plan slot (routed) or -1 (shared)
+  int hbase;          // first row of its tiles in the tiled copy of h
 };
+
+// Tiled copy of h: the shared expert's tiles from row 0, routed entry e's
+// from row roundup(B, 16) + offs[e] + 16 e.  Entry e needs 16 ceil(m_e/16)
+// <= m_e + 15 rows, so the ranges do not overlap, and all entries fit in
+// roundup(B, 16) + B k + 16 min(E, B k) rows.
+__host__ __device__ __forceinline__ int ht_rows(int B, int k, int E) {
+  return ((B + 15) & ~15) + B * k + 16 * (E < B * k ? E : B * k);
+}
 
 template <typename T>
 __device__ __forceinline__ ExpertView expert_view(const ExpertLaunch& a, const PlanView& p, int e_idx) {
@@ -134,12 +143,14 @@ __device__ __forceinline__ ExpertView expert_view(const ExpertLaunch& a, const P
     v.W13 = reinterpret_cast<const T*>(a.W13) + (size_t)e * 2 * a.I * a.d;
     v.W2 = reinterpret_cast<const T*>(a.W2) + (size_t)e * a.d * a.I;
     v.slot0 = p.offs[e_idx];
+    v.hbase = ((a.B + 15) & ~15) + p.offs[e_idx] + 16 * e_idx;
   } else {
     v.m = a.B;
     v.I = a.Is;
     v.W13 = a.Ws13;
     v.W2 = a.Ws2;
     v.slot0 = -1;
+    v.hbase = 0;
   }
   return v;
 }
@@ -152,6 +163,7 @@ __device__ __forceinline__ ExpertView shared_view(const ExpertLaunch& a) {
   v.W13 = a.Ws13;
   v.W2 = a.Ws2;
   v.slot0 = -1;
+  v.hbase = 0;
   return v;
 }
 
@@ -184,22 +196,38 @@ __device__ __forceinline__ uint16_t* h_lo(const ExpertLaunch& a) {
   return reinterpret_cast<uint16_t*>(a.h) + (size_t)h_rows(a) * a.hld;
 }
 
+// Element (token t of entry v, column i) of the tiled copy: within a tile,
+// K step j = i / 32, lane kq * 16 + row (kq = i / 8 % 4, row = t % 16) holds
+// the 8 values the matrix operand takes from that lane.  hld is a multiple
+// of 32 for bf16 weights.
+__device__ __forceinline__ size_t ht_index(const ExpertLaunch& a, const ExpertView& v, int t, int i) {
+  const int j = i >> 5, kq = (i >> 3) & 3, e8 = i & 7;
+  return (size_t)(v.hbase + (t & ~15)) * a.hld + (size_t)(((j * 64 + kq * 16 + (t & 15)) << 3) + e8);
+}
+
+// h of token t (slot row sr) of entry v, column i; with a tiled copy also
+// there.
 template <typename T>
-__device__ __forceinline__ void h_store(const ExpertLaunch& a, int sr, int i, float v) {
+__device__ __forceinline__ void h_store(const ExpertLaunch& a, const ExpertView& ev, int t, int sr, int i, float v) {
   const size_t o = (size_t)sr * a.hld + i;
   if constexpr (sizeof(T) == 2) {
     const bf16_t hi = f32_to_bf16(v);
     const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
     st_coherent16b(h_hi(a) + o, hi);
     st_coherent16b(h_lo(a) + o, lo);
+    if (a.ht_hi) {
+      const size_t q = ht_index(a, ev, t, i);
+      st_coherent16b(a.ht_hi + q, hi);
+      st_coherent16b(a.ht_lo + q, lo);
+    }
   } else {
     st_coherent(a.h + o, v);
   }
 }
 
-// Values i .. i+3 (i a multiple of 4) of slot row sr.
+// Values i .. i+3 (i a multiple of 4) of token t (slot row sr) of entry ev.
 template <typename T>
-__device__ __forceinline__ void h_store4(const ExpertLaunch& a, int sr, int i, f32x4 v) {
+__device__ __forceinline__ void h_store4(const ExpertLaunch& a, const ExpertView& ev, int t, int sr, int i, f32x4 v) {
   const size_t o = (size_t)sr * a.hld + i;
   if constexpr (sizeof(T) == 2) {
     uint32_t h0, l0, h1, l1;
@@ -208,6 +236,11 @@ __device__ __forceinline__ void h_store4(const ExpertLaunch& a, int sr, int i, f
     const coherent_rsrc_t r = coherent_rsrc(a.h);
     st_coherent8(r, (uint32_t)(o * 2), u32x2{h0, h1});
     st_coherent8(r, (uint32_t)(((size_t)h_rows(a) * a.hld + o) * 2), u32x2{l0, l1});
+    if (a.ht_hi) {
+      const uint32_t q = (uint32_t)(ht_index(a, ev, t, i) * 2);
+      st_coherent8(coherent_rsrc(a.ht_hi), q, u32x2{h0, h1});
+      st_coherent8(coherent_rsrc(a.ht_lo), q, u32x2{l0, l1});
+    }
   } else {
     st_coherent4(coherent_rsrc(a.h), (uint32_t)(o * 4), __builtin_bit_cast(u32x4, v));
   }
@@ -297,7 +330,7 @@ __device__ __forceinline__ void up_valu(const ExpertLaunch& a, const int32_t* sl
 #pragma unroll
     for (int t = 0; t < MB; ++t)
       if (t == lane) sr = srow[t];
-    h_store<T>(a, sr, i, silu(g) * u);
+    h_store<T>(a, v, lane, sr, i, silu(g) * u);
   }
 }
 
@@ -391,7 +424,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
     if (lane < 32 && i < v.I && t < v.m) {
       int tok, sr;
       token_of(a, slots, v, t, tok, sr);
-      h_store4<bf16_t>(a, sr, i, hv);
+      h_store4<bf16_t>(a, v, t, sr, i, hv);
     }
   }
 }
@@ -710,17 +743,20 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   const u32x4 zero = {0u, 0u, 0u, 0u};
   constexpr int JH = JM / 2;
   // h of one token tile in two halves of K: 32 registers of h at a time keep
-  // the wave within its register budget.  Only the lanes of real tokens load
-  // (an entry of one token moves one row of h, not sixteen, through the
-  // vector memory path); the others neither load nor zero their registers
-  // (the products take zero for them): writing a register that a load might
-  // still own makes the compiler wait for every load in flight.
+  // the wave within its register budget.  h comes from the tiled copy, where
+  // a K step of a tile is 1 KB in lane order (one fully used cache line per
+  // four lanes; from the slot rows, each lane of a quad hit a different
+  // line, and at batch 64 the h reads took longer than the weight stream).
+  // Only the lanes of real tokens load; the others neither load nor zero
+  // their registers (the products take zero for them): writing a register
+  // that a load might still own makes the compiler wait for every load in
+  // flight.
   auto load_half = [&](bool ok, const uint16_t* hh, const uint16_t* hl, int half, u32x4 (&hv)[JH], u32x4 (&lv)[JH]) {
     if (ok) {
 #pragma unroll
       for (int jj = 0; jj < JH; ++jj) {
         const int j = half * JH + jj;
-        const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+        const size_t off = (size_t)(j < J ? j : J - 1) * 512;
         hv[jj] = *reinterpret_cast<const u32x4*>(hh + off);
         lv[jj] = *reinterpret_cast<const u32x4*>(hl + off);
       }
@@ -754,8 +790,9 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   int tok0 = 0, sr0 = 0;
   const bool ok0 = row < v.m;
   if (ok0) token_of(a, slots, v, row, tok0, sr0);
-  const uint16_t* hh0 = h_hi(a) + (size_t)(ok0 ? sr0 : 0) * a.hld;
-  const uint16_t* hl0 = h_lo(a) + (size_t)(ok0 ? sr0 : 0) * a.hld;
+  const size_t tb0 = (size_t)v.hbase * a.hld + lane * 8;   // tile 0, this lane's 16 bytes
+  const uint16_t* hh0 = a.ht_hi + tb0;
+  const uint16_t* hl0 = a.ht_lo + tb0;
   u32x4 wv[JM];
   {
     u32x4 hv[JH], lv[JH];
@@ -777,8 +814,9 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
     int tok = 0, sr = 0;
     const bool ok = ti < v.m;
     if (ok) token_of(a, slots, v, ti, tok, sr);
-    const uint16_t* hh = h_hi(a) + (size_t)(ok ? sr : 0) * a.hld;
-    const uint16_t* hl = h_lo(a) + (size_t)(ok ? sr : 0) * a.hld;
+    const size_t tb = (size_t)(v.hbase + nt * 16) * a.hld + lane * 8;
+    const uint16_t* hh = a.ht_hi + tb;
+    const uint16_t* hl = a.ht_lo + tb;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {

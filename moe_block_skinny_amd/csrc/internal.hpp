@@ -23,6 +23,11 @@ struct ExpertLaunch {
   const void* Ws13;         // [2Is][d] or null
   const void* Ws2;          // [d][Is]
   float* h;                 // workspace
+  // h of the matrix-shape down in 16-token tiles (hi plane, lo plane; null:
+  // not written): an entry's tile is 16 x hld bf16 in the order the matrix
+  // operand reads it, so each K step of a tile is one contiguous 1 KB
+  uint16_t* ht_hi;
+  uint16_t* ht_lo;
   int hld;                  // row stride of h (max(I, Is))
   float* Yslot;             // [B][k+1][d]
   int force;                // VAR_AUTO, VAR_GEMV (vector path for all),
