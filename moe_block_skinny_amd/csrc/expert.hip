@@ -264,11 +264,13 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
 // resident at once), else 16 (one M tile per MFMA wave; the LDS tile stays
 // within 36 KB at B=64).
 // PAIRED (matrix shape, RT > 16): a.down_rows (17..32) rows per workgroup,
-// 16 waves; each entry goes to a pair of waves, one per 16-row half, so h of
-// an entry crosses from L2 once per pair of row tiles (per 16 rows it was
-// the larger part of the launch's L2 traffic at batch 64).
+// 8 waves of 256 registers; one wave takes both 16-row halves of an entry
+// (down_mfma_duo), so h of an entry crosses from L2 once per workgroup (per
+// 16 rows it was the larger part of the launch's L2 traffic at batch 64;
+// per 16-row half on a pair of waves the launch took 56.8 us at batch 64,
+// one wave for both 51.2 us).
 template <typename T, int PATHS, int RT, bool PIPE>
-__global__ __launch_bounds__((PATHS == kPathValu || RT > 16) ? 1024 : 512, (PATHS == kPathValu || RT > 16) ? 1 : 4)
+__global__ __launch_bounds__(PATHS == kPathValu ? 1024 : 512, (PATHS == kPathValu || RT > 16) ? 1 : 4)
 void expert_down_combine_kernel(ExpertLaunch a) {
   constexpr bool PAIRED = !PIPE && RT > 16 && PATHS != kPathValu;
   // PIPE (vector shape, short rows, h fits in LDS): h is staged in LDS with
@@ -307,16 +309,21 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   if constexpr (PIPE) {
     down_valu_pipe<T, RT>(a, p, ne, s_order, r0, rt, sink, s_h);
   } else if constexpr (PAIRED) {
-    // units (entry in order, 16-row half of the tile): wave w starts with
-    // unit w and then claims the next free unit from an LDS counter, so the
-    // waves finish together whatever each entry costs (a fixed deal of the
-    // entries left the last waves ~20 us behind the first at batch 64).  A
-    // unit's outputs go to its own rows of s_y, so the result does not depend
-    // on which wave takes which unit.
+    // entries in order: wave w starts with entry w and then claims the next
+    // free one from an LDS counter, so the waves finish together whatever
+    // each entry costs (a fixed deal of the entries left the last waves
+    // ~20 us behind the first at batch 64).  An entry's outputs go to its
+    // own rows of s_y, so the result does not depend on which wave takes
+    // which entry.
     const int r_end = r0 + rt < a.d ? r0 + rt : a.d;
     for (int u = wave;;) {
-      if (u >= 2 * ne) break;
-      down_dispatch<T, PATHS, 16>(a, p.slots, expert_view<T>(a, p, s_order[u >> 1]), r0 + 16 * (u & 1), sink, r_end);
+      if (u >= ne) break;
+      const ExpertView v = expert_view<T>(a, p, s_order[u]);
+      const int nt = (v.m + 15) / 16;
+      if (nt <= 1) down_mfma_duo<1>(a, p.slots, v, r0, sink, r_end);
+      else if (nt == 2) down_mfma_duo<2>(a, p.slots, v, r0, sink, r_end);
+      else if (nt == 3) down_mfma_duo<3>(a, p.slots, v, r0, sink, r_end);
+      else down_mfma_duo<4>(a, p.slots, v, r0, sink, r_end);
       int nx = 0;
       if ((threadIdx.x & 63) == 0) nx = atomicAdd(&s_next, 1);
       u = __builtin_amdgcn_readfirstlane(nx);
@@ -429,15 +436,15 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, ch
     a.down_rows = rt;
   }
   // matrix shape: rows split evenly over the compute units in multiples of
-  // 4; above 16 a pair of waves takes each entry (one per 16-row half)
+  // 4; above 16 one wave takes both 16-row halves of an entry (8 waves)
   const bool paired = !pipe && paths != kPathValu && a.bf16 && rt_pipe > 16 && rt_pipe <= 32;
   if (paired) {
     rt = rt_pipe;
     a.down_rows = rt;
   }
   const int g = (a.d + rt - 1) / rt;
-  int nw = max_entries(a) * (paired ? 2 : 1);
-  const int maxw = (paths == kPathValu || paired) ? 16 : 8;
+  int nw = max_entries(a);
+  const int maxw = paths == kPathValu ? 16 : 8;
   if (nw > maxw) nw = maxw;
   if (nw < 1) nw = 1;
   const size_t lds = (size_t)(a.B * a.k + a.B) * rt * sizeof(float) + (pipe ? h_bytes : 0);

@@ -829,6 +829,86 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   }
 }
 
+// Rows r0 .. r0+31 of entry v with one wave (matrix shape, the two 16-row
+// halves of a 17..32-row tile): the wave holds the W2 rows of both halves
+// (64 registers, all K steps) and a token tile's h in full K (hi and lo
+// planes, 64 registers), so each tile of h crosses from L2 once for the 32
+// rows and in one memory round trip; the next tile's h is requested before
+// the products of the current one (a second 64-register buffer).  Needs the
+// 256-register budget of two waves per SIMD.  Rows from r_end on re-read the
+// last row of the range and are not stored.  Each output is the same chain
+// of products as in down_mfma, hence the same bits.
+template <int NT>
+__device__ __forceinline__ void down_mfma_duo(const ExpertLaunch& a, const int32_t* slots, const ExpertView& v,
+                                              int r0, const YSink& sink, int r_end) {
+  constexpr int JM = kMaxInter / 32;
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, kq = lane >> 4;
+  const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
+  const int ra = r0 + row < r_end ? r0 + row : r_end - 1;
+  const int rb = r0 + 16 + row < r_end ? r0 + 16 + row : r_end - 1;
+  const bf16_t* wa = W2 + (size_t)ra * v.I;
+  const bf16_t* wb = W2 + (size_t)rb * v.I;
+  const int J = wave_uniform(v.I / 32);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load_h = [&](int nt, u32x4 (&hv)[JM], u32x4 (&lv)[JM]) {
+    if (nt * 16 + row < v.m) {
+      const size_t tb = (size_t)(v.hbase + nt * 16) * a.hld + lane * 8;
+#pragma unroll
+      for (int j = 0; j < JM; ++j) {
+        const size_t off = tb + (size_t)(j < J ? j : J - 1) * 512;
+        hv[j] = *reinterpret_cast<const u32x4*>(a.ht_hi + off);
+        lv[j] = *reinterpret_cast<const u32x4*>(a.ht_lo + off);
+      }
+    }
+  };
+  auto tile = [&](int nt, const u32x4 (&wva)[JM], const u32x4 (&wvb)[JM], const u32x4 (&hv)[JM],
+                  const u32x4 (&lv)[JM]) {
+    const bool ok = nt * 16 + row < v.m;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      if (j < J) {
+        const bf16x8 h = __builtin_bit_cast(bf16x8, ok ? hv[j] : zero);
+        const bf16x8 l = __builtin_bit_cast(bf16x8, ok ? lv[j] : zero);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wva[j]), h, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wvb[j]), h, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wva[j]), l, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wvb[j]), l, acc1, 0, 0, 0);
+      }
+    }
+    if (ok) {
+      int tok, sr;
+      token_of(a, slots, v, nt * 16 + row, tok, sr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * kq + i;
+        if (r < r_end) *sink.at(a, sr, r) = acc0[i];
+        if (r + 16 < r_end) *sink.at(a, sr, r + 16) = acc1[i];
+      }
+    }
+  };
+  u32x4 hA[JM], lA[JM], hB[JM], lB[JM];
+  load_h(0, hA, lA);
+  u32x4 wva[JM], wvb[JM];
+#pragma unroll
+  for (int j = 0; j < JM; ++j) {
+    const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
+    wva[j] = ld128_stream(wa + off);
+    wvb[j] = ld128_stream(wb + off);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (nt % 2 == 0) {
+      if (nt + 1 < NT) load_h(nt + 1, hB, lB);
+      tile(nt, wva, wvb, hA, lA);
+    } else {
+      if (nt + 1 < NT) load_h(nt + 1, hA, lA);
+      tile(nt, wva, wvb, hB, lB);
+    }
+  }
+}
+
 // ---- down projection as (entry, 64-row tile) tasks ------------------------
 
 // LDS image of one entry's h for the MFMA down: the token rows of the hi
