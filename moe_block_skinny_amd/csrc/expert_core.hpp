@@ -205,21 +205,23 @@ __device__ __forceinline__ size_t ht_index(const ExpertLaunch& a, const ExpertVi
   return (size_t)(v.hbase + (t & ~15)) * a.hld + (size_t)(((j * 64 + kq * 16 + (t & 15)) << 3) + e8);
 }
 
-// h of token t (slot row sr) of entry v, column i; with a tiled copy also
-// there.
+// h of token t (slot row sr) of entry v, column i: to the slot rows, or,
+// when the launch has the tiled copy (its down reads h only from there,
+// every entry on the matrix shape), to the tiled copy alone.
 template <typename T>
 __device__ __forceinline__ void h_store(const ExpertLaunch& a, const ExpertView& ev, int t, int sr, int i, float v) {
   const size_t o = (size_t)sr * a.hld + i;
   if constexpr (sizeof(T) == 2) {
     const bf16_t hi = f32_to_bf16(v);
     const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-    st_coherent16b(h_hi(a) + o, hi);
-    st_coherent16b(h_lo(a) + o, lo);
     if (a.ht_hi) {
       const size_t q = ht_index(a, ev, t, i);
       st_coherent16b(a.ht_hi + q, hi);
       st_coherent16b(a.ht_lo + q, lo);
+      return;
     }
+    st_coherent16b(h_hi(a) + o, hi);
+    st_coherent16b(h_lo(a) + o, lo);
   } else {
     st_coherent(a.h + o, v);
   }
@@ -233,14 +235,15 @@ __device__ __forceinline__ void h_store4(const ExpertLaunch& a, const ExpertView
     uint32_t h0, l0, h1, l1;
     split_bf16x2(v[0], v[1], h0, l0);
     split_bf16x2(v[2], v[3], h1, l1);
-    const coherent_rsrc_t r = coherent_rsrc(a.h);
-    st_coherent8(r, (uint32_t)(o * 2), u32x2{h0, h1});
-    st_coherent8(r, (uint32_t)(((size_t)h_rows(a) * a.hld + o) * 2), u32x2{l0, l1});
     if (a.ht_hi) {
       const uint32_t q = (uint32_t)(ht_index(a, ev, t, i) * 2);
       st_coherent8(coherent_rsrc(a.ht_hi), q, u32x2{h0, h1});
       st_coherent8(coherent_rsrc(a.ht_lo), q, u32x2{l0, l1});
+      return;
     }
+    const coherent_rsrc_t r = coherent_rsrc(a.h);
+    st_coherent8(r, (uint32_t)(o * 2), u32x2{h0, h1});
+    st_coherent8(r, (uint32_t)(((size_t)h_rows(a) * a.hld + o) * 2), u32x2{l0, l1});
   } else {
     st_coherent4(coherent_rsrc(a.h), (uint32_t)(o * 4), __builtin_bit_cast(u32x4, v));
   }

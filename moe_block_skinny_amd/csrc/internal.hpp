@@ -23,9 +23,10 @@ struct ExpertLaunch {
   const void* Ws13;         // [2Is][d] or null
   const void* Ws2;          // [d][Is]
   float* h;                 // workspace
-  // h of the matrix-shape down in 16-token tiles (hi plane, lo plane; null:
-  // not written): an entry's tile is 16 x hld bf16 in the order the matrix
-  // operand reads it, so each K step of a tile is one contiguous 1 KB
+  // h of the matrix-shape down in 16-token tiles (hi plane, lo plane).  When
+  // set, the gate/up launch writes h here instead of to the slot rows: an
+  // entry's tile is 16 x hld bf16 in the order the matrix operand reads it,
+  // so each K step of a tile is one contiguous 1 KB
   uint16_t* ht_hi;
   uint16_t* ht_lo;
   int hld;                  // row stride of h (max(I, Is))
