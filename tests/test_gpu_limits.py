@@ -74,3 +74,48 @@ def test_block_and_route_at_scope_limits(name):
     assert np.array_equal(host(rids), c.ids)
     assert np.array_equal(host(plan), c.plan)
     assert np.max(np.abs(host(rw) - c.w)) <= 1e-5
+
+
+# The matrix-shape down at its edges: 17..32 rows per workgroup with the last
+# workgroup's range cut short (d = 4128: 20 rows per workgroup, 8 in the
+# last; d = 5120: 20 rows, a 4-row second half), a shared expert with another
+# intermediate size than the routed ones (its h tiles are read with the
+# wider row stride), no shared expert, and the matrix shape forced at a
+# batch that would take the vector shape (entries of one to a few tokens,
+# h tiles mostly padding).
+EDGES = {
+    "rows20_shared_wider": (synth.MoEConfig("rows20_shared_wider", 24, 5120, 64, 4, 64, 96, "bf16", "gumbel"), None),
+    "ragged_tail_no_shared": (synth.MoEConfig("ragged_tail_no_shared", 64, 4128, 32, 2, 128, 0, "bf16", "zipf"), None),
+    "forced_matrix_b4": (synth.MoEConfig("forced_matrix_b4", 4, 7168, 64, 8, 128, 128, "bf16", "gumbel"), "mfma"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_block_matrix_down_edges(name):
+    cfg0, force = EDGES[name]
+    c = inputs.Case(cfg0, seed=11)
+    cfg = c.cfg
+    say("matrix down edge", name, "distinct experts", len(c.touched))
+    W13, W2, Ws13, Ws2 = weights(c)
+    bias = None if c.bias is None else dev(c.bias)
+    out = torch.full((cfg.B, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                         I=cfg.I, Is=cfg.Is))
+    prev = mb.set_variant(force) if force else None
+    try:
+        mb.moe_block(dev(c.X), dev(c.Wr), cfg.k, W13, W2, out, ws, Ws13, Ws2, bias, c.bias_ld, ids, w)
+        torch.cuda.synchronize()
+        say("  variant", mb.last_variant())
+    finally:
+        if force:
+            mb.set_variant(prev)
+    ref = c.oracle_block()["out"]
+    g = host(out)
+    assert np.array_equal(host(ids), c.ids)
+    assert np.max(np.abs(host(w) - c.w)) <= 1e-5
+    scale = rms(ref)
+    err = np.abs(g - ref)
+    say("  max|err|/rms", float(err.max() / scale))
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
