@@ -282,17 +282,45 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   const int rt = (PIPE || PAIRED) ? a.down_rows : RT;
   float* s_y = s_dyn;
   float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
-  for (int i = threadIdx.x; i < a.B * a.k; i += blockDim.x) s_tw[i] = a.topk_w[i];
+  // The gate weights, (PIPE) h and the plan are requested together, into
+  // registers, and written to LDS once all have arrived: one memory round
+  // trip before the first W2 request instead of one per array.  h goes to
+  // LDS as stored (fp32, or for bf16 weights the hi and lo planes, which are
+  // the word rows down_valu_pipe reads).
+  constexpr int kTwRegs = 2, kHRegs = 4;
+  const int ntw = a.B * a.k, n4 = PIPE ? (a.B * a.k + a.B) * a.hld / 4 : 0;
+  const int nt_ = (int)blockDim.x;
+  float twr[kTwRegs];
+  f32x4 hr[kHRegs];
+#pragma unroll
+  for (int q = 0; q < kTwRegs; ++q) {
+    const int i = threadIdx.x + q * nt_;
+    twr[q] = a.topk_w[i < ntw ? i : 0];
+  }
   if constexpr (PIPE) {
-    const int nrows = a.B * a.k + a.B;
-    // h to LDS as stored (fp32, or for bf16 weights the hi and lo planes,
-    // which are the word rows down_valu_pipe reads)
-    const int n4 = nrows * a.hld / 4;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x)
-      reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
+#pragma unroll
+    for (int q = 0; q < kHRegs; ++q) {
+      const int i = threadIdx.x + q * nt_;
+      hr[q] = reinterpret_cast<const f32x4*>(a.h)[i < n4 ? i : 0];
+    }
   }
   __shared__ int s_order[kMaxB * kMaxK + kMaxB];
-  const PlanView p = stage_plan(a, s_plan);   // its barrier also covers s_tw and s_h
+  const PlanView p = stage_plan(a, s_plan);
+#pragma unroll
+  for (int q = 0; q < kTwRegs; ++q) {
+    const int i = threadIdx.x + q * nt_;
+    if (i < ntw) s_tw[i] = twr[q];
+  }
+  for (int i = threadIdx.x + kTwRegs * nt_; i < ntw; i += nt_) s_tw[i] = a.topk_w[i];
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int q = 0; q < kHRegs; ++q) {
+      const int i = threadIdx.x + q * nt_;
+      if (i < n4) reinterpret_cast<f32x4*>(s_h)[i] = hr[q];
+    }
+    for (int i = threadIdx.x + kHRegs * nt_; i < n4; i += nt_)
+      reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
+  }
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * rt;
   const YSink sink = {s_y, 1, r0, rt};
