@@ -254,12 +254,17 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
  *      workgroup stores topk_ids, topk_w and the plan;
  *   3. down projection of every expert fused with the weighted combine: the
  *      per-slot outputs never leave the chip.
- * Otherwise: 1. router scoring + top-k + plan (the last workgroup to finish
- * selects), with the shared expert's gate/up in the same launch; 2. routed
- * gate/up + SwiGLU; 3. as above.
+ * Otherwise, on the vector-ALU shape: 1. router scoring + top-k + plan
+ * (the last workgroup to finish selects), with the shared expert's gate/up
+ * in the same launch; 2. routed gate/up + SwiGLU; 3. as above.  On the
+ * matrix-core shape (bf16, B > 8): 1. router products over K slices; 2. a
+ * finish launch that adds the slices and the bias and stores topk_ids and
+ * topk_w; 3. gate/up + SwiGLU, every workgroup building the plan from the
+ * ids, the shared expert one more entry, the heaviest token tiles cut in two
+ * K halves; 4. down + combine, reading h from a tiled copy in ws.
  * Same scope and results as moe_route, moe_expert_ffn and moe_combine in
- * sequence (bit for bit with the vector-ALU shapes; with the MFMA shape the
- * shared expert's K split differs, within fp32 rounding).  topk_ids /
+ * sequence (bit for bit with the vector-ALU shapes; with the matrix-core
+ * shape the gate/up's K splits differ, within fp32 rounding).  topk_ids /
  * topk_w are optional outputs (NULL: kept in ws). */
 moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
                        const void* Wr, const float* bias, int bias_ld, const void* W13,
