@@ -103,12 +103,12 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // ---- kernel shape of the skinny product --------------------------------------
 
 // Automatic shapes: the small-matrix (gemv) shape at B <= 2, split-K above.
-// The dense product takes the matrix shape from B = 6 (bf16, K % 32 == 0):
-// measured at N = 3072, K = 7168 the split-K shape grows by ~0.9 us per
-// token (11.5 us at B = 4, 15.1 at 8) while the matrix shape stays at
-// ~13.4 us.  The router keeps split-K up to B = 8, where the gate/up launch
-// selects from its logits.
-constexpr int kDenseSplitkMaxB = 5;
+// The dense product takes the matrix shape from B = 5 (bf16, K % 32 == 0):
+// measured at N = 3072, K = 7168 the split-K shape takes 11.4 us at B = 4
+// and 14.2-15.0 us at B = 5..8 (from B = 5 it runs the 8-token instance),
+// while the matrix shape stays at ~13.2 us.  The router keeps split-K up to
+// B = 8, where the gate/up launch selects from its logits.
+constexpr int kDenseSplitkMaxB = 4;
 
 moe_status_t resolve_skinny(int bf16, int B, int K, int* variant, bool router = true) {
   const int f = forced();
