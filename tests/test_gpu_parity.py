@@ -42,8 +42,8 @@ def ws_for(op, dtype, **kw):
     return mb.workspace(mb.workspace_bytes(op, dtype, **kw))
 
 
-SHAPES = {"gemv": [1, 2], "splitk": [1, 2, 3, 4, 5, 8], "mfma": [1, 2, 9, 16, 17, 33, 64],
-          "auto": [1, 2, 3, 4, 8, 16, 24, 48, 64]}
+SHAPES = {"gemv": [1, 2], "splitk": [1, 2, 3, 4, 5, 8], "mfma": [1, 2, 5, 9, 16, 17, 33, 64],
+          "auto": [1, 2, 3, 4, 5, 6, 8, 16, 24, 48, 64]}
 
 
 # ---------------------------------------------------------------- skinny_gemm
