@@ -113,23 +113,26 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     const bool all_mfma = PATHS == kPathBoth && p.n * tiles_m >= kUpAllMfmaTasks;
     auto mfma_entry = [&](int m) { return all_mfma || use_mfma<PATHS>(m); };
     // Tiles of entries with more than 16 tokens take longest (their
-    // activations are staged in several 16-token tiles per K step): when the
-    // grid still gives every task a workgroup of its own, each such tile is
-    // cut in two K slices on two workgroups, the later of which adds the
-    // halves and applies SwiGLU.  s_tstart[e]: first task of entry e;
-    // s_pbase[e] / s_cbase[e]: its first partial block (4 KB units) and tile
-    // counter (split entries); one wave, 64 entries per pass.
+    // activations are staged in several 16-token tiles per K step): the
+    // tiles of entries with at least smin token tiles are cut in two K
+    // slices on two workgroups, the later of which adds the halves and
+    // applies SwiGLU.  smin is the smallest of 2, 3, 4 for which the grid
+    // still gives every task a workgroup of its own (0: no cut), so the
+    // heaviest entries are cut first when not all can be.  s_tstart[e]:
+    // first task of entry e; s_pbase[e] / s_cbase[e]: its first partial
+    // block (4 KB units) and tile counter (cut entries); one wave, 64
+    // entries per pass.
     constexpr int kSplit = 2;
     __shared__ unsigned short s_pbase[kMaxE + 2];
     __shared__ unsigned short s_cbase[kMaxE + 2];
     __shared__ int s_use_split;
-    auto entry_tasks = [&](int e, bool split, int& pn, int& cn) {
+    auto entry_tasks = [&](int e, int smin, int& pn, int& cn) {
       const bool sh = e >= p.n;
       const int m = sh ? a.B : p.offs[e + 1] - p.offs[e];
       pn = cn = 0;
       if (!mfma_entry(m)) return sh ? tiles_s : tiles_r;
       const int tiles = sh ? tiles_ms : tiles_m;
-      if (split && m > 16) {
+      if (smin && (m + 15) / 16 >= smin) {
         cn = tiles;
         pn = tiles * kSplit * ((m + 15) / 16);
         return tiles * kSplit;
@@ -138,15 +141,28 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     };
     if (wave == 0) {
       const int lane = threadIdx.x & 63;
-      int total2 = 0;
+      // tasks uncut (t1), and with the entries of >= 2, 3, 4 token tiles cut
+      int t1 = 0, t2 = 0, t3 = 0, t4 = 0;
       if (a.up_part) {
         for (int e0 = 0; e0 < ne; e0 += 64) {
-          int pn, cn;
-          const int n = e0 + lane < ne ? entry_tasks(e0 + lane, true, pn, cn) : 0;
-          total2 += __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
+          const int e = e0 + lane;
+          int pn, cn, n = 0, x = 0, nt = 0;
+          if (e < ne) {
+            n = entry_tasks(e, 0, pn, cn);
+            const int m = e >= p.n ? a.B : p.offs[e + 1] - p.offs[e];
+            if (mfma_entry(m)) {
+              x = e >= p.n ? tiles_ms : tiles_m;   // a cut adds one task per tile
+              nt = (m + 15) / 16;
+            }
+          }
+          t1 += __builtin_amdgcn_readlane(wave_incl_scan(n), 63);
+          t2 += __builtin_amdgcn_readlane(wave_incl_scan(nt >= 2 ? x : 0), 63);
+          t3 += __builtin_amdgcn_readlane(wave_incl_scan(nt >= 3 ? x : 0), 63);
+          t4 += __builtin_amdgcn_readlane(wave_incl_scan(nt >= 4 ? x : 0), 63);
         }
       }
-      const bool split = a.up_part && total2 <= (int)gridDim.x;
+      const int G = (int)gridDim.x;
+      const int split = !a.up_part ? 0 : (t1 + t2 <= G ? 2 : (t1 + t3 <= G ? 3 : (t1 + t4 <= G ? 4 : 0)));
       int base = 0, pb = 0, cb = 0;
       for (int e0 = 0; e0 < ne; e0 += 64) {
         const int e = e0 + lane;
@@ -164,12 +180,12 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       }
       if (lane == 0) {
         s_tstart[ne] = base;
-        s_use_split = split ? 1 : 0;
+        s_use_split = split;
       }
     }
     __syncthreads();
     const int total = s_tstart[ne];
-    const bool use_split = s_use_split != 0;
+    const int smin = s_use_split;
     const int J = a.d / 32, nch = (J + kChunk - 1) / kChunk;
     for (int task = blockIdx.x; task < total; task += gridDim.x) {
       // entry of the task: the last e with s_tstart[e] <= task
@@ -185,7 +201,7 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       if (mfma_entry(v.m)) {
         UpSlice sl = {0, J, 0, 1, nullptr, nullptr};
         int tile = local;
-        if (use_split && v.m > 16) {
+        if (smin && (v.m + 15) / 16 >= smin) {
           const int q = local % kSplit, nt = (v.m + 15) / 16;
           tile = local / kSplit;
           sl.s0 = (q * nch / kSplit) * kChunk;

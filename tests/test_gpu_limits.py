@@ -119,3 +119,38 @@ def test_block_matrix_down_edges(name):
     err = np.abs(g - ref)
     say("  max|err|/rms", float(err.max() / scale))
     assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
+
+
+def test_block_gate_up_cuts_heaviest_entries_first():
+    """Batch 64 (Zipf routing) with a routing where cutting every entry of
+    more than 16 tokens into two K halves would need more gate/up tasks than
+    the launch has workgroups (512), but cutting those of more than 32 fits:
+    the cut then covers only the heavier entries.  The case is checked to be
+    one (counted from the oracle's routing), then the block against the
+    oracle as above."""
+    cfg = synth.CONFIGS["tp8_b64"]
+    c = inputs.Case(cfg, seed=1)
+    _, cnt = np.unique(c.ids, return_counts=True)
+    ms = list(cnt) + [cfg.B]                 # routed entries, then the shared one
+    tiles = 2 * cfg.I // 64                  # 64-row tasks per entry
+    t1 = tiles * len(ms)
+    assert t1 + tiles * sum(m > 16 for m in ms) > 512
+    assert t1 + tiles * sum(m > 32 for m in ms) <= 512
+    W13, W2, Ws13, Ws2 = weights(c)
+    out = torch.full((cfg.B, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                         I=cfg.I, Is=cfg.Is))
+    mb.moe_block(dev(c.X), dev(c.Wr), cfg.k, W13, W2, out, ws, Ws13, Ws2, dev(c.bias), c.bias_ld, ids, w)
+    torch.cuda.synchronize()
+    say("cut heaviest first: tasks uncut", t1, "variant", mb.last_variant())
+    ref = c.oracle_block()["out"]
+    g = host(out)
+    assert np.array_equal(host(ids), c.ids)
+    assert np.max(np.abs(host(w) - c.w)) <= 1e-5
+    scale = rms(ref)
+    err = np.abs(g - ref)
+    say("  max|err|/rms", float(err.max() / scale))
+    assert err.max() <= 2e-2 * scale
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
