@@ -676,46 +676,42 @@ __device__ __forceinline__ void down_valu_pipe(const ExpertLaunch& a, const Plan
 }
 
 // Entries of the plan (routed, then the shared one) ordered by falling token
-// count, ties by entry index, into s_order -- one wave.  Up to 256 entries:
-// one ballot per token count and 64 entries, from the largest count down
-// (each entry's count held in a register); more: by ranking, which reads
-// every other entry's count from LDS per entry (~3 us at 51 entries).
-__device__ __forceinline__ void order_entries(const ExpertLaunch& a, const PlanView& p, int ne, int* s_order) {
+// count, ties by entry index, into s_order -- one wave.  Each entry's count
+// sits in a register (KC registers of 64 entries); for every count that
+// occurs, from the largest down, one ballot per 64 entries places its
+// entries.  (Ranking each entry against every other one through LDS took
+// ~3 us at 51 entries and grows with the square of the count.)
+template <int KC>
+__device__ __forceinline__ void order_by_count(const ExpertLaunch& a, const PlanView& p, int ne, int* s_order) {
   const int lane = threadIdx.x & 63;
-  constexpr int kChunks = 4;
-  if (ne <= 64 * kChunks) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int m[kChunks];
-    uint32_t mmax = 0u;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int m[KC];
+  uint64_t present = 0ull;   // bit c-1: some entry has c tokens (1 <= c <= B <= 64)
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      const int i = q * 64 + lane;
-      m[q] = i < ne ? (i < p.n ? p.offs[i + 1] - p.offs[i] : a.B) : -1;   // -1: no entry
-      mmax = m[q] > (int)mmax ? (uint32_t)m[q] : mmax;
-    }
-    const int cmax = (int)wave_max_u32(mmax);
-    int pos = 0;
-    for (int c = cmax; c >= 0; --c) {
+  for (int q = 0; q < KC; ++q) {
+    const int i = q * 64 + lane;
+    m[q] = i < ne ? (i < p.n ? p.offs[i + 1] - p.offs[i] : a.B) : 0;
+    if (m[q] > 0) present |= 1ull << (m[q] - 1);
+  }
+  present = ((uint64_t)wave_or_u32((uint32_t)(present >> 32)) << 32) | wave_or_u32((uint32_t)present);
+  int pos = 0;
+  while (present) {
+    const int c = 64 - __builtin_clzll(present);   // the largest count left
+    present &= ~(1ull << (c - 1));
 #pragma unroll
-      for (int q = 0; q < kChunks; ++q) {
-        if (q * 64 >= ne) break;
-        const uint64_t bm = __ballot(m[q] == c);
-        if (m[q] == c) s_order[pos + __popcll(bm & below)] = q * 64 + lane;
-        pos += __popcll(bm);
-      }
+    for (int q = 0; q < KC; ++q) {
+      if (q * 64 >= ne) break;
+      const uint64_t bm = __ballot(m[q] == c);
+      if (m[q] == c) s_order[pos + __popcll(bm & below)] = q * 64 + lane;
+      pos += __popcll(bm);
     }
-    return;
   }
-  for (int i0 = 0; i0 < ne; i0 += 64) {
-    const int i = i0 + lane;
-    const int mi = i < ne ? (i < p.n ? p.offs[i + 1] - p.offs[i] : a.B) : -1;
-    int rank = 0;
-    for (int j = 0; j < ne; ++j) {
-      const int mj = j < p.n ? p.offs[j + 1] - p.offs[j] : a.B;
-      rank += (mj > mi || (mj == mi && j < i)) ? 1 : 0;
-    }
-    if (i < ne) s_order[rank] = i;
-  }
+}
+
+__device__ __forceinline__ void order_entries(const ExpertLaunch& a, const PlanView& p, int ne, int* s_order) {
+  if (ne <= 64) order_by_count<1>(a, p, ne, s_order);
+  else if (ne <= 256) order_by_count<4>(a, p, ne, s_order);
+  else order_by_count<(kMaxB * kMaxK + kMaxB + 63) / 64>(a, p, ne, s_order);   // entries <= B k + 1
 }
 
 // Entries ordered by falling number of 16-token tiles (4 classes at B <= 64),
