@@ -53,11 +53,32 @@ __device__ __forceinline__ PlanView plan_view(const ExpertLaunch& a, const int32
 
 // Copy the plan into LDS with the whole workgroup (one coalesced pass) and
 // return a view of it.  Ends with a barrier.
+// Copy n words from global memory to LDS with the whole workgroup: the
+// first 8 per thread are all requested before any is stored, so they cost
+// one memory round trip (a plain loop waits for each load before the next,
+// one round trip per word per thread).
+__device__ __forceinline__ void stage_words(int32_t* dst, const int32_t* src, int n) {
+  constexpr int R = 8;
+  const int nt = (int)blockDim.x;
+  int32_t r[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int i = threadIdx.x + q * nt;
+    r[q] = i < n ? src[i] : 0;   // lanes past n request nothing
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int i = threadIdx.x + q * nt;
+    if (i < n) dst[i] = r[q];
+  }
+  for (int i = threadIdx.x + R * nt; i < n; i += nt) dst[i] = src[i];
+}
+
 __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s_plan) {
   const int nslot = a.B * a.k;
   const int maxa = nslot < a.E ? nslot : a.E;
   const int words = 2 + 2 * maxa + nslot;
-  for (int i = threadIdx.x; i < words; i += blockDim.x) s_plan[i] = a.plan[i];
+  stage_words(s_plan, a.plan, words);
   __syncthreads();
   return plan_view(a, s_plan);
 }
@@ -71,7 +92,7 @@ __device__ __forceinline__ PlanView plan_from_ids(const ExpertLaunch& a, int32_t
   const int nslot = a.B * a.k;
   int32_t* s_ids = reinterpret_cast<int32_t*>(scratch);
   PlanScratch& ps = *reinterpret_cast<PlanScratch*>(scratch + kMaxB * kMaxK * 4);
-  for (int i = threadIdx.x; i < nslot; i += blockDim.x) s_ids[i] = a.ids_in[i];
+  stage_words(s_ids, a.ids_in, nslot);
   __syncthreads();
   const bool writer = blockIdx.x == gridDim.x - 1;
   plan_block(s_ids, nslot, a.k, a.E, s_plan, writer ? a.plan_out : nullptr, ps);
