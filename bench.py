@@ -1,33 +1,42 @@
 #!/usr/bin/env python3
-"""µs per decode MoE block and achieved HBM GB/s on one MI355X.
+"""µs per decode MoE block and achieved HBM GB/s on one MI355X, batch 1-64.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp16_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials T]
+                    [--workload sweep|tp8_b64|tp16_b1|tp16_b8|tiny|dense|oproj|stream|copy]
 
 A step is one pass of the whole decode MoE block (router scoring, top-k and
 plan, routed and shared expert gate/up + SwiGLU + down, weighted combine)
 over one batch of synthetic bf16 input, through the C ABI (moe_block).
-Default workload: one TP16 weight shard at batch 1 (d=7168, E=384, top-8,
-I=Is=128).  Other workloads: tp16_b8, tp8_b64, tiny, dense (the attention
-input projection, --batch B), oproj (the attention output projection with
-the residual added, --batch B).
 
+Default (--workload sweep): the metric's batch range in one run.  The
+headline `value` is the largest single-GPU workload, one TP8 weight shard at
+batch 64 (d=7168, E=384, top-8, I=Is=256, Zipf(1.1) routing); config.sweep
+holds the TP16 shard at batch 1 and at batch 8 (Gumbel routing), the dense
+attention input projection at B = 1, 8, 64, and config.stream the read-only
+128-bit streaming yardstick these are compared with.
+
+Timing of every entry, on one stream:
+  * every rotation set is run once, untimed, whatever --warmup is (weights
+    and page tables of every set touched before timing);
+  * W warm-up steps;
+  * T trials (default 7), each exactly K steps between two HIP events with
+    the device synchronised before and after; sets 0, 1, ... in turn, so
+    every trial runs the same sets.  value = median µs per step over the
+    trials; p10 / p90 alongside.
 Weights are random (seeded torch generator on the GPU) in R rotating full
 sets so that the bytes touched between two uses of a set exceed twice the
 256 MB Infinity Cache plus L2: each timed step reads HBM, not cache.
-Inputs are resident in HBM before the timed region.  W warm-up steps, then
-exactly K timed steps between two synchronised HIP events.
 
-Prints ONE JSON line.  Besides the headline, it carries
-  roofline:     the dominant kernel (the fused block kernel where the block
-                runs as one launch, else the launch with the largest time)
-                timed with HIP events
-                that its own dispatch records (hipExtLaunchKernel, on the
-                launch stream), algorithmic bytes / duration against the
-                8 TB/s HBM peak; traffic = counter-measured HBM bytes per
-                launch from profiles/traffic.json while the kernels are
-                unchanged since it was taken;
+Also on the line:
+  roofline:     the headline's dominant kernel (the launch with the largest
+                share of the block's time) timed with HIP events its own
+                dispatch records, on the launch stream; algorithmic bytes /
+                duration against the 8 TB/s HBM peak; traffic = counter-
+                measured HBM bytes per launch (profiles/traffic.json) while
+                the kernels are unchanged since the counters were taken;
   cpu_baseline: the CPU oracle timed on this host on a bounded sample of the
-                same workload.
+                headline workload, single-threaded and on all cores
+                (OpenMP over tokens), with the CPU model and affinity mask.
 """
 from __future__ import annotations
 
@@ -44,20 +53,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs per decode MoE block and achieved HBM GB/s (% of peak), batch 1–64"
 MALL_L2_BYTES = 256e6 + 32e6
+HEADLINE = "tp8_b64"
+SWEEP_MOE = ("tp16_b1", "tp16_b8")
+SWEEP_DENSE = (1, 8, 64)
+# rotating weight sets per workload: bytes touched between two uses of a set
+# above 2 x (Infinity Cache + L2)
+ROTATE = {"tiny": 128, "tp16_b1": 16, "tp16_b8": 4, "tp8_b64": 4, "dense": 16, "oproj": 16}
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="tp16_b1",
-                    choices=["tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "oproj", "copy"])
+    ap.add_argument("--steps", type=int, default=20, help="timed steps per trial")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--trials", type=int, default=7)
+    ap.add_argument("--workload", default="sweep",
+                    choices=["sweep", "tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "oproj", "stream", "copy"])
     ap.add_argument("--batch", type=int, default=1, help="dense / oproj workload batch")
-    ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: enough to defeat caches)")
+    ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: the workload's default)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--kernel-steps", type=int, default=100)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-steps", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU timing (single thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused"],
                     help="moe_block schedule: one fused launch where it applies, or three launches")
@@ -67,9 +83,123 @@ def parse():
     return ap.parse_args()
 
 
-def rotations(bytes_per_step: float, cap_sets: int) -> int:
-    r = int(2 * MALL_L2_BYTES // max(bytes_per_step, 1.0)) + 1
-    return max(2, min(r, cap_sets))
+def rotations(name: str, bytes_per_step: float, args) -> int:
+    if args.rotate:
+        return args.rotate
+    need = int(2 * MALL_L2_BYTES // max(bytes_per_step, 1.0)) + 1
+    return max(2, ROTATE.get(name, 2), need)
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q))
+
+
+def trial_stats(ms_list):
+    us = [m * 1e3 for m in ms_list]
+    return dict(n=len(us), median_us=round(pct(us, 50), 3), p10_us=round(pct(us, 10), 3),
+                p90_us=round(pct(us, 90), 3), min_us=round(min(us), 3), max_us=round(max(us), 3))
+
+
+# ---------------------------------------------------------------- timing
+
+def timed_trials(step, R, args, torch):
+    """Every set once (untimed), W warm-up steps, then T trials of exactly K
+    steps (sets 0 .. K-1 mod R) between two events.  Returns ms per step of
+    each trial."""
+    for r in range(R):
+        step(r)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(args.trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / args.steps)
+    return out
+
+
+def graph_trials(step, R, args, torch, outs):
+    """Trials of graph replays: one graph per weight set, each holding one
+    step captured on a side stream.  Before timing, every graph is replayed
+    three times with plain launches of the other sets in between, and each
+    replay must reproduce the plain launch's output bits."""
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for r in range(R):
+            outs[r].fill_(0)
+            graphs[r].replay()
+            step(r + 1)               # plain launches between the replays
+            torch.cuda.synchronize()
+            if not torch.equal(outs[r].view(torch.int16), ref[r].view(torch.int16)):
+                raise RuntimeError("graph replay %d of set %d differs from the plain launch" % (rep, r))
+    res = []
+    for _ in range(args.trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / args.steps)
+    return res
+
+
+def kernel_times(step, kernel_id, n, torch, mb):
+    """Duration (ms) of each launch of one kernel over n steps (sets 0 ..
+    n-1 mod R), from HIP events the library's dispatch of that kernel
+    records on its stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    try:
+        for i in range(n):
+            mb.profile_events(kernel_id, evs[i][0], evs[i][1])
+            step(i)
+    finally:
+        mb.profile_events(kernel_id)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def stored_traffic(workload, launch):
+    """HBM bytes per launch of `launch` measured by rocprofv3 counters
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a 256 MiB
+    copy) and stored in profiles/traffic.json, or None when the library
+    sources have changed since the counters were taken."""
+    from moe_block_skinny_amd import build as hip_build
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != hip_build.source_digest():
+        return None
+    k = t.get("workloads", {}).get(workload, {}).get(launch)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------- MoE block
@@ -102,14 +232,47 @@ def moe_sets(cfg, R, seed, torch):
     return sets
 
 
-def run_moe(args, torch, mb, synth):
-    cfg = synth.CONFIGS[args.workload]
+# symbol (as a kernel trace names it) of each launch of the block
+KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel + route_finish_kernel (router mode)",
+                 "expert_up": "expert_up_kernel", "expert_down_combine": "expert_down_combine_kernel",
+                 "block": "moe_block_kernel"}
+
+
+def launch_bytes(cfg, n, esz, bias_b, route_in_up):
+    """Algorithmic HBM bytes of each launch of the block, for n distinct
+    routed experts: the weights it streams (once), the activations it must
+    read and the results it must write.  Workspace traffic between launches
+    (h and, when the gate/up launch selects, the logits; fp32) is counted as
+    the producer's output and the consumer's input; the completion counter
+    and the plan are not.  The shared expert's gate/up runs in the gate/up
+    launch when that launch also selects (small batch), else in the router
+    launch (vector shape) or as an entry of the gate/up launch (matrix)."""
+    B, d, E, k, I, Is = cfg.B, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is
+    x = B * d * esz
+    shared_up = 2 * Is * d * esz + B * Is * 4 if Is else 0
+    route = E * d * esz + x + bias_b
+    up = n * 2 * I * d * esz + x + B * k * I * 4
+    if route_in_up:
+        route += B * E * 4                      # logits out
+        up += B * E * 4 + B * k * 8 + shared_up  # logits in, ids + weights out
+    elif B <= 8:
+        route += B * k * 8 + shared_up
+    else:
+        route += B * k * 8
+        up += shared_up
+    down = n * d * I * esz + B * k * I * 4 + B * k * 4 + B * d * esz
+    if Is:
+        down += d * Is * esz + B * Is * 4
+    return {"route": route, "expert_up": up, "expert_down_combine": down}
+
+
+def run_moe(name, args, torch, mb, synth, with_roofline):
+    cfg = synth.CONFIGS[name]
     esz = 2 if cfg.dtype == "bf16" else 4
     expert_bytes = 3 * cfg.I * cfg.d * esz
     shared_bytes = 3 * cfg.Is * cfg.d * esz
     est = cfg.E * cfg.d * esz + min(cfg.B * cfg.k, cfg.E) * 0.9 * expert_bytes + shared_bytes
-    full_set = (cfg.E * cfg.d + 3 * cfg.E * cfg.I * cfg.d + 3 * cfg.Is * cfg.d) * esz
-    R = args.rotate or rotations(est, cap_sets=max(2, int(60e9 // full_set)))
+    R = rotations(name, est, args)
     sets = moe_sets(cfg, R, args.seed, torch)
     dt = mb.DT_BF16 if cfg.dtype == "bf16" else mb.DT_F32
     ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, dt, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
@@ -122,11 +285,12 @@ def run_moe(args, torch, mb, synth):
 
     mb.set_block_schedule(args.schedule)
     if args.graph:
-        ms = graph_loop(step, R, args, torch, [s["out"] for s in sets])
+        ms = graph_trials(step, R, args, torch, [s["out"] for s in sets])
     else:
-        ms = timed_loop(step, args, torch)
-    fused = "fused" in mb.last_variant()
-    route_in_up = "top-k/plan" in mb.last_variant()
+        ms = timed_trials(step, R, args, torch)
+    variant = mb.last_variant()
+    fused = "fused" in variant
+    route_in_up = "top-k/plan" in variant
     # algorithmic bytes per set: every selected expert's weights once, the
     # router and shared expert, x (and bias) read once, out written once
     per_set = []
@@ -141,152 +305,153 @@ def run_moe(args, torch, mb, synth):
     launches = ((("block", mb.KERNEL_BLOCK),) if fused else
                 (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
                  ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)))
-    for name, kid in launches:
-        kern[name] = kernel_times(step, kid, args, torch, mb)
-        # the profiled launches run sets warmup + steps + i (see kernel_times)
-        sel = (lambda i: per_set[i][1]) if fused else (lambda i: per_set[i][2][name])
-        kbytes[name] = [sel((args.warmup + args.steps + i) % R) for i in range(len(kern[name]))]
-    # the dominant kernel: the largest share of the block's time
-    dom = max(kern, key=lambda k: sum(kern[k]))
-    durs = kern[dom]
-    achieved = sum(kbytes[dom]) / (sum(durs) * 1e-3) / 1e9         # GB/s
-    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=stored_traffic(cfg.name, dom),
-                kernel=KERNEL_SYMBOL[dom], bytes_per_launch=round(sum(kbytes[dom]) / len(durs)),
-                avg_us=round(sum(durs) / len(durs) * 1e3, 3))
+    nk = max(1, args.kernel_steps)
+    for lname, kid in launches:
+        kern[lname] = kernel_times(step, kid, nk, torch, mb)
+        sel = (lambda i: per_set[i][1]) if fused else (lambda i, l=lname: per_set[i][2][l])
+        kbytes[lname] = [sel(i % R) for i in range(nk)]
     per_kernel = {k: dict(us=round(sum(v) / len(v) * 1e3, 3),
-                          gbs=round(sum(kbytes[k]) / (sum(v) * 1e-3) / 1e9, 1)) for k, v in kern.items()}
-    us = ms * 1e3
+                          gbs=round(sum(kbytes[k]) / (sum(v) * 1e-3) / 1e9, 1),
+                          frac=round(sum(kbytes[k]) / (sum(v) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+                  for k, v in kern.items()}
+    st = trial_stats(ms)
+    us = st["median_us"]
     gbs = avg_bytes / (us * 1e-6) / 1e9
-    config = dict(workload="%s: decode MoE block, one TP weight shard, B=%d, d=%d, E=%d, top-%d, "
-                           "I=%d, Is=%d, %s routing" % (cfg.name, cfg.B, cfg.d, cfg.E, cfg.k, cfg.I,
-                                                         cfg.Is, cfg.routing),
-                  B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is, rotate=R,
-                  distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
-                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
-                  kernels=per_kernel,
-                  launch="graph replay" if args.graph else "plain launches",
-                  variant=mb.last_variant())
-    cpu = None if args.no_cpu_baseline else cpu_baseline_moe(cfg, args)
-    return us, ms, cfg.dtype, config, roof, cpu
-
-
-# symbol (as a kernel trace names it) of each launch of the block
-KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel (router mode)", "expert_up": "expert_up_kernel",
-                 "expert_down_combine": "expert_down_combine_kernel", "block": "moe_block_kernel"}
-
-
-def launch_bytes(cfg, n, esz, bias_b, route_in_up):
-    """Algorithmic HBM bytes of each launch of the block, for n distinct
-    routed experts: the weights it streams (once), the activations it must
-    read and the results it must write.  Workspace traffic between launches
-    (h and, when the gate/up launch selects, the logits; fp32) is counted as
-    the producer's output and the consumer's input; the completion counter
-    and the plan are not.  The shared expert's gate/up runs in the gate/up
-    launch when that launch also selects (small batch), else in the router
-    launch."""
-    B, d, E, k, I, Is = cfg.B, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is
-    x = B * d * esz
-    shared_up = 2 * Is * d * esz + B * Is * 4 if Is else 0
-    route = E * d * esz + x + bias_b
-    up = n * 2 * I * d * esz + x + B * k * I * 4
-    if route_in_up:
-        route += B * E * 4                      # logits out
-        up += B * E * 4 + B * k * 8 + shared_up  # logits in, ids + weights out
-    else:
-        route += B * k * 8 + shared_up
-    down = n * d * I * esz + B * k * I * 4 + B * k * 4 + B * d * esz
-    if Is:
-        down += d * Is * esz + B * Is * 4
-    return {"route": route, "expert_up": up, "expert_down_combine": down}
+    entry = dict(workload="%s: decode MoE block, one TP weight shard, B=%d, d=%d, E=%d, top-%d, "
+                          "I=%d, Is=%d, %s routing" % (cfg.name, cfg.B, cfg.d, cfg.E, cfg.k, cfg.I,
+                                                        cfg.Is, cfg.routing),
+                 B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is, rotate=R,
+                 us=us, trials=st,
+                 distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
+                 gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                 kernels=per_kernel,
+                 launch="graph replay" if args.graph else "plain launches",
+                 variant=variant)
+    roof = None
+    if with_roofline:
+        dom = max(kern, key=lambda k: sum(kern[k]))
+        durs = kern[dom]
+        achieved = sum(kbytes[dom]) / (sum(durs) * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=stored_traffic(cfg.name, dom),
+                    kernel=KERNEL_SYMBOL[dom], launch=dom, bytes_per_launch=round(sum(kbytes[dom]) / len(durs)),
+                    avg_us=round(sum(durs) / len(durs) * 1e3, 3), launches_timed=len(durs))
+    del sets, ws
+    torch.cuda.empty_cache()
+    return entry, roof, cfg
 
 
 # ---------------------------------------------------------------- dense
 
-def run_dense(args, torch, mb, synth):
-    B, N, K = args.batch, synth.DENSE_N, synth.DENSE_K
+def run_gemm(kind, B, args, torch, mb, synth, with_roofline):
+    """The attention input projection (kind "dense": Y = X . W^T, X [B][7168],
+    W [3072][7168]) or the output projection with the residual added (kind
+    "oproj": Y = X . W^T + R, X [B][3072], W [7168][3072], R [B][7168]), bf16."""
+    if kind == "dense":
+        N, K = synth.DENSE_N, synth.DENSE_K
+    else:
+        N, K = synth.OPROJ_N, synth.OPROJ_K
     wbytes = N * K * 2
-    R = args.rotate or rotations(wbytes, cap_sets=64)
+    R = rotations(kind, wbytes, args)
     sets = []
     for r in range(R):
         g = torch.Generator(device="cuda").manual_seed(args.seed * 1000003 + r)
-        sets.append(dict(X=torch.randn((B, K), generator=g, device="cuda", dtype=torch.bfloat16),
-                         W=(torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * K ** -0.5).to(torch.bfloat16),
-                         Y=torch.empty((B, N), device="cuda", dtype=torch.bfloat16)))
+        s = dict(X=torch.randn((B, K), generator=g, device="cuda", dtype=torch.bfloat16),
+                 W=(torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * K ** -0.5).to(torch.bfloat16),
+                 Y=torch.empty((B, N), device="cuda", dtype=torch.bfloat16))
+        if kind == "oproj":
+            s["R"] = torch.randn((B, N), generator=g, device="cuda", dtype=torch.bfloat16)
+        sets.append(s)
     ws = mb.workspace(mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K))
 
     def step(i):
         s = sets[i % R]
-        mb.skinny_gemm(s["X"], s["W"], s["Y"], ws)
+        if kind == "dense":
+            mb.skinny_gemm(s["X"], s["W"], s["Y"], ws)
+        else:
+            mb.skinny_gemm_residual(s["X"], s["W"], s["R"], s["Y"], ws)
 
-    ms = timed_loop(step, args, torch)
-    nbytes = wbytes + B * K * 2 + B * N * 2
-    durs = kernel_times(step, mb.KERNEL_SKINNY, args, torch, mb)
-    achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
-    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=stored_traffic("dense_b%d" % B, "skinny_gemm"),
-                kernel="skinny_valu_kernel / skinny_mfma_kernel",
-                bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
-    us = ms * 1e3
-    config = dict(workload="dense skinny GEMM (attention input projection): Y[%d x %d] = "
-                           "X[%d x %d] . W[%d x %d]^T, bf16" % (B, N, B, K, N, K),
-                  B=B, N=N, K=K, rotate=R, algorithmic_bytes=nbytes,
-                  gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
-                  hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  variant=mb.last_variant())
-    cpu = None if args.no_cpu_baseline else cpu_baseline_dense(B, N, K, args)
-    return us, ms, "bf16", config, roof, cpu
-
-
-# ---------------------------------------------------------------- oproj
-
-def run_oproj(args, torch, mb, synth):
-    """Attention output projection with the residual added:
-    Y = X . W^T + R, X [B][3072], W [7168][3072], R and Y [B][7168], bf16."""
-    B, N, K = args.batch, synth.OPROJ_N, synth.OPROJ_K
-    wbytes = N * K * 2
-    R_sets = args.rotate or rotations(wbytes, cap_sets=64)
-    sets = []
-    for r in range(R_sets):
-        g = torch.Generator(device="cuda").manual_seed(args.seed * 1000003 + r)
-        sets.append(dict(X=torch.randn((B, K), generator=g, device="cuda", dtype=torch.bfloat16),
-                         W=(torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * K ** -0.5).to(torch.bfloat16),
-                         R=torch.randn((B, N), generator=g, device="cuda", dtype=torch.bfloat16),
-                         Y=torch.empty((B, N), device="cuda", dtype=torch.bfloat16)))
-    ws = mb.workspace(mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K))
-
-    def step(i):
-        s = sets[i % R_sets]
-        mb.skinny_gemm_residual(s["X"], s["W"], s["R"], s["Y"], ws)
-
-    ms = timed_loop(step, args, torch)
-    nbytes = wbytes + B * K * 2 + 2 * B * N * 2
-    durs = kernel_times(step, mb.KERNEL_SKINNY, args, torch, mb)
-    achieved = nbytes / (sum(durs) / len(durs) * 1e-3) / 1e9
-    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=stored_traffic("oproj_b%d" % B, "skinny_gemm"),
-                kernel="skinny_valu_kernel / skinny_mfma_kernel",
-                bytes_per_launch=nbytes, avg_us=round(sum(durs) / len(durs) * 1e3, 3))
-    us = ms * 1e3
-    config = dict(workload="attention output projection + residual: Y[%d x %d] = X[%d x %d] . W[%d x %d]^T "
-                           "+ R, bf16" % (B, N, B, K, N, K),
-                  B=B, N=N, K=K, rotate=R_sets, algorithmic_bytes=nbytes,
-                  gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
-                  hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  variant=mb.last_variant())
-    cpu = None if args.no_cpu_baseline else cpu_baseline_oproj(B, args)
-    return us, ms, "bf16", config, roof, cpu
+    ms = timed_trials(step, R, args, torch)
+    variant = mb.last_variant()
+    nbytes = wbytes + B * K * 2 + B * N * 2 * (2 if kind == "oproj" else 1)
+    durs = kernel_times(step, mb.KERNEL_SKINNY, max(1, args.kernel_steps), torch, mb)
+    kus = sum(durs) / len(durs) * 1e3
+    st = trial_stats(ms)
+    us = st["median_us"]
+    what = ("dense skinny GEMM (attention input projection): Y[%d x %d] = X[%d x %d] . W[%d x %d]^T, bf16"
+            if kind == "dense" else
+            "attention output projection + residual: Y[%d x %d] = X[%d x %d] . W[%d x %d]^T + R, bf16")
+    entry = dict(workload=what % (B, N, B, K, N, K), B=B, N=N, K=K, rotate=R, us=us, trials=st,
+                 algorithmic_bytes=nbytes, gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                 hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 kernel_us=round(kus, 3), kernel_gbs=round(nbytes / (kus * 1e-6) / 1e9, 1),
+                 variant=variant)
+    roof = None
+    if with_roofline:
+        achieved = nbytes / (kus * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=stored_traffic("%s_b%d" % (kind, B), "skinny_gemm"),
+                    kernel="skinny_valu_kernel / skinny_mfma_kernel", launch="skinny_gemm",
+                    bytes_per_launch=nbytes, avg_us=round(kus, 3), launches_timed=len(durs))
+    del sets, ws
+    torch.cuda.empty_cache()
+    return entry, roof
 
 
-# ---------------------------------------------------------------- copy
+# ---------------------------------------------------------------- yardsticks
+
+def run_stream(args, torch, mb):
+    """The read-only streaming yardstick (moe_stream_read: 128-bit
+    nontemporal loads, one contiguous 1 KB per wave instruction): 4 rotating
+    1 GiB buffers (the rate away from launch overheads), and 16 rotating
+    44 MB buffers (the dense product's weight size: the rate one launch of
+    that size reaches, its fixed launch latency included).  Best grid of a
+    few; the XOR of the sink is checked against the buffer's."""
+    out = {}
+    for label, nbytes, R in (("1gib", 1 << 30, 4), ("44mb", 3072 * 7168 * 2, 16)):
+        bufs = []
+        for r in range(R):
+            g = torch.Generator(device="cuda").manual_seed(77 + r)
+            bufs.append(torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, device="cuda",
+                                      dtype=torch.int32))
+        best = None
+        for wg in (512, 1024, 2048):
+            sink = torch.empty(wg, dtype=torch.int32, device="cuda")
+
+            def step(i, sink=sink):
+                mb.stream_read(bufs[i % R], sink)
+
+            ms = timed_trials(step, R, args, torch)
+            st = trial_stats(ms)
+            gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+            if best is None or gbs > best["gbs"]:
+                best = dict(bytes=nbytes, rotate=R, workgroups=wg, us=st["median_us"], trials=st,
+                            gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        # every word read: XOR of the sink == XOR of the buffer
+        sink = torch.empty(best["workgroups"], dtype=torch.int32, device="cuda")
+        mb.stream_read(bufs[0], sink)
+        best["checked"] = _xor_all(sink, torch) == _xor_all(bufs[0], torch)
+        out[label] = best
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+def _xor_all(t, torch):
+    """XOR of every element of an int32 tensor: pairwise halving, exact."""
+    t = t.reshape(-1)
+    while t.numel() > 1:
+        if t.numel() % 2:
+            t = torch.cat([t, torch.zeros(1, dtype=t.dtype, device=t.device)])
+        t = torch.bitwise_xor(t[0::2], t[1::2])
+    return int(t[0].item())
+
 
 def run_copy(args, torch):
-    """A plain device copy of known size (256 MiB), as the yardstick for the
-    HBM byte counters (FETCH_SIZE / WRITE_SIZE) and for achievable
-    bandwidth on this GPU: 2 x 256 MiB of compulsory traffic per copy."""
+    """A plain device copy of known size (256 MiB), the yardstick for the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE): 2 x 256 MiB of traffic per copy."""
     n = 256 << 20
     R = 4
     src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(r) for r in range(R)]
@@ -295,110 +460,48 @@ def run_copy(args, torch):
     def step(i):
         dst.copy_(src[i % R])
 
-    ms = timed_loop(step, args, torch)
-    us = ms * 1e3
-    gbs = 2 * n / (us * 1e-6) / 1e9
-    config = dict(workload="device copy of 256 MiB (read + write)", bytes=2 * n, rotate=R,
-                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
-    roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="copy")
-    return us, ms, "u8", config, roof, None
-
-
-# ---------------------------------------------------------------- traffic
-
-def stored_traffic(workload, launch):
-    """HBM bytes per launch of `launch` (route, expert_up, ...) measured by rocprofv3 counters
-    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a 256 MiB copy)
-    and stored in profiles/traffic.json, or None when the library sources have
-    changed since the counters were taken."""
-    from moe_block_skinny_amd import build as hip_build
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("source_digest") != hip_build.source_digest():
-        return None
-    k = t.get("workloads", {}).get(workload, {}).get(launch)
-    return None if k is None else k.get("bytes_per_launch")
-
-
-# ---------------------------------------------------------------- timing
-
-def timed_loop(step, args, torch):
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / args.steps
-
-
-def graph_loop(step, R, args, torch, outs):
-    """Per-step time of graph replays: one graph per weight set, each holding
-    one step captured on a side stream.  Before timing, every graph is
-    replayed three times with plain launches of the other sets in between,
-    and each replay must reproduce the plain launch's output bits."""
-    for i in range(max(args.warmup, R)):
-        step(i)
-    torch.cuda.synchronize()
-    ref = [o.clone() for o in outs]
-    graphs = []
-    side = torch.cuda.Stream()
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            step(r)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        for r in range(R):
-            outs[r].fill_(0)
-            graphs[r].replay()
-            step(r + 1)               # plain launches between the replays
-            torch.cuda.synchronize()
-            if not torch.equal(outs[r].view(torch.int16), ref[r].view(torch.int16)):
-                raise RuntimeError("graph replay %d of set %d differs from the plain launch" % (rep, r))
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / args.steps
-
-
-def kernel_times(step, kernel_id, args, torch, mb):
-    """Duration (ms) of each launch of one kernel over kernel-steps steps,
-    from HIP events the library records around that launch on its stream."""
-    n = max(1, args.kernel_steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in evs:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    try:
-        for i in range(n):
-            mb.profile_events(kernel_id, evs[i][0], evs[i][1])
-            step(args.warmup + args.steps + i)
-    finally:
-        mb.profile_events(kernel_id)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    ms = timed_trials(step, R, args, torch)
+    st = trial_stats(ms)
+    gbs = 2 * n / (st["median_us"] * 1e-6) / 1e9
+    return dict(workload="device copy of 256 MiB (read + write)", bytes=2 * n, rotate=R, us=st["median_us"],
+                trials=st, gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
 
 
 # ---------------------------------------------------------------- CPU oracle
 
-def cpu_baseline_moe(cfg, args):
-    import numpy as np
+def cpu_info():
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = list(range(os.cpu_count() or 1))
+    return model, aff
+
+
+def _ranges(cpus):
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(str(cpus[i]) if i == j else "%d-%d" % (cpus[i], cpus[j]))
+        i = j + 1
+    return ",".join(out)
+
+
+def cpu_baseline(cfg, args):
+    """The oracle as it stands on the host: whole blocks of the headline
+    workload (seed 0, only the selected experts' weights drawn), repeated
+    until --cpu-seconds have passed, once with the plain single-thread build
+    and once with the OpenMP build (tokens on every core it may use)."""
     from moe_block_skinny_amd import synth
     from oracle import oracle as orc
 
@@ -409,52 +512,50 @@ def cpu_baseline_moe(cfg, args):
     W13 = [synth.expert_w13(cfg, args.seed, e) if e in touched else None for e in range(cfg.E)]
     W2 = [synth.expert_w2(cfg, args.seed, e) if e in touched else None for e in range(cfg.E)]
     Ws13, Ws2 = synth.shared_w13(cfg, args.seed), synth.shared_w2(cfg, args.seed)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        orc.moe_block(X, Wr, cfg.k, W13, W2, Ws13, Ws2, bias, ld)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
-                sample="%d blocks of the %s workload (seed %d, %d distinct experts), fp64 C oracle, "
-                       "one thread, %.1f s" % (n, cfg.name, args.seed, len(touched), el),
-                cpu=platform.processor() or platform.machine(), host_cpus=os.cpu_count())
+    res = {}
+    for par in (False, True):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            orc.moe_block(X, Wr, cfg.k, W13, W2, Ws13, Ws2, bias, ld, parallel=par)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res[par] = (el / n * 1e6, n, el, orc.threads(par))
+    model, aff = cpu_info()
+    (us1, n1, el1, _), (usp, npar, elp, thr) = res[False], res[True]
+    return dict(value=round(usp, 1), unit="µs", cores=thr, kind="oracle",
+                sample="%d blocks of the %s workload (seed %d, B=%d, %d distinct experts) on %d threads "
+                       "(OpenMP over tokens) in %.1f s; single-thread: %d blocks in %.1f s; fp64 C oracle"
+                       % (npar, cfg.name, args.seed, cfg.B, len(touched), thr, elp, n1, el1),
+                single_thread_us=round(us1, 1), all_cores_us=round(usp, 1), threads=thr,
+                cpu_model=model, affinity=_ranges(aff), affinity_cpus=len(aff), host_cpus=os.cpu_count())
 
 
-def cpu_baseline_dense(B, N, K, args):
+def cpu_baseline_gemm(kind, B, args):
     from moe_block_skinny_amd import synth
     from oracle import oracle as orc
 
-    X, W = synth.dense_x(B), synth.dense_w()
+    if kind == "dense":
+        X, W = synth.dense_x(B), synth.dense_w()
+        f = lambda: orc.skinny_gemm(X, W)
+    else:
+        X, W, R = synth.oproj_x(B), synth.oproj_w(), synth.oproj_r(B)
+        f = lambda: orc.skinny_gemm_residual(X, W, R)
     n, t0 = 0, time.perf_counter()
     while True:
-        orc.skinny_gemm(X, W)
+        f()
         n += 1
         el = time.perf_counter() - t0
         if el >= args.cpu_seconds:
             break
+    model, aff = cpu_info()
     return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
-                sample="%d skinny GEMMs at B=%d, fp64 C oracle, one thread, %.1f s" % (n, B, el),
-                host_cpus=os.cpu_count())
+                sample="%d %s products at B=%d, fp64 C oracle, one thread, %.1f s" % (n, kind, B, el),
+                cpu_model=model, affinity=_ranges(aff), host_cpus=os.cpu_count())
 
 
-def cpu_baseline_oproj(B, args):
-    from moe_block_skinny_amd import synth
-    from oracle import oracle as orc
-
-    X, W, R = synth.oproj_x(B), synth.oproj_w(), synth.oproj_r(B)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        orc.skinny_gemm_residual(X, W, R)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    return dict(value=round(el / n * 1e6, 1), unit="µs", cores=1, kind="oracle",
-                sample="%d output projections with residual at B=%d, fp64 C oracle, one thread, %.1f s"
-                       % (n, B, el), host_cpus=os.cpu_count())
-
+# ---------------------------------------------------------------- main
 
 def main():
     args = parse()
@@ -470,18 +571,62 @@ def main():
     from moe_block_skinny_amd import synth
 
     torch.cuda.set_device(0)
-    if args.workload == "copy":
-        us, ms, dtype, config, roof, cpu = run_copy(args, torch)
-    elif args.workload == "dense":
-        us, ms, dtype, config, roof, cpu = run_dense(args, torch, mb, synth)
-    elif args.workload == "oproj":
-        us, ms, dtype, config, roof, cpu = run_oproj(args, torch, mb, synth)
+    t_start = time.perf_counter()
+    cpu = None
+    dtype = "bf16"
+    if args.workload in ("sweep",) + tuple(synth.CONFIGS):
+        head = HEADLINE if args.workload == "sweep" else args.workload
+        entry, roof, cfg = run_moe(head, args, torch, mb, synth, True)
+        dtype = cfg.dtype
+        print("[bench] %s: %.3f us (p10 %.3f, p90 %.3f)" % (head, entry["us"], entry["trials"]["p10_us"],
+                                                          entry["trials"]["p90_us"]), file=sys.stderr, flush=True)
+        config = dict(entry)
+        if args.workload == "sweep":
+            sweep = {}
+            for name in SWEEP_MOE:
+                e, _, _ = run_moe(name, args, torch, mb, synth, False)
+                sweep[name] = e
+                print("[bench] %s: %.3f us" % (name, e["us"]), file=sys.stderr, flush=True)
+            for B in SWEEP_DENSE:
+                e, _ = run_gemm("dense", B, args, torch, mb, synth, False)
+                sweep["dense_b%d" % B] = e
+                print("[bench] dense B=%d: %.3f us" % (B, e["us"]), file=sys.stderr, flush=True)
+            config["sweep"] = sweep
+            stream = run_stream(args, torch, mb)
+            config["stream"] = stream
+            ref = stream["1gib"]["gbs"]
+            config["stream_frac"] = round(config["gbs"] / ref, 4)
+            for e in sweep.values():
+                e["stream_frac"] = round(e["gbs"] / ref, 4)
+            print("[bench] stream 1 GiB: %.1f GB/s" % ref, file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(cfg, args)
+        value = entry["us"]
+    elif args.workload in ("dense", "oproj"):
+        entry, roof = run_gemm(args.workload, args.batch, args, torch, mb, synth, True)
+        config = dict(entry)
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline_gemm(args.workload, args.batch, args)
+        value = entry["us"]
+    elif args.workload == "stream":
+        st = run_stream(args, torch, mb)
+        config = dict(workload="read-only 128-bit streaming yardstick (moe_stream_read)", stream=st)
+        e = st["1gib"]
+        roof = dict(bound="hbm", achieved=e["gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=e["hbm_frac"],
+                    traffic=None, kernel="stream_read_kernel", launch="stream", bytes_per_launch=e["bytes"],
+                    avg_us=e["us"])
+        value, dtype = e["us"], "u32"
     else:
-        us, ms, dtype, config, roof, cpu = run_moe(args, torch, mb, synth)
-    line = dict(metric=METRIC, value=round(us, 3), unit="µs", n_gpus=1, steps=args.steps,
-                warmup=args.warmup, ms_per_step=round(ms, 6), higher_is_better=False,
-                scaling="weak", vs_baseline=None, dtype=dtype, data="synthetic", config=config,
-                roofline=roof, cpu_baseline=cpu)
+        entry = run_copy(args, torch)
+        config = dict(entry)
+        roof = dict(bound="hbm", achieved=entry["gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=entry["hbm_frac"],
+                    traffic=None, kernel="copy", launch="copy", bytes_per_launch=entry["bytes"], avg_us=entry["us"])
+        value, dtype = entry["us"], "u8"
+    config["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
+    line = dict(metric=METRIC, value=round(value, 3), unit="µs", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, trials=args.trials, ms_per_step=round(value / 1e3, 6),
+                higher_is_better=False, scaling="weak", vs_baseline=None, dtype=dtype, data="synthetic",
+                config=config, roofline=roof, cpu_baseline=cpu)
     print(json.dumps(line, ensure_ascii=False), flush=True)
 
 

@@ -151,7 +151,8 @@ typedef enum {
   MOE_KERNEL_EXPERT_DOWN = 2,  /* expert down projection */
   MOE_KERNEL_COMBINE = 3,      /* weighted combine */
   MOE_KERNEL_SKINNY = 4,       /* dense skinny product */
-  MOE_KERNEL_BLOCK = 5         /* the whole block in one launch (moe_block) */
+  MOE_KERNEL_BLOCK = 5,        /* the whole block in one launch (moe_block) */
+  MOE_KERNEL_STREAM = 6        /* the read-only streaming yardstick (moe_stream_read) */
 } moe_kernel_t;
 
 /* Profiling hook (for timing one kernel with HIP events on the stream it is
@@ -162,6 +163,26 @@ typedef enum {
  * start_event / stop_event are hipEvent_t handles owned by the caller.
  * Returns MOE_EINVAL for an unknown kernel or only one NULL event. */
 moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event);
+
+/* Byte offset in ws of the fused schedule's barrier status word (a uint32,
+ * inside the workspace header, the same for every op and size).  It reads 0
+ * unless a grid-wide barrier of a fused moe_block call gave up waiting (the
+ * call's outputs are then invalid); no call clears it, moe_workspace_init
+ * does.  The fused launch is cooperative, so the runtime refuses it when the
+ * grid cannot be resident at once, and the word is not expected to move. */
+size_t moe_workspace_status_offset(void);
+
+/* Measurement yardstick, not part of the block (WRITEUP part 1 §4: small-
+ * batch decode is bound by reading weights): reads `bytes` of src (device
+ * memory, 16-byte aligned, bytes a positive multiple of 16) with 128-bit
+ * nontemporal loads -- each wave instruction one contiguous 1 KB, the access
+ * of the weight streams -- in `workgroups` workgroups of 256 threads, each
+ * over one contiguous slice, and stores the XOR of slice w's 32-bit words to
+ * sink[w] (uint32 [workgroups], device memory), so the XOR of all of sink
+ * equals the XOR of every word of src.  Its rate is the measured read
+ * ceiling the kernels are compared with.  1 <= workgroups <= 65536;
+ * MOE_EINVAL otherwise. */
+moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 /* Zero-fill a workspace (with a kernel, so it may be captured in a graph). */
 moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
@@ -227,7 +248,11 @@ moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const 
                             const void* Ws13, const void* Ws2, float* Yslot, void* ws,
                             size_t ws_bytes, void* stream);
 
-/* Weighted combine:
+/* Weighted combine (WRITEUP part 1 §3: each token's output is the sum of its
+ * routed experts' outputs and the shared expert's, which runs for every
+ * token; the routed outputs are weighted by the gate weights of moe_route, as
+ * the block's workload definitions state -- softmax over the router logits,
+ * renormalised over the top-k, no extra scale):
  *   out[t] = sum_{j ascending} topk_w[t][j] * Yslot[t][j] + (has_shared ?
  *   Yslot[t][k] : 0), accumulated in fp32 in that order, stored as dtype
  *   (bf16: round to nearest-even).  Yslot fp32 [B][k+1][d], topk_w fp32
@@ -235,7 +260,11 @@ moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const 
 moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, const float* topk_w,
                          int has_shared, void* out, void* stream);
 
-/* The whole block, every intermediate in ws.
+/* The whole block, every intermediate in ws (WRITEUP part 1 §3: router
+ * scores, then the routed experts, and a shared expert for every token, its
+ * output added to the routed ones; AREX "每层从 23 个内核减到 13 个": the
+ * block's stages in fewer kernels; the arithmetic is that of moe_route,
+ * moe_expert_ffn and moe_combine above).
  * Small batch on the vector shape with short expert rows (B*k <= 64, I and
  * Is at most 16 vector chunks -- 128 bf16, 64 fp32), on request ONE launch
  * (schedule "fused"): one 16-wave workgroup per compute unit, all resident,

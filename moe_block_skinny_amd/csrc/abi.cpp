@@ -40,7 +40,8 @@ struct ProfileHook {
 
 static_assert((int)K_ROUTE == (int)MOE_KERNEL_ROUTE && (int)K_EXPERT_UP == (int)MOE_KERNEL_EXPERT_UP &&
                   (int)K_EXPERT_DOWN == (int)MOE_KERNEL_EXPERT_DOWN && (int)K_COMBINE == (int)MOE_KERNEL_COMBINE &&
-                  (int)K_SKINNY == (int)MOE_KERNEL_SKINNY && (int)K_BLOCK == (int)MOE_KERNEL_BLOCK,
+                  (int)K_SKINNY == (int)MOE_KERNEL_SKINNY && (int)K_BLOCK == (int)MOE_KERNEL_BLOCK &&
+                  (int)K_STREAM == (int)MOE_KERNEL_STREAM,
               "kernel ids");
 
 moe_status_t fail(moe_status_t s, const char* fmt, ...) {
@@ -398,7 +399,7 @@ moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event)
     g_prof.start = g_prof.stop = nullptr;
     return MOE_OK;
   }
-  if (kernel < MOE_KERNEL_ROUTE || kernel > MOE_KERNEL_BLOCK) return fail(MOE_EINVAL, "unknown kernel %d", kernel);
+  if (kernel < MOE_KERNEL_ROUTE || kernel > MOE_KERNEL_STREAM) return fail(MOE_EINVAL, "unknown kernel %d", kernel);
   if (!start_event || !stop_event) return fail(MOE_EINVAL, "both events or neither");
   g_prof.kernel = kernel;
   g_prof.start = reinterpret_cast<hipEvent_t>(start_event);
@@ -444,6 +445,19 @@ size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I,
       return block_ws(bf16, B, d, E, k, I, Is).total;
   }
   return 0;
+}
+
+size_t moe_workspace_status_offset(void) {
+  return kSyncOff + (size_t)(2 + 2 * kBlockMaxGrid) * kFlagStride * 4;
+}
+
+moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+  g_err[0] = 0;
+  if (!aligned(src) || !aligned(sink)) return fail(MOE_EINVAL, "src or sink null or misaligned");
+  if (bytes == 0 || bytes % 16) return fail(MOE_EINVAL, "bytes=%zu not a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > 65536) return fail(MOE_EINVAL, "workgroups=%d outside 1..65536", workgroups);
+  return hip_status(launch_stream_read(src, bytes, sink, workgroups, reinterpret_cast<hipStream_t>(stream)),
+                    "stream read launch");
 }
 
 moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {

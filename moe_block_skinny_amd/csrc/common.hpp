@@ -381,6 +381,16 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
          (uint32_t)__builtin_amdgcn_readlane((int)v, 32) | (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
 }
 
+// Wave-wide bitwise XOR, uniform result (the same DPP steps as wave_max_u32).
+__device__ __forceinline__ uint32_t wave_xor_u32(uint32_t v) {
+  v ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+  v ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);
+  v ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false);
+  v ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) ^ (uint32_t)__builtin_amdgcn_readlane((int)v, 16) ^
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) ^ (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (classic DPP scan:
 // row_shr 1, 2, 4, 8, then row_bcast15 and row_bcast31 carry row totals).
 __device__ __forceinline__ int wave_incl_scan(int v) {

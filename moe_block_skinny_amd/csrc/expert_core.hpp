@@ -51,8 +51,6 @@ __device__ __forceinline__ PlanView plan_view(const ExpertLaunch& a, const int32
   return p;
 }
 
-// Copy the plan into LDS with the whole workgroup (one coalesced pass) and
-// return a view of it.  Ends with a barrier.
 // Copy n words from global memory to LDS with the whole workgroup: the
 // first 8 per thread are all requested before any is stored, so they cost
 // one memory round trip (a plain loop waits for each load before the next,
@@ -74,6 +72,8 @@ __device__ __forceinline__ void stage_words(int32_t* dst, const int32_t* src, in
   for (int i = threadIdx.x + R * nt; i < n; i += nt) dst[i] = src[i];
 }
 
+// Copy the plan into LDS with the whole workgroup (one coalesced pass) and
+// return a view of it.  Ends with a barrier.
 __device__ __forceinline__ PlanView stage_plan(const ExpertLaunch& a, int32_t* s_plan) {
   const int nslot = a.B * a.k;
   const int maxa = nslot < a.E ? nslot : a.E;

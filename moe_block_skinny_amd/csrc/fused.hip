@@ -209,13 +209,19 @@ hipError_t launch_moe_block_fused(BlockLaunch& f, hipStream_t st, char* desc, si
   const size_t lds = block_lds(f.ex, rt);
   void* k = f.ex.bf16 ? block_kernel_for<bf16_t>(f.ex.B) : block_kernel_for<float>(f.ex.B);
   const dim3 grid(G), block(kBlockWaves * 64);
+  // A cooperative launch: the runtime refuses it unless every workgroup of
+  // the grid can be resident at once, which the two grid-wide barriers need
+  // (a workgroup that never started would leave the others polling until
+  // the spin limit, then reading logits and h that were never written).
+  // With the profiling hook armed the events are recorded on the stream
+  // around the launch (a cooperative dispatch takes no events itself).
   hipEvent_t e0 = nullptr, e1 = nullptr;
   void* args[] = {&f};
-  hipError_t err;
-  if (profile_events_for(K_BLOCK, &e0, &e1))
-    err = hipExtLaunchKernel(k, grid, block, args, lds, st, e0, e1, 0);
-  else
-    err = hipLaunchKernel(k, grid, block, args, lds, st);
+  const bool prof = profile_events_for(K_BLOCK, &e0, &e1);
+  hipError_t err = hipSuccess;
+  if (prof) err = hipEventRecord(e0, st);
+  if (err == hipSuccess) err = hipLaunchCooperativeKernel(k, grid, block, args, (unsigned)lds, st);
+  if (err == hipSuccess && prof) err = hipEventRecord(e1, st);
   if (desc)
     snprintf(desc, desc_len, "fused grid=%d waves/wg=%d router tasks=%d shared tasks=%d rows/wg=%d", G, kBlockWaves,
              f.router_tasks, f.shared_tasks, rt);

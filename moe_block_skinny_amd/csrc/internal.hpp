@@ -134,7 +134,8 @@ struct CombineLaunch {
 
 // Kernel ids of the profiling hook (same values as the public moe_kernel_t).
 enum KernelId {
-  K_ROUTE = 0, K_EXPERT_UP = 1, K_EXPERT_DOWN = 2, K_COMBINE = 3, K_SKINNY = 4, K_BLOCK = 5, K_NONE = -1
+  K_ROUTE = 0, K_EXPERT_UP = 1, K_EXPERT_DOWN = 2, K_COMBINE = 3, K_SKINNY = 4, K_BLOCK = 5, K_STREAM = 6,
+  K_NONE = -1
 };
 
 // Events armed for kernel `id` by moe_profile_events (abi.cpp), if any.
@@ -158,6 +159,9 @@ hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc,
 hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// Read-only streaming yardstick (stream.hip): `workgroups` workgroups read
+// bytes (a multiple of 16) of src; sink[w] = XOR of slice w's 32-bit words.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
 // Fused block: the workgroups it would launch (0: the fused kernel cannot
 // hold the whole grid resident, so it must not be used), and the launch.
 int moe_block_fused_grid(const ExpertLaunch& ex, int bf16, int B);

@@ -44,6 +44,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_DT_F32 0
 #define ORACLE_DT_BF16 1
@@ -100,6 +103,7 @@ void oracle_skinny_gemm_residual(int dt, int B, int N, int K, const void *X,
 void oracle_router_logits(int dt, int B, int d, int E, const void *X,
                           const void *Wr, const float *bias, int bias_ld,
                           double *logits) {
+#pragma omp parallel for schedule(dynamic, 1)
   for (int t = 0; t < B; ++t)
     for (int e = 0; e < E; ++e) {
       double l = dot(X, (size_t)t * d, Wr, (size_t)e * d, dt, d);
@@ -207,36 +211,28 @@ void oracle_expert(int dt, int d, int I, const void *X, size_t x_off,
   free(hh);
 }
 
-/* Whole block.  W13e / W2e are arrays of E pointers, one per expert
- * ([2I][d] and [d][I]); an expert no token selects may be NULL.  Ws13
- * [2Is][d] and Ws2 [d][Is] are the shared expert (Ws13 NULL: none).
- * Outputs (any may be NULL except out): logits [B][E], ids [B][k],
- * w [B][k], plan, yslot [B][k+1][d] (slot k is the shared expert, zero if
- * none), out [B][d].  Returns 0, or -1 if a selected expert has no weights. */
-int oracle_moe_block(int dt, int B, int d, int E, int k, int I, int Is,
-                     const void *X, const void *Wr, const float *bias,
-                     int bias_ld, const void *const *W13e,
-                     const void *const *W2e, const void *Ws13,
-                     const void *Ws2, double *logits, int32_t *ids,
-                     double *w, int32_t *plan, double *yslot, double *out) {
-  double *lg = logits ? logits : (double *)malloc(sizeof(double) * (size_t)B * E);
-  int32_t *id = ids ? ids : (int32_t *)malloc(sizeof(int32_t) * (size_t)B * k);
-  double *ww = w ? w : (double *)malloc(sizeof(double) * (size_t)B * k);
+/* Token t of the block: its k routed experts, each weighted, then the shared
+ * expert with weight 1, summed in that order into out[t]; the per-slot
+ * outputs to yslot[t] if not NULL.  Returns -1 if a selected expert has no
+ * weights. */
+static int block_token(int dt, int t, int d, int k, int I, int Is,
+                       const void *X, const int32_t *id, const double *ww,
+                       const void *const *W13e, const void *const *W2e,
+                       const void *Ws13, const void *Ws2, double *yslot,
+                       double *out) {
   double *y = (double *)malloc(sizeof(double) * (size_t)d);
+  double *o = out + (size_t)t * d;
   int rc = 0;
-  oracle_route(dt, B, d, E, k, X, Wr, bias, bias_ld, lg, id, ww, plan);
-  for (int t = 0; t < B && rc == 0; ++t) {
-    double *o = out + (size_t)t * d;
-    for (int r = 0; r < d; ++r) o[r] = 0.0;
-    for (int j = 0; j < k; ++j) {
-      int e = id[(size_t)t * k + j];
-      if (!W13e[e] || !W2e[e]) { rc = -1; break; }
-      oracle_expert(dt, d, I, X, (size_t)t * d, W13e[e], W2e[e], y, NULL);
-      for (int r = 0; r < d; ++r) o[r] += ww[(size_t)t * k + j] * y[r];
-      if (yslot)
-        memcpy(yslot + ((size_t)t * (k + 1) + j) * d, y, sizeof(double) * d);
-    }
-    if (rc) break;
+  for (int r = 0; r < d; ++r) o[r] = 0.0;
+  for (int j = 0; j < k && rc == 0; ++j) {
+    int e = id[(size_t)t * k + j];
+    if (!W13e[e] || !W2e[e]) { rc = -1; break; }
+    oracle_expert(dt, d, I, X, (size_t)t * d, W13e[e], W2e[e], y, NULL);
+    for (int r = 0; r < d; ++r) o[r] += ww[(size_t)t * k + j] * y[r];
+    if (yslot)
+      memcpy(yslot + ((size_t)t * (k + 1) + j) * d, y, sizeof(double) * d);
+  }
+  if (rc == 0) {
     if (Ws13) {
       oracle_expert(dt, d, Is, X, (size_t)t * d, Ws13, Ws2, y, NULL);
       for (int r = 0; r < d; ++r) o[r] += y[r];
@@ -247,10 +243,45 @@ int oracle_moe_block(int dt, int B, int d, int E, int k, int I, int Is,
       memcpy(yslot + ((size_t)t * (k + 1) + k) * d, y, sizeof(double) * d);
   }
   free(y);
+  return rc;
+}
+
+/* Whole block.  W13e / W2e are arrays of E pointers, one per expert
+ * ([2I][d] and [d][I]); an expert no token selects may be NULL.  Ws13
+ * [2Is][d] and Ws2 [d][Is] are the shared expert (Ws13 NULL: none).
+ * Outputs (any may be NULL except out): logits [B][E], ids [B][k],
+ * w [B][k], plan, yslot [B][k+1][d] (slot k is the shared expert, zero if
+ * none), out [B][d].  Returns 0, or -1 if a selected expert has no weights.
+ * Tokens are independent; built with OpenMP (the all-cores timing build)
+ * they run in parallel, each with the same arithmetic. */
+int oracle_moe_block(int dt, int B, int d, int E, int k, int I, int Is,
+                     const void *X, const void *Wr, const float *bias,
+                     int bias_ld, const void *const *W13e,
+                     const void *const *W2e, const void *Ws13,
+                     const void *Ws2, double *logits, int32_t *ids,
+                     double *w, int32_t *plan, double *yslot, double *out) {
+  double *lg = logits ? logits : (double *)malloc(sizeof(double) * (size_t)B * E);
+  int32_t *id = ids ? ids : (int32_t *)malloc(sizeof(int32_t) * (size_t)B * k);
+  double *ww = w ? w : (double *)malloc(sizeof(double) * (size_t)B * k);
+  int rc = 0;
+  oracle_route(dt, B, d, E, k, X, Wr, bias, bias_ld, lg, id, ww, plan);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : rc)
+  for (int t = 0; t < B; ++t)
+    rc |= block_token(dt, t, d, k, I, Is, X, id, ww, W13e, W2e, Ws13, Ws2,
+                      yslot, out);
   if (!logits) free(lg);
   if (!ids) free(id);
   if (!w) free(ww);
-  return rc;
+  return rc ? -1 : 0;
+}
+
+/* Threads the block runs its tokens on: 1 in the plain build. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* Weighted combine on given per-slot outputs (for checking the combine stage

@@ -27,43 +27,61 @@ DT_F32 = 0
 DT_BF16 = 1
 
 
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
+_lib_omp = None
+
+
 def build(force: bool = False) -> str:
-    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(
-            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-             "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"],
-            check=True,
-        )
-        os.replace(tmp, _LIB)
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction): the plain
+    single-thread library, and the same source with OpenMP (tokens of a block
+    in parallel) for the all-cores CPU timing."""
+    for lib, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+            tmp = lib + ".tmp%d" % os.getpid()
+            subprocess.run(
+                ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                 "-shared", "-fPIC"] + extra + ["-o", tmp, _SRC, "-lm"],
+                check=True,
+            )
+            os.replace(tmp, lib)
     return _LIB
 
 
-def _load():
-    global _lib
+def _declare(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_skinny_gemm.argtypes = [I, I, I, I, P, P, P]
+    lib.oracle_skinny_gemm_residual.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_router_logits.argtypes = [I, I, I, I, P, P, P, I, P]
+    lib.oracle_topk.argtypes = [I, I, P, P, P]
+    lib.oracle_plan_words.restype = I
+    lib.oracle_plan_words.argtypes = [I, I, I]
+    lib.oracle_plan.argtypes = [I, I, I, P, P]
+    lib.oracle_route.argtypes = [I, I, I, I, I, P, P, P, I, P, P, P, P]
+    lib.oracle_expert.argtypes = [I, I, I, P, ctypes.c_size_t, P, P, P, P]
+    lib.oracle_moe_block.restype = I
+    lib.oracle_moe_block.argtypes = [I] * 7 + [P, P, P, I, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_combine.argtypes = [I, I, I, P, P, I, P]
+    lib.oracle_threads.restype = I
+    lib.oracle_threads.argtypes = []
+    return lib
+
+
+def _load(parallel: bool = False):
+    global _lib, _lib_omp
     with _lock:
         if _lib is None:
             build()
-            lib = ctypes.CDLL(_LIB)
-            P = ctypes.c_void_p
-            I = ctypes.c_int
-            lib.oracle_silu.restype = ctypes.c_double
-            lib.oracle_silu.argtypes = [ctypes.c_double]
-            lib.oracle_skinny_gemm.argtypes = [I, I, I, I, P, P, P]
-            lib.oracle_skinny_gemm_residual.argtypes = [I, I, I, I, P, P, P, P]
-            lib.oracle_router_logits.argtypes = [I, I, I, I, P, P, P, I, P]
-            lib.oracle_topk.argtypes = [I, I, P, P, P]
-            lib.oracle_plan_words.restype = I
-            lib.oracle_plan_words.argtypes = [I, I, I]
-            lib.oracle_plan.argtypes = [I, I, I, P, P]
-            lib.oracle_route.argtypes = [I, I, I, I, I, P, P, P, I, P, P, P, P]
-            lib.oracle_expert.argtypes = [I, I, I, P, ctypes.c_size_t, P, P, P, P]
-            lib.oracle_moe_block.restype = I
-            lib.oracle_moe_block.argtypes = [I] * 7 + [P, P, P, I, P, P, P, P, P, P, P, P, P, P]
-            lib.oracle_combine.argtypes = [I, I, I, P, P, I, P]
-            _lib = lib
-    return _lib
+            _lib = _declare(ctypes.CDLL(_LIB))
+            _lib_omp = _declare(ctypes.CDLL(_LIB_OMP))
+    return _lib_omp if parallel else _lib
+
+
+def threads(parallel: bool = False) -> int:
+    """Threads the oracle's block runs its tokens on (1 for the plain build)."""
+    return _load(parallel).oracle_threads()
 
 
 def _dt(a: np.ndarray) -> int:
@@ -165,10 +183,11 @@ def expert(x_row, W13, W2):
     return y, h
 
 
-def moe_block(X, Wr, k, W13e, W2e, Ws13=None, Ws2=None, bias=None, bias_ld=0):
+def moe_block(X, Wr, k, W13e, W2e, Ws13=None, Ws2=None, bias=None, bias_ld=0, parallel=False):
     """Whole block.  W13e / W2e: sequences of E per-expert arrays (or None for
     experts no token selects).  Returns a dict with logits, ids, w, plan,
-    yslot [B][k+1][d] and out [B][d]."""
+    yslot [B][k+1][d] and out [B][d].  parallel: the OpenMP build (tokens on
+    all cores; same arithmetic per token)."""
     X, Wr, bias = _c(X), _c(Wr), _c(bias, np.float32)
     Ws13, Ws2 = _c(Ws13), _c(Ws2)
     B, d = X.shape
@@ -191,7 +210,7 @@ def moe_block(X, Wr, k, W13e, W2e, Ws13=None, Ws2=None, bias=None, bias_ld=0):
     pl = np.empty(plan_words(B, k, E), np.int32)
     ys = np.empty((B, k + 1, d), np.float64)
     out = np.empty((B, d), np.float64)
-    rc = _load().oracle_moe_block(
+    rc = _load(parallel).oracle_moe_block(
         _dt(X), B, d, E, k, I or 0, Is, _p(X), _p(Wr), _p(bias), bias_ld,
         ctypes.cast(p13, ctypes.c_void_p), ctypes.cast(p2, ctypes.c_void_p),
         _p(Ws13), _p(Ws2), _p(L), _p(ids), _p(w), _p(pl), _p(ys), _p(out))

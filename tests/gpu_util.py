@@ -6,6 +6,8 @@ import sys
 import numpy as np
 import torch
 
+from moe_block_skinny_amd import synth
+
 DEV = "cuda"
 
 
@@ -39,6 +41,44 @@ def rms(a) -> float:
 def say(*args):
     print("[gpu-test]", *args, flush=True)
     sys.stdout.flush()
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Exact values rounded as the GPU rounds its fp32 output: to fp32, then
+    to bf16 (nearest, ties to even); returned widened to float64."""
+    b = synth.to_bf16_bits(np.asarray(a, np.float64).astype(np.float32))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# Block output bars (bf16 output, fp32 internals).
+STATED_BAR = 2e-2     # max|err| <= 2e-2 * rms(ref), the stated bar
+FP32_BLOCK = 1e-3     # bound on the fp32-internal error of a block output, x rms(ref)
+
+
+def check_block_output(g: np.ndarray, ref: np.ndarray) -> tuple:
+    """Assert the bf16 block-output bars; return (max|err|/rms, the same for
+    the exact result rounded to bf16).
+
+    Per element: |g - ref| <= |bf16(ref) - ref| + 2 * FP32_BLOCK * rms.  The
+    GPU rounds its fp32 result r = ref + delta (|delta| <= FP32_BLOCK * rms)
+    to bf16; if that rounds like ref does, the error is ref's own rounding
+    error; if not, a rounding midpoint lies between ref and r, so ref's own
+    rounding error is at least half an ulp minus |delta| and the GPU's at
+    most half an ulp plus |delta|.
+    The stated bar max|err| <= 2e-2 rms is asserted wherever the exact result
+    rounded to bf16 leaves room for it (its own max error plus 2 * FP32_BLOCK
+    below the bar); outputs reaching ~6 rms can exceed it by rounding alone.
+    """
+    scale = rms(ref)
+    err = np.abs(g - ref)
+    rnd = np.abs(bf16_round(ref) - ref)
+    bad = err > rnd + 2 * FP32_BLOCK * scale
+    assert not bad.any(), "bf16-aware per-element bar: %d elements, worst excess %.3g rms" % (
+        int(bad.sum()), float(np.max(err - rnd) / scale))
+    r_err, r_rnd = float(err.max() / scale), float(rnd.max() / scale)
+    if r_rnd + 2 * FP32_BLOCK <= STATED_BAR:
+        assert r_err <= STATED_BAR, "max|err|/rms %.4g above the stated bar" % r_err
+    return r_err, r_rnd
 
 
 def fp32_sum_bound(Xd: np.ndarray, Wd: np.ndarray) -> np.ndarray:

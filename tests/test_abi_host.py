@@ -54,7 +54,7 @@ def test_workspace_bytes():
     assert f(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=64, N=3072, K=7168) >= 2 * 64 * 3072 * 4
 
 
-def status_str():
+def test_status_str():
     assert lib.moe_status_str(0) == b"ok"
     assert lib.moe_status_str(3) == b"workspace too small"
 

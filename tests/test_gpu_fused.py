@@ -3,8 +3,9 @@ schedule and the CPU oracle (needs an MI355X).
 
 Both schedules run the same device functions with the same split of every
 sum, so their outputs, ids and weights must agree bit for bit; both must
-meet the oracle bars of the block (ids exact, weights 1e-5, output within
-2^-8 |ref| + 1e-3 rms for bf16).  Ragged shapes: d not a multiple of the
+meet the oracle bars of the block (ids exact, weights 1e-5; for bf16 the
+bars of check_block_output: per element |bf16(ref) - ref| + 2e-3 rms, and
+max|err| <= 2e-2 rms where rounding leaves room for it).  Ragged shapes: d not a multiple of the
 rows per workgroup, E not a multiple of the router's 4-row tasks, I and Is
 giving an odd number of 2-pair tasks, B*k = 64 with fewer experts than
 slots.
@@ -18,7 +19,7 @@ import torch
 from moe_block_skinny_amd import binding as mb
 from moe_block_skinny_amd import synth
 from tests import inputs
-from tests.gpu_util import dev, host, rms, say
+from tests.gpu_util import check_block_output, dev, host, rms, say
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +78,9 @@ def run(c, weights, ws=None, calls=1):
         w = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
         mb.moe_block(X, Wr, cfg.k, W13, W2, out, ws, Ws13, Ws2, bias, c.bias_ld, ids, w)
         outs.append((out, ids, w))
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        # no grid barrier of the fused schedule gave up waiting
+        assert mb.workspace_status(ws) == 0
     return outs
 
 
@@ -103,12 +106,13 @@ def test_fused_equals_launches_and_oracle(name):
     g = host(of)
     assert np.array_equal(host(idf), c.ids)
     assert np.max(np.abs(host(wf) - c.w)) <= 1e-5
-    scale = rms(ref["out"])
-    err = np.abs(g - ref["out"])
-    say("  max|err|/rms(out)", err.max() / scale)
     if cfg.dtype == "bf16":
-        assert np.all(err <= 2.0 ** -8 * np.abs(ref["out"]) + 1e-3 * scale)
+        r_err, r_rnd = check_block_output(g, ref["out"])
+        say("  max|err|/rms(out) %.5f, exact result rounded to bf16: %.5f" % (r_err, r_rnd))
     else:
+        scale = rms(ref["out"])
+        err = np.abs(g - ref["out"])
+        say("  max|err|/rms(out)", err.max() / scale)
         assert err.max() <= 1e-4 * scale
 
 

@@ -2,12 +2,12 @@
 MI355X): the largest routing problem the ABI accepts (B = 64 tokens, E = 512
 experts, top-16: 1024 slots), every expert chosen by every token (k = E),
 top-1, and the smallest batch that takes the matrix shapes (B = 9).  Expert
-ids and the plan bit-exact; the block output within 2^-8 |ref| + 1e-3 rms
-per element (fp32 internals plus one bf16 rounding).  The stated bar
-max|err| <= 2e-2 * rms is not asserted here: these synthetic outputs reach
-six times their rms, where rounding the exact result to bf16 alone moves it
-by up to 2^-8 * 6 rms = 0.024 rms (the max-scope case measures 0.0225 for
-the rounded oracle, and the same for the GPU)."""
+ids and the plan bit-exact; the block output within the bf16-aware bar of
+check_block_output: per element |err| <= |bf16(ref) - ref| + 2e-3 rms, and
+the stated max|err| <= 2e-2 rms wherever rounding the exact result to bf16
+leaves room for it.  In the max-scope case it does not: its outputs reach
+6.2 times their rms, and the exact result rounded to bf16 is already
+0.0225 rms away from itself (asserted below), above the stated bar."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +15,7 @@ import torch
 from moe_block_skinny_amd import binding as mb
 from moe_block_skinny_amd import synth
 from tests import inputs
-from tests.gpu_util import dev, host, rms, say
+from tests.gpu_util import check_block_output, dev, host, rms, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,10 +60,11 @@ def test_block_and_route_at_scope_limits(name):
     g = host(out)
     assert np.array_equal(host(ids), c.ids)
     assert np.max(np.abs(host(w) - c.w)) <= 1e-5
-    scale = rms(ref)
-    err = np.abs(g - ref)
-    say("  max|err|/rms", float(err.max() / scale))
-    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
+    r_err, r_rnd = check_block_output(g, ref)
+    say("  max|err|/rms %.5f, exact result rounded to bf16: %.5f" % (r_err, r_rnd))
+    if name == "max_scope":
+        # rounding alone exceeds the stated bar here (outputs up to ~6.2 rms)
+        assert 0.0220 <= r_rnd <= 0.0230
     # the router alone: ids, weights and the plan it builds itself
     rids = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
     rw = torch.full((cfg.B, cfg.k), float("nan"), device="cuda")
@@ -115,10 +116,9 @@ def test_block_matrix_down_edges(name):
     g = host(out)
     assert np.array_equal(host(ids), c.ids)
     assert np.max(np.abs(host(w) - c.w)) <= 1e-5
-    scale = rms(ref)
-    err = np.abs(g - ref)
-    say("  max|err|/rms", float(err.max() / scale))
-    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
+    r_err, r_rnd = check_block_output(g, ref)
+    say("  max|err|/rms %.5f, exact result rounded to bf16: %.5f" % (r_err, r_rnd))
+    assert r_rnd + 2e-3 <= 2e-2    # the stated bar applies here and was asserted
 
 
 def test_block_gate_up_cuts_heaviest_entries_first():
@@ -149,8 +149,6 @@ def test_block_gate_up_cuts_heaviest_entries_first():
     g = host(out)
     assert np.array_equal(host(ids), c.ids)
     assert np.max(np.abs(host(w) - c.w)) <= 1e-5
-    scale = rms(ref)
-    err = np.abs(g - ref)
-    say("  max|err|/rms", float(err.max() / scale))
-    assert err.max() <= 2e-2 * scale
-    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * scale)
+    r_err, r_rnd = check_block_output(g, ref)
+    say("  max|err|/rms %.5f, exact result rounded to bf16: %.5f" % (r_err, r_rnd))
+    assert r_rnd + 2e-3 <= 2e-2    # the stated bar applies here and was asserted

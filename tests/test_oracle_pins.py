@@ -415,3 +415,20 @@ def test_hand_worked_example():
     s = lambda z: z / (1 + math.exp(-z))
     out_ref = [eval(expr, {"s": s, "e": e}) for expr in g["out_closed_form"]]
     assert np.allclose(r["out"][0], out_ref, rtol=1e-14, atol=1e-15)
+
+
+def test_parallel_build_gives_the_same_bits():
+    """The OpenMP build (tokens of the block on all cores, used for the
+    all-cores CPU timing) computes every token with the same arithmetic as
+    the plain build, so the two agree bit for bit."""
+    cfg = synth.MoEConfig("omp", 6, 256, 12, 3, 32, 32, "bf16", "gumbel")
+    X, Wr = synth.x(cfg, 4), synth.router_w(cfg, 4)
+    bias, ld = synth.bias(cfg, 4)
+    W13 = [synth.expert_w13(cfg, 4, e) for e in range(cfg.E)]
+    W2 = [synth.expert_w2(cfg, 4, e) for e in range(cfg.E)]
+    Ws13, Ws2 = synth.shared_w13(cfg, 4), synth.shared_w2(cfg, 4)
+    a = orc.moe_block(X, Wr, cfg.k, W13, W2, Ws13, Ws2, bias, ld)
+    b = orc.moe_block(X, Wr, cfg.k, W13, W2, Ws13, Ws2, bias, ld, parallel=True)
+    assert orc.threads(False) == 1 and orc.threads(True) >= 1
+    for key in ("logits", "ids", "w", "plan", "yslot", "out"):
+        assert np.array_equal(a[key], b[key]), key
