@@ -103,29 +103,62 @@ def trial_stats(ms_list):
 
 # ---------------------------------------------------------------- timing
 
-def timed_trials(step, R, args, torch):
-    """Every set once (untimed), W warm-up steps, then T trials of exactly K
-    steps (sets 0 .. K-1 mod R) between two events.  Returns ms per step of
-    each trial."""
-    for r in range(R):
-        step(r)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    out = []
-    for _ in range(args.trials):
+_CYCLES_PER_US = None
+
+
+def hold_stream(torch, us):
+    """Keep the current stream busy for about `us` microseconds with a spin
+    kernel (torch.cuda._sleep), so that the host can queue a whole trial
+    behind it: the timed steps then run back to back on the GPU instead of
+    at the rate the Python caller issues them.  The spin rate is measured
+    once with events."""
+    global _CYCLES_PER_US
+    if _CYCLES_PER_US is None:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _CYCLES_PER_US = 2_000_000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    torch.cuda._sleep(int(us * _CYCLES_PER_US))
+
+
+def timed_trials(step, R, args, torch, info=None):
+    """Every set once (untimed), W warm-up steps, then T trials of exactly K
+    steps (sets 0 .. K-1 mod R) between two events.  Each trial is queued
+    behind a spin kernel long enough for the host to issue all K steps
+    first (twice the host's measured issue time, at least 300 us), so the
+    trial measures the GPU running the steps back to back; `info` receives
+    the host's issue time per step and whether every trial was fully queued
+    before its first step ran.  Returns ms per step of each trial."""
+    t0 = time.perf_counter()
+    for r in range(R):
+        step(r)
+    host_us = (time.perf_counter() - t0) * 1e6 / R
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    out, queued = [], True
+    hold_us = max(300.0, 2.0 * host_us * args.steps)
+    for _ in range(args.trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold_stream(torch, hold_us)
+        t0 = time.perf_counter()
+        e0.record()
         for i in range(args.steps):
             step(i)
         e1.record()
+        issued = (time.perf_counter() - t0) * 1e6
+        queued = queued and issued < hold_us
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1) / args.steps)
+    if info is not None:
+        info.update(host_issue_us_per_step=round(host_us, 2), hold_us=round(hold_us, 1), queued_ahead=queued)
     return out
-
-
 def graph_trials(step, R, args, torch, outs):
     """Trials of graph replays: one graph per weight set, each holding one
     step captured on a side stream.  Before timing, every graph is replayed
@@ -156,6 +189,7 @@ def graph_trials(step, R, args, torch, outs):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        hold_stream(torch, max(300.0, 40.0 * args.steps))
         e0.record()
         for i in range(args.steps):
             graphs[i % R].replay()
@@ -284,10 +318,11 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
                      s["bias"], s["bias_ld"], topk_ids=s["ids"])
 
     mb.set_block_schedule(args.schedule)
+    info = {}
     if args.graph:
         ms = graph_trials(step, R, args, torch, [s["out"] for s in sets])
     else:
-        ms = timed_trials(step, R, args, torch)
+        ms = timed_trials(step, R, args, torch, info)
     variant = mb.last_variant()
     fused = "fused" in variant
     route_in_up = "top-k/plan" in variant
@@ -321,7 +356,7 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
                           "I=%d, Is=%d, %s routing" % (cfg.name, cfg.B, cfg.d, cfg.E, cfg.k, cfg.I,
                                                         cfg.Is, cfg.routing),
                  B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, Is=cfg.Is, rotate=R,
-                 us=us, trials=st,
+                 us=us, trials=dict(st, **info),
                  distinct_experts=round(avg_n, 2), algorithmic_bytes=round(avg_bytes),
                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                  kernels=per_kernel,
@@ -372,7 +407,8 @@ def run_gemm(kind, B, args, torch, mb, synth, with_roofline):
         else:
             mb.skinny_gemm_residual(s["X"], s["W"], s["R"], s["Y"], ws)
 
-    ms = timed_trials(step, R, args, torch)
+    info = {}
+    ms = timed_trials(step, R, args, torch, info)
     variant = mb.last_variant()
     nbytes = wbytes + B * K * 2 + B * N * 2 * (2 if kind == "oproj" else 1)
     durs = kernel_times(step, mb.KERNEL_SKINNY, max(1, args.kernel_steps), torch, mb)
@@ -382,7 +418,7 @@ def run_gemm(kind, B, args, torch, mb, synth, with_roofline):
     what = ("dense skinny GEMM (attention input projection): Y[%d x %d] = X[%d x %d] . W[%d x %d]^T, bf16"
             if kind == "dense" else
             "attention output projection + residual: Y[%d x %d] = X[%d x %d] . W[%d x %d]^T + R, bf16")
-    entry = dict(workload=what % (B, N, B, K, N, K), B=B, N=N, K=K, rotate=R, us=us, trials=st,
+    entry = dict(workload=what % (B, N, B, K, N, K), B=B, N=N, K=K, rotate=R, us=us, trials=dict(st, **info),
                  algorithmic_bytes=nbytes, gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
                  hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                  kernel_us=round(kus, 3), kernel_gbs=round(nbytes / (kus * 1e-6) / 1e9, 1),
@@ -423,8 +459,9 @@ def run_stream(args, torch, mb):
             def step(i, sink=sink):
                 mb.stream_read(bufs[i % R], sink)
 
-            ms = timed_trials(step, R, args, torch)
-            st = trial_stats(ms)
+            info = {}
+            ms = timed_trials(step, R, args, torch, info)
+            st = dict(trial_stats(ms), **info)
             gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
             if best is None or gbs > best["gbs"]:
                 best = dict(bytes=nbytes, rotate=R, workgroups=wg, us=st["median_us"], trials=st,
