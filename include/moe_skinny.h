@@ -301,6 +301,23 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* moe_block without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus ws, ws_bytes),
+ * scope, kernels and results as moe_block, bit for bit.  The workspace is a
+ * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES per GPU (held
+ * until the process ends); sizes whose moe_workspace_bytes(MOE_OP_BLOCK, ...)
+ * exceed it return MOE_EUNSUPPORTED (every size moe_block accepts fits).
+ * The call allocates nothing; before the block it clears the scratch's
+ * counter words with a small kernel on `stream`.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (24u << 20)
+moe_status_t moe_block_noalloc(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                               const void* Wr, const float* bias, int bias_ld, const void* W13,
+                               const void* W2, const void* Ws13, const void* Ws2, void* out,
+                               int32_t* topk_ids, float* topk_w, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

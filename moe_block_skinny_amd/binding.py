@@ -46,6 +46,7 @@ SIGNATURES = {
     "moe_expert_ffn": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "moe_block": (_I, [_I] * 7 + [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_block_noalloc": (_I, [_I] * 7 + [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -323,6 +324,23 @@ def moe_block(X, Wr, k, W13, W2, out, ws, Ws13=None, Ws2=None, bias=None, bias_l
     _check(lib.moe_block(_dt(X), B, d, E, k, I, Is, _ptr(X), _ptr(Wr), _ptr(bias), bias_ld,
                          _ptr(W13), _ptr(W2), _ptr(Ws13), _ptr(Ws2), _ptr(out), _ptr(topk_ids),
                          _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_block_noalloc(X, Wr, k, W13, W2, out, Ws13=None, Ws2=None, bias=None, bias_ld=0,
+                      topk_ids=None, topk_w=None, stream=None):
+    """moe_block on the library's device-resident scratch (no workspace
+    argument, nothing allocated); calls overlapping on one GPU race."""
+    a = _Args()
+    B, d, E, I, Is = _experts(a, X, W13, W2, Ws13, Ws2)
+    a.arr("Wr", Wr, (E, d), X.dtype)
+    _bias(a, bias, bias_ld, B, E)
+    a.arr("out", out, (B, d), X.dtype)
+    a.arr("topk_ids", topk_ids, (B, k), torch.int32, optional=True)
+    a.arr("topk_w", topk_w, (B, k), torch.float32, optional=True)
+    a.on_gpu()
+    _check(lib.moe_block_noalloc(_dt(X), B, d, E, k, I, Is, _ptr(X), _ptr(Wr), _ptr(bias), bias_ld,
+                                 _ptr(W13), _ptr(W2), _ptr(Ws13), _ptr(Ws2), _ptr(out), _ptr(topk_ids),
+                                 _ptr(topk_w), _stream(stream)))
 
 
 def stream_read(src, sink, stream=None):

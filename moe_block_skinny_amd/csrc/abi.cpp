@@ -30,6 +30,7 @@ std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 std::atomic<int> g_sched{-1};  // block schedule; -1: not yet read from the environment
 
 constexpr int kMaxI = kMaxInter;   // kMaxB, kMaxE, kMaxK, kMaxInter: route_core.hpp
+static_assert(kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
 constexpr size_t kAlign = 256;
 
 // Profiling hook: events recorded by the dispatch of one kernel.
@@ -603,31 +604,54 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
   return s;
 }
 
-moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
-                       const void* Wr, const float* bias, int bias_ld, const void* W13,
-                       const void* W2, const void* Ws13, const void* Ws2, void* out,
-                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  moe_status_t s = check_route_dims(dtype, B, d, E, k);
+}  // extern "C"
+
+namespace {
+
+// Arguments of moe_block and of its allocation-free variant.
+struct BlockArgs {
+  int dtype, B, d, E, k, I, Is;
+  const void *X, *Wr;
+  const float* bias;
+  int bias_ld;
+  const void *W13, *W2, *Ws13, *Ws2;
+  void* out;
+  int32_t* topk_ids;
+  float* topk_w;
+};
+
+// Every check of the block's arguments but the workspace's, on the host:
+// the kernel shapes and the workspace layout the launch will use.
+moe_status_t block_check(const BlockArgs& a, int* v, int* force, BlockWs* L) {
+  moe_status_t s = check_route_dims(a.dtype, a.B, a.d, a.E, a.k);
   if (s) return s;
-  if ((s = check_inter(dtype, I, "I"))) return s;
-  if (Ws13 && (s = check_inter(dtype, Is, "Is"))) return s;
-  if (!aligned(X) || !aligned(Wr) || !aligned(W13) || !aligned(W2) || !aligned(out))
+  if ((s = check_inter(a.dtype, a.I, "I"))) return s;
+  if (a.Ws13 && (s = check_inter(a.dtype, a.Is, "Is"))) return s;
+  if (!aligned(a.X) || !aligned(a.Wr) || !aligned(a.W13) || !aligned(a.W2) || !aligned(a.out))
     return fail(MOE_EINVAL, "X, Wr, W13, W2 or out null or misaligned");
-  if (Ws13 && (!aligned(Ws13) || !aligned(Ws2))) return fail(MOE_EINVAL, "Ws13 or Ws2 null or misaligned");
-  if (bias && !aligned(bias)) return fail(MOE_EINVAL, "bias misaligned");
-  if (bias && bias_ld != 0 && bias_ld != E) return fail(MOE_EINVAL, "bias_ld must be 0 or E");
-  if ((topk_ids && !aligned(topk_ids)) || (topk_w && !aligned(topk_w)))
+  if (a.Ws13 && (!aligned(a.Ws13) || !aligned(a.Ws2))) return fail(MOE_EINVAL, "Ws13 or Ws2 null or misaligned");
+  if (a.bias && !aligned(a.bias)) return fail(MOE_EINVAL, "bias misaligned");
+  if (a.bias && a.bias_ld != 0 && a.bias_ld != a.E) return fail(MOE_EINVAL, "bias_ld must be 0 or E");
+  if ((a.topk_ids && !aligned(a.topk_ids)) || (a.topk_w && !aligned(a.topk_w)))
     return fail(MOE_EINVAL, "topk_ids or topk_w misaligned");
+  const int bf16 = a.dtype == MOE_DT_BF16;
+  if ((s = resolve_skinny(bf16, a.B, a.d, v))) return s;
+  if ((s = expert_force(a.dtype, a.B, force))) return s;
+  *L = block_ws(bf16, a.B, a.d, a.E, a.k, a.I, a.Ws13 ? a.Is : 0);
+  return MOE_OK;
+}
+
+// The block's launches on workspace w (layout L), arguments already checked.
+moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, char* w, hipStream_t st) {
+  const int dtype = A.dtype, B = A.B, d = A.d, E = A.E, k = A.k, I = A.I, Is = A.Is;
+  const void *X = A.X, *Wr = A.Wr, *W13 = A.W13, *W2 = A.W2, *Ws13 = A.Ws13, *Ws2 = A.Ws2;
+  const float* bias = A.bias;
+  const int bias_ld = A.bias_ld;
+  void* out = A.out;
+  int32_t* topk_ids = A.topk_ids;
+  float* topk_w = A.topk_w;
   const int bf16 = dtype == MOE_DT_BF16;
-  int v, force;
-  if ((s = resolve_skinny(bf16, B, d, &v))) return s;
-  if ((s = expert_force(dtype, B, &force))) return s;
-  const BlockWs L = block_ws(bf16, B, d, E, k, I, Ws13 ? Is : 0);
-  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
-  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
-  char* w = static_cast<char*>(ws);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  moe_status_t s;
   int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(w + L.ids);
   float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.w);
   int32_t* plan = reinterpret_cast<int32_t*>(w + L.plan);
@@ -717,6 +741,50 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   snprintf(desc, sizeof desc, "route[%s] %s; %s", d1, d2, d3);
   record("moe_block", B, desc);
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                       const void* Wr, const float* bias, int bias_ld, const void* W13,
+                       const void* W2, const void* Ws13, const void* Ws2, void* out,
+                       int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  const BlockArgs a = {dtype, B, d, E, k, I, Is, X, Wr, bias, bias_ld, W13, W2, Ws13, Ws2, out, topk_ids, topk_w};
+  int v, force;
+  BlockWs L;
+  moe_status_t s = block_check(a, &v, &force, &L);
+  if (s) return s;
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  return block_run(a, v, force, L, static_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_block_noalloc(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                               const void* Wr, const float* bias, int bias_ld, const void* W13,
+                               const void* W2, const void* Ws13, const void* Ws2, void* out,
+                               int32_t* topk_ids, float* topk_w, void* stream) {
+  g_err[0] = 0;
+  const BlockArgs a = {dtype, B, d, E, k, I, Is, X, Wr, bias, bias_ld, W13, W2, Ws13, Ws2, out, topk_ids, topk_w};
+  int v, force;
+  BlockWs L;
+  moe_status_t s = block_check(a, &v, &force, &L);
+  if (s) return s;
+  if (L.total > kNoallocScratchBytes)
+    return fail(MOE_EUNSUPPORTED, "these sizes need %zu bytes of workspace, above the %zu bytes of the "
+                "library's scratch (use moe_block with a workspace)", L.total, (size_t)kNoallocScratchBytes);
+  // the device address of this GPU's scratch array (looked up once per device)
+  char* w = nullptr;
+  if ((s = hip_status(noalloc_scratch(reinterpret_cast<void**>(&w)), "scratch address"))) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the scratch keeps the last call's contents: the counter words every
+  // launch expects at zero are cleared first (a kernel, so the call may be
+  // captured in a graph)
+  if ((s = hip_status(launch_fill_zero(w, kCounterBytes + 2 * kFlagStride * 4, st), "scratch counters")))
+    return s;
+  return block_run(a, v, force, L, w, st);
 }
 
 }  // extern "C"

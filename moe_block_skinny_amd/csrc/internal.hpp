@@ -167,6 +167,12 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 int moe_block_fused_grid(const ExpertLaunch& ex, int bf16, int B);
 hipError_t launch_moe_block_fused(BlockLaunch& f, hipStream_t st, char* desc, size_t desc_len);
 
+// moe_block_noalloc: bytes of the library's device-resident scratch (one
+// array per GPU, noalloc.hip), and the device address of the current
+// device's copy (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)24 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Row blocks of the skinny kernel for a given variant (host-side geometry).
 int skinny_rows_per_block(int variant, int router);
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router);
