@@ -103,8 +103,9 @@ typedef enum {
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
-/* Static text for a status code. */
-const char* moe_status_str(moe_status_t s);
+/* Static text for a status code (any int: "unknown status" outside
+ * moe_status_t). */
+const char* moe_status_str(int s);
 
 /* Detail of the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);

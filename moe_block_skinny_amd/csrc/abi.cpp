@@ -380,7 +380,7 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-const char* moe_status_str(moe_status_t s) {
+const char* moe_status_str(int s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument";
