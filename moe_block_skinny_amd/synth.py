@@ -32,6 +32,7 @@ import numpy as np
 _T_X, _T_WR, _T_W13, _T_W2, _T_WS13, _T_WS2, _T_GUMBEL, _T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 _T_DX, _T_DW = 9, 10
 _T_OX, _T_OW, _T_OR = 11, 12, 13
+_T_LAT = 14
 
 
 @dataclass(frozen=True)
@@ -61,6 +62,9 @@ CONFIGS = {
 DENSE_N = 3072
 DENSE_K = 7168
 DENSE_BATCHES = (1, 2, 4, 8, 16, 32, 64)
+# latent input projection concatenated with the router (the pages give no
+# latent dimension): Wl [LATENT_L][d]
+LATENT_L = 1024
 # attention output projection with residual: back from one rank's attention
 # width (taken equal to the input projection's share, 3072) to d = 7168
 OPROJ_N = 7168
@@ -189,3 +193,8 @@ def oproj_w(N: int = OPROJ_N, K: int = OPROJ_K, seed: int = 0) -> np.ndarray:
 def oproj_r(B: int, N: int = OPROJ_N, seed: int = 0) -> np.ndarray:
     """The residual stream entering the output projection: N(0, 1)."""
     return to_bf16_bits(_normal(_rng(seed, _T_OR, B), (B, N), 1.0))
+
+
+def latent_w(cfg: MoEConfig, seed: int, L: int = LATENT_L) -> np.ndarray:
+    """Latent input projection Wl [L][d] ~ N(0, 1/d)."""
+    return _encode(_normal(_rng(seed, _T_LAT), (L, cfg.d), cfg.d ** -0.5), cfg.dtype)

@@ -112,6 +112,17 @@ void oracle_router_logits(int dt, int B, int d, int E, const void *X,
     }
 }
 
+/* Latent input projection ([WRITEUP] part 1 §3: the router scores and the
+ * latent input projection both take the token's hidden state x, and the
+ * specialised path computes them as one matrix product):
+ * latent[t][j] = sum_c X[t][c] Wl[j][c]; X [B][d], Wl [L][d]. */
+void oracle_latent_projection(int dt, int B, int d, int L, const void *X,
+                              const void *Wl, double *latent) {
+  for (int t = 0; t < B; ++t)
+    for (int j = 0; j < L; ++j)
+      latent[(size_t)t * L + j] = dot(X, (size_t)t * d, Wl, (size_t)j * d, dt, d);
+}
+
 /* Top-k of one token's logits.  The k winners are taken one at a time: each
  * round picks the largest remaining fp32-rounded logit, and on an exact tie
  * the lower expert index.  They are returned in ascending expert id, with

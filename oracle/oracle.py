@@ -64,6 +64,7 @@ def _declare(lib):
     lib.oracle_moe_block.restype = I
     lib.oracle_moe_block.argtypes = [I] * 7 + [P, P, P, I, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_combine.argtypes = [I, I, I, P, P, I, P]
+    lib.oracle_latent_projection.argtypes = [I, I, I, I, P, P, P]
     lib.oracle_threads.restype = I
     lib.oracle_threads.argtypes = []
     return lib
@@ -181,6 +182,17 @@ def expert(x_row, W13, W2):
     h = np.empty(I, np.float64)
     _load().oracle_expert(_dt(x_row), d, I, _p(x_row), 0, _p(W13), _p(W2), _p(y), _p(h))
     return y, h
+
+
+def latent_projection(X, Wl) -> np.ndarray:
+    """Latent input projection latent = X . Wl^T: X [B][d], Wl [L][d] ->
+    float64 [B][L]."""
+    X, Wl = _c(X), _c(Wl)
+    B, d = X.shape
+    L = Wl.shape[0]
+    out = np.empty((B, L), np.float64)
+    _load().oracle_latent_projection(_dt(X), B, d, L, _p(X), _p(Wl), _p(out))
+    return out
 
 
 def moe_block(X, Wr, k, W13e, W2e, Ws13=None, Ws2=None, bias=None, bias_ld=0, parallel=False):

@@ -31,6 +31,8 @@ MUTANTS = {
                            "for (int r = 0; r < d; ++r) o[r] += 0.5 * y[r];"),
     "combine_shared_inverted": ("if (has_shared) s +=", "if (!has_shared) s +="),
     "plan_token_not_slot": ("slots[pos++] = s;", "slots[pos++] = s / k;"),
+    "latent_rows_transposed": ("latent[(size_t)t * L + j] = dot(X, (size_t)t * d, Wl, (size_t)j * d, dt, d);",
+                               "latent[(size_t)t * L + j] = dot(X, (size_t)t * d, Wl, (size_t)j, dt, d);"),
     "residual_transposed": ("elem(R, dt, (size_t)b * N + n)", "elem(R, dt, (size_t)n * B + b)"),
     "residual_dropped": ("dot(X, (size_t)b * K, W, (size_t)n * K, dt, K) +\n          elem(R",
                          "dot(X, (size_t)b * K, W, (size_t)n * K, dt, K) +\n          0.0 * elem(R"),

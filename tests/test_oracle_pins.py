@@ -432,3 +432,33 @@ def test_parallel_build_gives_the_same_bits():
     assert orc.threads(False) == 1 and orc.threads(True) >= 1
     for key in ("logits", "ids", "w", "plan", "yslot", "out"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_latent_projection_pins(dt):
+    """Latent input projection: against numpy float64 on random inputs
+    (within the fp64 sum bound), bit-exact on small integers, K-split parts
+    summing to the unsplit product, and a permutation matrix gathering the
+    input columns it names."""
+    rng = np.random.default_rng(31)
+    B, d, L = 3, 96, 40
+    X = rng.standard_normal((B, d)).astype(np.float32)
+    Wl = rng.standard_normal((L, d)).astype(np.float32)
+    if dt == "bf16":
+        X, Wl = synth.to_bf16_bits(X), synth.to_bf16_bits(Wl)
+    Y = orc.latent_projection(X, Wl)
+    ref = widen(X) @ widen(Wl).T
+    assert Y.shape == (B, L)
+    assert np.all(np.abs(Y - ref) <= 2 * d * 2.0 ** -53 * (np.abs(widen(X)) @ np.abs(widen(Wl)).T) + 1e-300)
+    Xi, Wi = rng.integers(-3, 4, (B, 2048)), rng.integers(-3, 4, (L, 2048))
+    Xb, Wb = synth.to_bf16_bits(Xi.astype(np.float32)), synth.to_bf16_bits(Wi.astype(np.float32))
+    Yi = orc.latent_projection(Xb, Wb)
+    assert np.array_equal(Yi, (Xi @ Wi.T).astype(np.float64))
+    parts = sum(orc.latent_projection(np.ascontiguousarray(Xb[:, a:a + 512]), np.ascontiguousarray(Wb[:, a:a + 512]))
+                for a in range(0, 2048, 512))
+    assert np.array_equal(parts, Yi)
+    cols = rng.permutation(d)[:L]
+    P = np.zeros((L, d), np.float32)
+    P[np.arange(L), cols] = 1.0
+    Pe = P if dt == "f32" else synth.to_bf16_bits(P)
+    assert np.array_equal(orc.latent_projection(X, Pe), widen(X)[:, cols])
