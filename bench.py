@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--trials", type=int, default=7)
     ap.add_argument("--workload", default="sweep",
-                    choices=["sweep", "tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "oproj", "stream", "copy"])
+                    choices=["sweep", "tiny", "tp16_b1", "tp16_b8", "tp8_b64", "dense", "oproj", "latent", "stream",
+                             "copy"])
     ap.add_argument("--batch", type=int, default=1, help="dense / oproj workload batch")
     ap.add_argument("--rotate", type=int, default=0, help="weight sets (0: the workload's default)")
     ap.add_argument("--seed", type=int, default=0)
@@ -362,6 +363,8 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
                  kernels=per_kernel,
                  launch="graph replay" if args.graph else "plain launches",
                  variant=variant)
+    if cfg.B * cfg.k <= 64 and cfg.Is and cfg.dtype == "bf16" and args.schedule == "auto" and not args.graph:
+        entry["shared_placements"] = shared_placements(cfg, sets, R, ws, args, torch, mb)
     roof = None
     if with_roofline:
         dom = max(kern, key=lambda k: sum(kern[k]))
@@ -375,6 +378,38 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
     del sets, ws
     torch.cuda.empty_cache()
     return entry, roof, cfg
+
+
+def shared_placements(cfg, sets, R, ws, args, torch, mb):
+    """Block µs with the shared expert's gate/up in the gate/up launch, in the
+    router launch (one pass over x), and the whole shared expert on a second
+    stream (moe_block_streams), each timed like the headline."""
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def block(i):
+        s = sets[i % R]
+        mb.moe_block(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, s["Ws13"], s["Ws2"],
+                     s["bias"], s["bias_ld"], topk_ids=s["ids"])
+
+    def streams(i):
+        s = sets[i % R]
+        mb.moe_block_streams(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, side, fork, join,
+                             s["Ws13"], s["Ws2"], s["bias"], s["bias_ld"], topk_ids=s["ids"])
+
+    out = {}
+    for label, place, step in (("gate_up_launch", "up", block), ("router_launch", "router", block),
+                               ("side_stream", "up", streams)):
+        prev = mb.set_shared_schedule(place)
+        try:
+            info = {}
+            st = trial_stats(timed_trials(step, R, args, torch, info))
+        finally:
+            mb.set_shared_schedule(prev)
+        out[label] = dict(us=st["median_us"], p10_us=st["p10_us"], p90_us=st["p90_us"],
+                          queued_ahead=info.get("queued_ahead"))
+    torch.cuda.synchronize()
+    return out
 
 
 # ---------------------------------------------------------------- dense
@@ -434,6 +469,53 @@ def run_gemm(kind, B, args, torch, mb, synth, with_roofline):
     del sets, ws
     torch.cuda.empty_cache()
     return entry, roof
+
+
+# ---------------------------------------------------------------- latent
+
+def run_route_latent(B, args, torch, mb, synth):
+    """The router with the latent input projection in one product over x
+    (moe_route_latent, L = 1024 latent rows) against the same work as two
+    launches (moe_route, then skinny_gemm for the latent rows): d = 7168,
+    E = 384, top-8, bf16, plain routing."""
+    cfg = synth.CONFIGS["tp16_b1"]
+    d, E, k, L = cfg.d, cfg.E, cfg.k, synth.LATENT_L
+    wbytes = (E + L) * d * 2
+    R = rotations("dense", wbytes, args)
+    sets = []
+    for r in range(R):
+        g = torch.Generator(device="cuda").manual_seed(args.seed * 1000003 + 500 + r)
+        sets.append(dict(X=torch.randn((B, d), generator=g, device="cuda", dtype=torch.bfloat16),
+                         Wr=(torch.randn((E, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16),
+                         Wl=(torch.randn((L, d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16),
+                         ids=torch.empty((B, k), dtype=torch.int32, device="cuda"),
+                         w=torch.empty((B, k), device="cuda"),
+                         plan=torch.empty((mb.plan_words(B, k, E),), dtype=torch.int32, device="cuda"),
+                         lat=torch.empty((B, L), dtype=torch.bfloat16, device="cuda")))
+    ws = mb.workspace(max(mb.workspace_bytes(mb.OP_ROUTE_LATENT, mb.DT_BF16, B=B, d=d, E=E, k=k, N=L),
+                          mb.workspace_bytes(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=L, K=d)))
+
+    def merged(i):
+        s = sets[i % R]
+        mb.moe_route_latent(s["X"], s["Wr"], s["Wl"], k, s["ids"], s["w"], s["plan"], s["lat"], ws)
+
+    def separate(i):
+        s = sets[i % R]
+        mb.moe_route(s["X"], s["Wr"], k, s["ids"], s["w"], s["plan"], ws)
+        mb.skinny_gemm(s["X"], s["Wl"], s["lat"], ws)
+
+    out = {}
+    for label, step in (("merged", merged), ("separate", separate)):
+        info = {}
+        st = dict(trial_stats(timed_trials(step, R, args, torch, info)), **info)
+        nbytes = wbytes + B * d * 2 + B * L * 2
+        out[label] = dict(us=st["median_us"], trials=st, gbs=round(nbytes / (st["median_us"] * 1e-6) / 1e9, 1),
+                          variant=mb.last_variant())
+    out.update(B=B, d=d, E=E, L=L, rotate=R, algorithmic_bytes=wbytes + B * d * 2 + B * L * 2,
+               workload="router + latent input projection (L=%d) over x [%d x %d], bf16" % (L, B, d))
+    del sets, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---------------------------------------------------------------- yardsticks
@@ -629,6 +711,12 @@ def main():
                 sweep["dense_b%d" % B] = e
                 print("[bench] dense B=%d: %.3f us" % (B, e["us"]), file=sys.stderr, flush=True)
             config["sweep"] = sweep
+            config["route_latent"] = {}
+            for B in (1, 64):
+                e = run_route_latent(B, args, torch, mb, synth)
+                config["route_latent"]["b%d" % B] = e
+                print("[bench] router + latent B=%d: merged %.3f us, separate %.3f us"
+                      % (B, e["merged"]["us"], e["separate"]["us"]), file=sys.stderr, flush=True)
             stream = run_stream(args, torch, mb)
             config["stream"] = stream
             ref = stream["1gib"]["gbs"]
@@ -645,6 +733,15 @@ def main():
         if not args.no_cpu_baseline:
             cpu = cpu_baseline_gemm(args.workload, args.batch, args)
         value = entry["us"]
+    elif args.workload == "latent":
+        e = run_route_latent(args.batch, args, torch, mb, synth)
+        config = dict(e)
+        m = e["merged"]
+        roof = dict(bound="hbm", achieved=m["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(m["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="skinny_valu_kernel / skinny_mfma_kernel + route_finish_kernel (router + latent rows)",
+                    launch="route", bytes_per_launch=e["algorithmic_bytes"], avg_us=m["us"])
+        value = m["us"]
     elif args.workload == "stream":
         st = run_stream(args, torch, mb)
         config = dict(workload="read-only 128-bit streaming yardstick (moe_stream_read)", stream=st)

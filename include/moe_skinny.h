@@ -97,7 +97,8 @@ typedef enum {
   MOE_OP_SKINNY_GEMM = 0,
   MOE_OP_ROUTE = 1,
   MOE_OP_EXPERT_FFN = 2,
-  MOE_OP_BLOCK = 3
+  MOE_OP_BLOCK = 3,
+  MOE_OP_ROUTE_LATENT = 4
 } moe_op_t;
 
 /* Version of this ABI (MOE_ABI_VERSION). */
@@ -127,6 +128,18 @@ int moe_set_variant(int variant);
 typedef enum { MOE_SCHEDULE_AUTO = 0, MOE_SCHEDULE_LAUNCHES = 1, MOE_SCHEDULE_FUSED = 2 } moe_schedule_t;
 int moe_set_block_schedule(int schedule);
 
+/* Where moe_block runs the shared expert's gate/up in the small-batch
+ * schedule (B*k <= 64, vector shape; WRITEUP part 1 §3: the shared expert
+ * overlaps routing): MOE_SHARED_IN_UP (its tiles first in the gate/up
+ * launch, streaming while the other workgroups select the top-k) or
+ * MOE_SHARED_IN_ROUTER (in the router launch: one pass over x for the router
+ * rows and the shared gate/up rows).  MOE_SHARED_AUTO takes the one measured
+ * faster on MI355X (currently MOE_SHARED_IN_UP).  Also set by the
+ * MOE_SHARED_SCHEDULE environment variable (up, router).  All placements
+ * give identical bits.  Returns the previous setting. */
+typedef enum { MOE_SHARED_AUTO = 0, MOE_SHARED_IN_UP = 1, MOE_SHARED_IN_ROUTER = 2 } moe_shared_schedule_t;
+int moe_set_shared_schedule(int schedule);
+
 /* int32 words of a routing plan for B tokens, top-k of E experts:
  * 2 + 2*min(E, B*k) + B*k.  Layout, with maxa = min(E, B*k):
  *   plan[0]                    n, the number of distinct experts selected
@@ -141,7 +154,8 @@ int moe_plan_words(int B, int k, int E);
  *   MOE_OP_SKINNY_GEMM: dtype, B, N, K
  *   MOE_OP_ROUTE:       dtype, B, d, E, k
  *   MOE_OP_EXPERT_FFN:  dtype, B, d, E, k, I, Is
- *   MOE_OP_BLOCK:       dtype, B, d, E, k, I, Is */
+ *   MOE_OP_BLOCK:       dtype, B, d, E, k, I, Is
+ *   MOE_OP_ROUTE_LATENT: dtype, B, d, E, k, and N = L (the latent rows) */
 size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I, int Is, int N,
                            int K);
 
@@ -231,6 +245,24 @@ moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, con
                        const float* bias, int bias_ld, int32_t* topk_ids, float* topk_w,
                        int32_t* plan, float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Router with the latent input projection in the same product (WRITEUP
+ * part 1 §3: the router scores and the latent input projection both take
+ * the token's hidden state and are computed as one matrix product, so x is
+ * read once and both weight matrices stream in one launch):
+ *   everything moe_route computes and returns, and
+ *   latent_out[t][j] = sum_c X[t][c] * Wl[j][c]   (no bias), accumulated in
+ *   fp32, stored as latent_dtype (dtype or MOE_DT_F32; bf16: round to
+ *   nearest-even).
+ *   Wl [L][d] of dtype; latent_out [B][L].  The product runs over the E + L
+ *   rows [Wr; Wl] with moe_route's kernel shapes; selection, weights and
+ *   plan use the E router rows only.  Scope: that of moe_route, plus L a
+ *   multiple of 16 up to 8192 and E a multiple of 4.  Workspace:
+ *   moe_workspace_bytes(MOE_OP_ROUTE_LATENT, dtype, B, d, E, k, 0, 0, L, 0). */
+moe_status_t moe_route_latent(int dtype, int B, int d, int E, int k, int L, const void* X, const void* Wr,
+                              const void* Wl, const float* bias, int bias_ld, int32_t* topk_ids, float* topk_w,
+                              int32_t* plan, void* latent_out, int latent_dtype, float* logits_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* Routed and shared experts (WRITEUP part 1 §3; SwiGLU expert FFN):
  *   for every slot s = t*k + j of the plan, with e its expert:
  *     h = silu(X[t] . W13[e][0:I]^T) * (X[t] . W13[e][I:2I]^T),
@@ -302,18 +334,37 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* moe_block with the shared expert on a second stream (WRITEUP part 1 §3:
+ * the shared expert runs on its own stream, overlapping routing and the
+ * routed experts).  Same arguments, scope checks, workspace and results (bit
+ * for bit) as moe_block, plus side_stream (a hipStream_t other than stream,
+ * default priority) and two caller-owned hipEvent_t: fork_event is recorded
+ * on stream and waited for by side_stream, which then runs the shared
+ * expert's gate/up and down; join_event is recorded on side_stream and
+ * waited for by stream before the down + combine launch, which adds the
+ * shared expert's output.  The router and routed gate/up launches on stream
+ * overlap the side stream's work.  Applies to the small-batch three-launch
+ * schedule (B*k <= 64, vector shape) with a shared expert; MOE_EUNSUPPORTED
+ * otherwise.  Both streams' work must be complete before ws is reused. */
+moe_status_t moe_block_streams(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                               const void* Wr, const float* bias, int bias_ld, const void* W13,
+                               const void* W2, const void* Ws13, const void* Ws2, void* out,
+                               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream,
+                               void* side_stream, void* fork_event, void* join_event);
+
 /* moe_block without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments (minus ws, ws_bytes),
  * scope, kernels and results as moe_block, bit for bit.  The workspace is a
  * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES per GPU (held
  * until the process ends); sizes whose moe_workspace_bytes(MOE_OP_BLOCK, ...)
- * exceed it return MOE_EUNSUPPORTED (every size moe_block accepts fits).
+ * exceed it return MOE_EUNSUPPORTED (every B, E, k, I, Is moe_block accepts
+ * fits up to d = 16384).
  * The call allocates nothing; before the block it clears the scratch's
  * counter words with a small kernel on `stream`.  Every call on one GPU
  * shares that GPU's array: calls that may overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller. */
-#define MOE_NOALLOC_SCRATCH_BYTES (24u << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
 moe_status_t moe_block_noalloc(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
                                const void* Wr, const float* bias, int bias_ld, const void* W13,
                                const void* W2, const void* Ws13, const void* Ws2, void* out,

@@ -19,11 +19,13 @@ LIB_PATH = os.path.join(_HERE, "libmoe_skinny.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 DT_F32, DT_BF16 = 0, 1
 VARIANT_AUTO, VARIANT_GEMV, VARIANT_SPLITK, VARIANT_MFMA = range(4)
-OP_SKINNY_GEMM, OP_ROUTE, OP_EXPERT_FFN, OP_BLOCK = range(4)
+OP_SKINNY_GEMM, OP_ROUTE, OP_EXPERT_FFN, OP_BLOCK, OP_ROUTE_LATENT = range(5)
 KERNEL_ROUTE, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_SKINNY, KERNEL_BLOCK, KERNEL_STREAM = range(7)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "splitk": VARIANT_SPLITK, "mfma": VARIANT_MFMA}
 SCHEDULE_AUTO, SCHEDULE_LAUNCHES, SCHEDULE_FUSED = range(3)
 SCHEDULES = {"auto": SCHEDULE_AUTO, "launches": SCHEDULE_LAUNCHES, "fused": SCHEDULE_FUSED}
+SHARED_AUTO, SHARED_IN_UP, SHARED_IN_ROUTER = range(3)
+SHARED_SCHEDULES = {"auto": SHARED_AUTO, "up": SHARED_IN_UP, "router": SHARED_IN_ROUTER}
 
 # name: (restype, argtypes)
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -34,6 +36,7 @@ SIGNATURES = {
     "moe_last_variant": (ctypes.c_char_p, []),
     "moe_set_variant": (_I, [_I]),
     "moe_set_block_schedule": (_I, [_I]),
+    "moe_set_shared_schedule": (_I, [_I]),
     "moe_plan_words": (_I, [_I, _I, _I]),
     "moe_workspace_bytes": (_Z, [_I] * 10),
     "moe_workspace_init": (_I, [_P, _Z, _P]),
@@ -43,9 +46,11 @@ SIGNATURES = {
     "skinny_gemm": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _Z, _P]),
     "skinny_gemm_residual": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "moe_route": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_route_latent": (_I, [_I] * 6 + [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "moe_expert_ffn": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "moe_block": (_I, [_I] * 7 + [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_block_streams": (_I, [_I] * 7 + [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _P, _P, _P]),
     "moe_block_noalloc": (_I, [_I] * 7 + [_P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -170,6 +175,11 @@ def set_block_schedule(name_or_id) -> int:
     return lib.moe_set_block_schedule(v)
 
 
+def set_shared_schedule(name_or_id) -> int:
+    v = SHARED_SCHEDULES[name_or_id] if isinstance(name_or_id, str) else int(name_or_id)
+    return lib.moe_set_shared_schedule(v)
+
+
 def plan_words(B: int, k: int, E: int) -> int:
     return lib.moe_plan_words(B, k, E)
 
@@ -263,6 +273,33 @@ def moe_route(X, Wr, k, topk_ids, topk_w, plan, ws, bias=None, bias_ld=0, logits
                          ws.numel(), _stream(stream)))
 
 
+def moe_route_latent(X, Wr, Wl, k, topk_ids, topk_w, plan, latent_out, ws, bias=None, bias_ld=0,
+                     logits_out=None, stream=None):
+    """moe_route with the latent input projection latent_out = X . Wl^T in the
+    same product over X (latent_out of X's dtype or fp32)."""
+    B, d = _shape("X", X, 2)
+    E, _ = _shape("Wr", Wr, 2)
+    L, _ = _shape("Wl", Wl, 2)
+    a = _Args()
+    a.arr("X", X, (B, d), X.dtype)
+    a.arr("Wr", Wr, (E, d), X.dtype)
+    a.arr("Wl", Wl, (L, d), X.dtype)
+    _bias(a, bias, bias_ld, B, E)
+    a.arr("topk_ids", topk_ids, (B, k), torch.int32)
+    a.arr("topk_w", topk_w, (B, k), torch.float32)
+    a.arr("plan", plan, (plan_words(B, k, E),), torch.int32)
+    _shape("latent_out", latent_out, 2)
+    if latent_out.dtype not in (X.dtype, torch.float32):
+        raise TypeError("latent_out: dtype %s, expected %s or torch.float32" % (latent_out.dtype, X.dtype))
+    a.arr("latent_out", latent_out, (B, L), latent_out.dtype)
+    a.arr("logits_out", logits_out, (B, E), torch.float32, optional=True)
+    a.workspace(ws)
+    a.on_gpu()
+    _check(lib.moe_route_latent(_dt(X), B, d, E, k, L, _ptr(X), _ptr(Wr), _ptr(Wl), _ptr(bias), bias_ld,
+                                _ptr(topk_ids), _ptr(topk_w), _ptr(plan), _ptr(latent_out), _dt(latent_out),
+                                _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def _experts(a, X, W13, W2, Ws13, Ws2):
     """Shapes of the expert weights against X [B][d]: (B, d, E, I, Is)."""
     B, d = _shape("X", X, 2)
@@ -324,6 +361,34 @@ def moe_block(X, Wr, k, W13, W2, out, ws, Ws13=None, Ws2=None, bias=None, bias_l
     _check(lib.moe_block(_dt(X), B, d, E, k, I, Is, _ptr(X), _ptr(Wr), _ptr(bias), bias_ld,
                          _ptr(W13), _ptr(W2), _ptr(Ws13), _ptr(Ws2), _ptr(out), _ptr(topk_ids),
                          _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _event(e):
+    """Raw hipEvent_t of a torch.cuda.Event (recorded once, so that it exists)."""
+    if hasattr(e, "cuda_event"):
+        if not e.cuda_event:
+            e.record()
+        return e.cuda_event
+    return e
+
+
+def moe_block_streams(X, Wr, k, W13, W2, out, ws, side_stream, fork_event, join_event, Ws13=None, Ws2=None,
+                      bias=None, bias_ld=0, topk_ids=None, topk_w=None, stream=None):
+    """moe_block with the shared expert on side_stream (torch.cuda.Stream),
+    ordered by fork_event / join_event (torch.cuda.Event objects)."""
+    a = _Args()
+    B, d, E, I, Is = _experts(a, X, W13, W2, Ws13, Ws2)
+    a.arr("Wr", Wr, (E, d), X.dtype)
+    _bias(a, bias, bias_ld, B, E)
+    a.arr("out", out, (B, d), X.dtype)
+    a.arr("topk_ids", topk_ids, (B, k), torch.int32, optional=True)
+    a.arr("topk_w", topk_w, (B, k), torch.float32, optional=True)
+    a.workspace(ws)
+    a.on_gpu()
+    _check(lib.moe_block_streams(_dt(X), B, d, E, k, I, Is, _ptr(X), _ptr(Wr), _ptr(bias), bias_ld,
+                                 _ptr(W13), _ptr(W2), _ptr(Ws13), _ptr(Ws2), _ptr(out), _ptr(topk_ids),
+                                 _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream), _stream(side_stream),
+                                 _event(fork_event), _event(join_event)))
 
 
 def moe_block_noalloc(X, Wr, k, W13, W2, out, Ws13=None, Ws2=None, bias=None, bias_ld=0,

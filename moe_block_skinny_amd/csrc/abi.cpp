@@ -28,8 +28,10 @@ thread_local char g_err[512] = "";
 thread_local char g_variant[256] = "";
 std::atomic<int> g_force{-1};  // -1: not yet read from the environment
 std::atomic<int> g_sched{-1};  // block schedule; -1: not yet read from the environment
+std::atomic<int> g_shared{-1}; // where the shared expert's gate/up runs; -1: not yet read
 
 constexpr int kMaxI = kMaxInter;   // kMaxB, kMaxE, kMaxK, kMaxInter: route_core.hpp
+constexpr int kMaxLatent = 8192;   // latent rows of moe_route_latent
 static_assert(kNoallocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
 constexpr size_t kAlign = 256;
 
@@ -82,6 +84,22 @@ int schedule() {
     int expect = -1;
     g_sched.compare_exchange_strong(expect, f);
     f = g_sched.load();
+  }
+  return f;
+}
+
+int shared_schedule() {
+  int f = g_shared.load();
+  if (f < 0) {
+    f = MOE_SHARED_AUTO;
+    const char* e = getenv("MOE_SHARED_SCHEDULE");
+    if (e) {
+      if (!strcmp(e, "up")) f = MOE_SHARED_IN_UP;
+      else if (!strcmp(e, "router")) f = MOE_SHARED_IN_ROUTER;
+    }
+    int expect = -1;
+    g_shared.compare_exchange_strong(expect, f);
+    f = g_shared.load();
   }
   return f;
 }
@@ -195,7 +213,7 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 // the fused barrier lines in the header, then h, ids, weights and plan.
 struct BlockWs {
   SkinnyWs route;
-  size_t route_off, ffn_h, ids, w, plan, sync, up_part, ht, total;
+  size_t route_off, ffn_h, ids, w, plan, sync, up_part, ht, side_h, side_y, total;
   int hld;
 };
 
@@ -228,6 +246,12 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
     b.ht = o;
     o = up(o + (size_t)2 * ht_rows(B, k, E) * b.hld * 2);
   }
+  // the shared expert on a side stream (moe_block_streams): its h (B rows)
+  // and its outputs fp32 [B][d]
+  b.side_h = o;
+  o = up(o + (size_t)B * b.hld * 4);
+  b.side_y = o;
+  o = up(o + (size_t)B * d * 4);
   b.total = o;
   return b;
 }
@@ -416,6 +440,13 @@ int moe_set_variant(int variant) {
   return prev;
 }
 
+int moe_set_shared_schedule(int sched) {
+  const int prev = shared_schedule();
+  if (sched < MOE_SHARED_AUTO || sched > MOE_SHARED_IN_ROUTER) return prev;
+  g_shared.store(sched);
+  return prev;
+}
+
 int moe_set_block_schedule(int sched) {
   const int prev = schedule();
   if (sched < MOE_SCHEDULE_AUTO || sched > MOE_SCHEDULE_FUSED) return prev;
@@ -444,6 +475,9 @@ size_t moe_workspace_bytes(int op, int dtype, int B, int d, int E, int k, int I,
     case MOE_OP_BLOCK:
       if (E <= 0 || d <= 0 || k <= 0) return 0;
       return block_ws(bf16, B, d, E, k, I, Is).total;
+    case MOE_OP_ROUTE_LATENT:   // N = L, the latent rows
+      if (E <= 0 || d <= 0 || N <= 0) return 0;
+      return skinny_ws(B, E + N, d, bf16, true).total;
   }
   return 0;
 }
@@ -555,6 +589,42 @@ moe_status_t moe_route(int dtype, int B, int d, int E, int k, const void* X, con
   return s;
 }
 
+moe_status_t moe_route_latent(int dtype, int B, int d, int E, int k, int L, const void* X, const void* Wr,
+                              const void* Wl, const float* bias, int bias_ld, int32_t* topk_ids, float* topk_w,
+                              int32_t* plan, void* latent_out, int latent_dtype, float* logits_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status_t s = check_route_dims(dtype, B, d, E, k);
+  if (s) return s;
+  if (L <= 0) return fail(MOE_EINVAL, "L=%d", L);
+  if (L % 16 || L > kMaxLatent) return fail(MOE_EUNSUPPORTED, "L=%d must be a multiple of 16 up to %d", L, kMaxLatent);
+  if (E % 4) return fail(MOE_EUNSUPPORTED, "E=%d must be a multiple of 4 with a latent projection", E);
+  if (latent_dtype != dtype && latent_dtype != MOE_DT_F32) return fail(MOE_EINVAL, "latent_dtype %d", latent_dtype);
+  if (!aligned(X) || !aligned(Wr) || !aligned(Wl) || !aligned(latent_out))
+    return fail(MOE_EINVAL, "X, Wr, Wl or latent_out null or misaligned");
+  if (!aligned(topk_ids) || !aligned(topk_w) || !aligned(plan))
+    return fail(MOE_EINVAL, "topk_ids, topk_w or plan null or misaligned");
+  if (bias && !aligned(bias)) return fail(MOE_EINVAL, "bias misaligned");
+  if (bias && bias_ld != 0 && bias_ld != E) return fail(MOE_EINVAL, "bias_ld must be 0 or E");
+  if (logits_out && !aligned(logits_out)) return fail(MOE_EINVAL, "logits_out misaligned");
+  const int bf16 = dtype == MOE_DT_BF16;
+  int v;
+  if ((s = resolve_skinny(bf16, B, d, &v))) return s;
+  const size_t need = skinny_ws(B, E + L, d, bf16, true).total;
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  SkinnyLaunch a = route_launch(dtype, v, B, d, E + L, k, X, Wr, bias, bias_ld, topk_ids, topk_w, plan, logits_out,
+                                static_cast<char*>(ws), 1);
+  a.Wlat = Wl;
+  a.L = L;
+  a.latent_out = latent_out;
+  a.latent_bf16 = latent_dtype == MOE_DT_BF16;
+  char desc[200];
+  s = hip_status(launch_skinny(a, reinterpret_cast<hipStream_t>(stream), desc, sizeof desc), "moe_route_latent launch");
+  if (!s) record("moe_route_latent", B, desc);
+  return s;
+}
+
 moe_status_t moe_expert_ffn(int dtype, int B, int d, int E, int k, int I, const void* X,
                             const int32_t* plan, const void* W13, const void* W2, int Is,
                             const void* Ws13, const void* Ws2, float* Yslot, void* ws,
@@ -642,7 +712,8 @@ moe_status_t block_check(const BlockArgs& a, int* v, int* force, BlockWs* L) {
 }
 
 // The block's launches on workspace w (layout L), arguments already checked.
-moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, char* w, hipStream_t st) {
+moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, char* w, hipStream_t st,
+                       hipStream_t side = nullptr, hipEvent_t fork = nullptr, hipEvent_t join = nullptr) {
   const int dtype = A.dtype, B = A.B, d = A.d, E = A.E, k = A.k, I = A.I, Is = A.Is;
   const void *X = A.X, *Wr = A.Wr, *W13 = A.W13, *W2 = A.W2, *Ws13 = A.Ws13, *Ws2 = A.Ws2;
   const float* bias = A.bias;
@@ -704,13 +775,38 @@ moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, c
     record("moe_block", B, d1);
     return MOE_OK;
   }
+  if (side && (!route_in_up || !Ws13 || fused))
+    return fail(MOE_EUNSUPPORTED, "the shared expert runs on a side stream only in the small-batch schedule "
+                                  "(B*k <= 64, vector shape) with a shared expert");
+  char d0[64] = "";
+  if (side) {
+    // the shared expert alone on the side stream, overlapping routing and
+    // the routed gate/up: a launch with k = 0, so h rows and outputs are the
+    // B tokens (same products as in the block's own launches)
+    ExpertLaunch exs = ex;
+    exs.k = 0;
+    exs.h = reinterpret_cast<float*>(w + L.side_h);
+    exs.Yslot = reinterpret_cast<float*>(w + L.side_y);
+    exs.ht_hi = exs.ht_lo = nullptr;
+    if ((s = hip_status(hipEventRecord(fork, st), "fork event"))) return s;
+    if ((s = hip_status(hipStreamWaitEvent(side, fork, 0), "side stream wait"))) return s;
+    if ((s = hip_status(launch_shared_up(exs, side), "shared gate/up launch"))) return s;
+    if ((s = hip_status(launch_shared_down(exs, side), "shared down launch"))) return s;
+    if ((s = hip_status(hipEventRecord(join, side), "join event"))) return s;
+    snprintf(d0, sizeof d0, "shared on side stream; ");
+  }
   if (route_in_up) {
-    ex.skip_shared = 0;
+    // the shared expert's gate/up: in the gate/up launch (its tiles first,
+    // streaming while the other workgroups select), in the router launch
+    // (one pass over x), or on the side stream
+    const int ssched = shared_schedule();
+    const bool in_router = Ws13 && !side && ssched == MOE_SHARED_IN_ROUTER;
+    ex.skip_shared = (in_router || side) ? 1 : 0;
     ex.ids_out = ids;
     ex.w_out = tw;
     ex.plan_out = plan;
     if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, st, d1,
-                       sizeof d1, nullptr, 0, &ex.logits)))
+                       sizeof d1, in_router ? &ex : nullptr, 0, &ex.logits)))
       return s;
   } else {
     // the vector router launch carries the shared expert's vector gate/up;
@@ -734,11 +830,15 @@ moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, c
   {
     ExpertLaunch exd = ex;
     exd.ids_in = nullptr;   // the down launch reads the plan the gate/up launch stored
+    if (side) {
+      exd.y_shared = reinterpret_cast<const float*>(w + L.side_y);
+      if ((s = hip_status(hipStreamWaitEvent(st, join, 0), "join wait"))) return s;
+    }
     if ((s = hip_status(launch_expert_down_combine(exd, st, d3, sizeof d3), "expert down+combine launch")))
       return s;
   }
   char desc[480];
-  snprintf(desc, sizeof desc, "route[%s] %s; %s", d1, d2, d3);
+  snprintf(desc, sizeof desc, "%sroute[%s] %s; %s", d0, d1, d2, d3);
   record("moe_block", B, desc);
   return MOE_OK;
 }
@@ -760,6 +860,32 @@ moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, con
   if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
   if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   return block_run(a, v, force, L, static_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_block_streams(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
+                               const void* Wr, const float* bias, int bias_ld, const void* W13,
+                               const void* W2, const void* Ws13, const void* Ws2, void* out,
+                               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream,
+                               void* side_stream, void* fork_event, void* join_event) {
+  g_err[0] = 0;
+  const BlockArgs a = {dtype, B, d, E, k, I, Is, X, Wr, bias, bias_ld, W13, W2, Ws13, Ws2, out, topk_ids, topk_w};
+  int v, force;
+  BlockWs L;
+  moe_status_t s = block_check(a, &v, &force, &L);
+  if (s) return s;
+  if (!side_stream || !fork_event || !join_event)
+    return fail(MOE_EINVAL, "side_stream, fork_event and join_event are required");
+  if (side_stream == stream) return fail(MOE_EINVAL, "side_stream must differ from stream");
+  if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");
+  if (ws_bytes < L.total) return fail(MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  const int bf16 = dtype == MOE_DT_BF16;
+  const bool small = expert_paths(bf16, force, B) == kPathValu && v != VAR_MFMA && B * k <= 64;
+  if (!small || !Ws13 || schedule() == MOE_SCHEDULE_FUSED)
+    return fail(MOE_EUNSUPPORTED, "the shared expert runs on a side stream only in the three-launch small-batch "
+                                  "schedule (B*k <= 64, vector shape) with a shared expert");
+  return block_run(a, v, force, L, static_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream),
+                   reinterpret_cast<hipStream_t>(side_stream), reinterpret_cast<hipEvent_t>(fork_event),
+                   reinterpret_cast<hipEvent_t>(join_event));
 }
 
 moe_status_t moe_block_noalloc(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,

@@ -340,7 +340,7 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * rt;
   const YSink sink = {s_y, 1, r0, rt};
-  const int ne = entries(a, p, true);
+  const int ne = entries(a, p, a.y_shared == nullptr);   // the shared entry, unless computed elsewhere
   // entries by falling token count, dealt to the waves in snake order
   // (w, 2nw-1-w, 2nw+w, ...) so their token totals come out close
   __shared__ int s_next;
@@ -385,12 +385,36 @@ void expert_down_combine_kernel(ExpertLaunch a) {
     const int t = idx / rt, r = idx % rt;
     if (r0 + r >= a.d) continue;
     const float v = combine_one(s_tw + t * a.k, a.k, has_shared, [&](int j) {
+      if (j == a.k && a.y_shared) return a.y_shared[(size_t)t * a.d + r0 + r];
       return s_y[(j < a.k ? t * a.k + j : a.B * a.k + t) * rt + r];
     });
     const size_t o = (size_t)t * a.d + r0 + r;
     if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[o] = f32_to_bf16(v);
     else reinterpret_cast<float*>(a.out)[o] = v;
   }
+}
+
+// ---- the shared expert alone (side stream) ---------------------------------
+
+// Gate/up + SwiGLU of the shared expert: tasks of 2 pairs on 4 waves (waves
+// w and w + 2 take the two halves of d for pair w), the tasks and products
+// of the shared tiles in expert_up_kernel, hence the same bits.
+template <typename T>
+__global__ __launch_bounds__(kUpWaves * 64) void shared_up_kernel(ExpertLaunch a) {
+  constexpr int PPT = kUpPairsValu;
+  __shared__ float s_red[PPT * 2 * kPartStride];
+  const int wave = threadIdx.x >> 6;
+  up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), blockIdx.x * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
+}
+
+// Down projection of the shared expert: 64 output rows per workgroup, 16
+// per wave (down_valu, the products of the block's vector down), into
+// a.Yslot laid out [B][1][d] (a launch with k = 0).
+template <typename T>
+__global__ __launch_bounds__(256) void shared_down_kernel(ExpertLaunch a) {
+  const int wave = threadIdx.x >> 6;
+  const YSink sink = {a.Yslot, 0, 0, 0};
+  down_dispatch<T, kPathValu>(a, nullptr, wave_uniform(shared_view(a)), blockIdx.x * kDownRows + wave * 16, sink);
 }
 
 // ---- combine -------------------------------------------------------------------
@@ -507,6 +531,20 @@ hipError_t launch_expert_down_combine(const ExpertLaunch& a0, hipStream_t st, ch
   if (desc)
     snprintf(desc, desc_len, "down+combine grid=%d rows/wg=%d waves/wg=%d%s force=%d", g, rt, nw,
              pipe ? " prefetch" : (paired ? " paired" : ""), a.force);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_up(const ExpertLaunch& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.Is + kUpPairsValu - 1) / kUpPairsValu)), block(kUpWaves * 64);
+  if (a.bf16) launch(K_EXPERT_UP, shared_up_kernel<bf16_t>, grid, block, 0, st, a);
+  else launch(K_EXPERT_UP, shared_up_kernel<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_down(const ExpertLaunch& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.d + kDownRows - 1) / kDownRows)), block(256);
+  if (a.bf16) launch(K_NONE, shared_down_kernel<bf16_t>, grid, block, 0, st, a);
+  else launch(K_NONE, shared_down_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -49,6 +49,10 @@ struct ExpertLaunch {
   // workgroup builds the plan from them; the last also stores it (plan_out)
   const int32_t* ids_in;
   int down_rows;            // rows per workgroup of the prefetching down+combine
+  // shared expert computed on a side stream: its per-token output fp32
+  // [B][d]; the down+combine launch then leaves the shared entry out and
+  // adds y_shared in the combine (null: the shared entry is one of its own)
+  const float* y_shared;
   // gate/up on the matrix shape: the K-slice partial sums of tiles cut in
   // two (up_part, null: none are cut) and one arrival counter per such tile
   // (up_counter, zero on entry and left at zero)
@@ -76,8 +80,8 @@ struct SkinnyLaunch {
   int finish;
   const float* bias;
   int bias_ld;
-  float* logits;            // [M][N] workspace
-  float* logits_out;        // optional copy [M][N]
+  float* logits;            // [M][E] workspace (E = N - L router rows)
+  float* logits_out;        // optional copy [M][E]
   uint32_t* done_counter;   // zero on entry
   int k;
   int32_t* topk_ids;
@@ -101,6 +105,13 @@ struct SkinnyLaunch {
   // launch builds the plan from the ids
   int defer;
   int plan_by_consumer;
+  // latent input projection concatenated with the router (router mode):
+  // rows E .. N-1 of the product (E = N - L) are Wlat [L][K]; their sums go
+  // to latent_out [M][L] (no bias), in the element type or fp32
+  const void* Wlat;
+  int L;
+  void* latent_out;
+  int latent_bf16;
 };
 
 // The whole block in one launch (fused kernel, small batch on the vector
@@ -158,6 +169,11 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
 hipError_t launch_expert_down(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_expert_down_combine(const ExpertLaunch& a, hipStream_t st, char* desc, size_t desc_len);
 hipError_t launch_combine(const CombineLaunch& a, hipStream_t st);
+// The shared expert alone (a launch with k = 0: h rows and outputs are the
+// B tokens): gate/up + SwiGLU into a.h, then the down projection into
+// a.Yslot fp32 [B][d], with the same products as the block's launches.
+hipError_t launch_shared_up(const ExpertLaunch& a, hipStream_t st);
+hipError_t launch_shared_down(const ExpertLaunch& a, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // Read-only streaming yardstick (stream.hip): `workgroups` workgroups read
 // bytes (a multiple of 16) of src; sink[w] = XOR of slice w's 32-bit words.
@@ -170,7 +186,7 @@ hipError_t launch_moe_block_fused(BlockLaunch& f, hipStream_t st, char* desc, si
 // moe_block_noalloc: bytes of the library's device-resident scratch (one
 // array per GPU, noalloc.hip), and the device address of the current
 // device's copy (looked up once per device).
-constexpr size_t kNoallocScratchBytes = (size_t)24 << 20;
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 // Row blocks of the skinny kernel for a given variant (host-side geometry).

@@ -51,7 +51,7 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
   const int nw = (blockDim.x >> 6) < NTK ? (blockDim.x >> 6) : NTK;
   const int wave = threadIdx.x >> 6;
   if (wave >= nw) return;
-  const int E = a.N, M = a.M, k = a.k;
+  const int E = a.N - a.L, M = a.M, k = a.k;
   for (int t0 = wave; t0 < M; t0 += nw * QB) {
     float lv[QB][kNI];
 #pragma unroll
@@ -73,7 +73,7 @@ __device__ __forceinline__ void topk_tokens(const SkinnyLaunch& a, TopkScratch* 
 // the whole workgroup, into a.plan.
 __device__ __forceinline__ void route_plan(const SkinnyLaunch& a, const int32_t* s_ids) {
   __shared__ PlanScratch s_ps;
-  plan_block(s_ids, a.M * a.k, a.k, a.N, a.plan, nullptr, s_ps);
+  plan_block(s_ids, a.M * a.k, a.k, a.N - a.L, a.plan, nullptr, s_ps);
 }
 
 // Top-k of every token and the plan, by one workgroup.  NTK: waves that
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x;
-  const int E = a.N, k = a.k;
+  const int E = a.N - a.L, k = a.k;   // router rows; the partial rows hold all N
   float lv[kNI];
   // wave 0's bias values, requested with the partial sums (requested after
   // the sums, they cost one more memory round trip: 1.2 us at batch 64)
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
 #pragma unroll
       for (int q = 0; q < kFinishSlices; ++q) {
         const int qc = qb + q < q1 ? qb + q : q1 - 1;
-        const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * E);
+        const f32x4* row = reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * a.N);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           const int j = lane + 64 * v;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
 #pragma unroll
       for (int i = 0; i < kNI; ++i) {
         const int e = lane + 64 * i;
-        lv[i] += a.part[((size_t)q * a.M + t) * E + (e < E ? e : E - 1)];
+        lv[i] += a.part[((size_t)q * a.M + t) * a.N + (e < E ? e : E - 1)];
       }
   }
   if (wave == 0) {
@@ -190,6 +190,27 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
     }
     topk_wave(lv, E, k, s_tk[0], s_ids + t * k, s_w + t * k, a.topk_ids + (size_t)t * k,
               a.topk_w + (size_t)t * k);
+  }
+  if (a.L) {
+    // the latent projection columns E .. N-1 of this token: every slice's
+    // partials of 4 columns per thread, requested per group of slices, added
+    // in slice order (E and L multiples of 4)
+    for (int c = 4 * (int)threadIdx.x; c < a.L; c += 4 * (int)blockDim.x) {
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < a.ks_n; qb += kFinishSlices) {
+        f32x4 pv[kFinishSlices];
+#pragma unroll
+        for (int q = 0; q < kFinishSlices; ++q) {
+          const int qc = qb + q < a.ks_n ? qb + q : a.ks_n - 1;
+          pv[q] = *reinterpret_cast<const f32x4*>(a.part + ((size_t)qc * a.M + t) * a.N + E + c);
+        }
+#pragma unroll
+        for (int q = 0; q < kFinishSlices; ++q)
+          if (qb + q < a.ks_n) sum += pv[q];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) finish_value(a, t, E + c + i, sum[i]);
+    }
   }
   if (a.plan_by_consumer) return;   // the gate/up launch builds the plan from the ids
   if (!arrive_last(a.done_counter, gridDim.x, &s_last)) return;
@@ -301,12 +322,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   const int J = a.K / 32;
   const int s0 = ks * a.ks_steps;
   const int s1 = s0 + a.ks_steps < J ? s0 + a.ks_steps : J;
-  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
   const int ra = n0 + mfma_row_a(), rb = n0 + mfma_row_b();
   const bool oka = ra < a.N, okb = rb < a.N;
-  const bf16_t* wa = W + (size_t)(oka ? ra : a.N - 1) * a.K + mfma_col_off();
-  const bf16_t* wb = W + (size_t)(okb ? rb : a.N - 1) * a.K + mfma_col_off();
+  const bf16_t* wa = product_row<bf16_t>(a, ra) + mfma_col_off();
+  const bf16_t* wb = product_row<bf16_t>(a, rb) + mfma_col_off();
   const bf16_t* xrow[PPT];
   bool xok[PPT];
 #pragma unroll
@@ -411,8 +431,18 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   }
 }
 
+// Router with latent rows on the vector shape: 4 rows per 8-wave workgroup,
+// so that with the router kernel's register count (one 16-wave or two
+// 8-wave workgroups per compute unit) the E + L rows (1408 at E = 384, L =
+// 1024) run in one round of resident workgroups: two rows per 16-wave
+// workgroup took three rounds, and the merged product was slower than the
+// router and the latent product launched apart.
+constexpr int kRouterLatentRows = 4;
+constexpr int kRouterLatentWaves = 8;
+
 int skinny_rows_per_block(int variant, int router) {
   if (variant == VAR_MFMA) return kMfmaRows;
+  if (router == 2) return kRouterLatentRows;
   if (router) return kRouterRows;
   if (variant == VAR_SPLITK) return 4;
   return 2;
@@ -444,8 +474,10 @@ int shared_up_tiles_host(const ExpertLaunch& ex, int nw) {
 
 hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, size_t desc_len) {
   SkinnyLaunch a = a0;
-  const int rows = skinny_rows_per_block(a.variant, a.router);
+  const bool latent_rows = a.router && a.L > 0 && a.variant != VAR_MFMA;
+  const int rows = skinny_rows_per_block(a.variant, latent_rows ? 2 : a.router);
   const int nrg = (a.N + rows - 1) / rows;
+  if (latent_rows) a.S = kRouterLatentWaves;
   const int nw = a.S;
   if (a.variant == VAR_MFMA) {
     if (a.router && a.finish) router_mfma_slices(a.M, a.N, a.K, &a.ks_n, &a.ks_steps);
@@ -494,6 +526,20 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
       else hipLaunchKernelGGL(route_finish_kernel, fg, dim3(kFinishWaves * 64), 0, st, a);
     }
     name = split ? "mfma + finish launch" : "mfma";
+  } else if (latent_rows) {
+    name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
+    constexpr int RL = kRouterLatentRows;
+    if (a.bf16) {
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<bf16_t, RL, 1, 2, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<bf16_t, RL, 2, 2, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<bf16_t, RL, 4, 1, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<bf16_t, RL, 8, 1, true>, grid, block, 0, st, a);
+    } else {
+      if (a.M <= 1) launch(K_ROUTE, skinny_valu_kernel<float, RL, 1, 2, true>, grid, block, 0, st, a);
+      else if (a.M <= 2) launch(K_ROUTE, skinny_valu_kernel<float, RL, 2, 2, true>, grid, block, 0, st, a);
+      else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<float, RL, 4, 1, true>, grid, block, 0, st, a);
+      else launch(K_ROUTE, skinny_valu_kernel<float, RL, 8, 1, true>, grid, block, 0, st, a);
+    }
   } else if (a.router) {
     name = a.variant == VAR_SPLITK ? "splitk" : "gemv";
     if (a.bf16) {

@@ -15,12 +15,28 @@
 
 namespace moe {
 
-// Result (t, n) of the product: a router logit (+ bias) or a stored value.
+// Weight row n of the product (clamped to N - 1): a router or dense row, or,
+// from E = N - L on, a row of the latent input projection.
+template <typename T>
+__device__ __forceinline__ const T* product_row(const SkinnyLaunch& a, int n) {
+  n = n < a.N ? n : a.N - 1;
+  const int E = a.N - a.L;
+  return n < E ? reinterpret_cast<const T*>(a.W) + (size_t)n * a.K
+               : reinterpret_cast<const T*>(a.Wlat) + (size_t)(n - E) * a.K;
+}
+
+// Result (t, n) of the product: a router logit (+ bias), a latent projection
+// value, or a stored value.
 __device__ __forceinline__ void finish_value(const SkinnyLaunch& a, int t, int n, float v) {
-  if (a.router) {
+  const int E = a.N - a.L;
+  if (a.router && n >= E) {
+    const size_t o = (size_t)t * a.L + (n - E);
+    if (a.latent_bf16) reinterpret_cast<bf16_t*>(a.latent_out)[o] = f32_to_bf16(v);
+    else reinterpret_cast<float*>(a.latent_out)[o] = v;
+  } else if (a.router) {
     if (a.bias) v += a.bias[(size_t)t * a.bias_ld + n];
-    st_coherent(&a.logits[(size_t)t * a.N + n], v);   // read by other workgroups of the launch
-    if (a.logits_out) a.logits_out[(size_t)t * a.N + n] = v;
+    st_coherent(&a.logits[(size_t)t * E + n], v);   // read by other workgroups of the launch
+    if (a.logits_out) a.logits_out[(size_t)t * E + n] = v;
   } else {
     const size_t o = (size_t)t * a.N + n;
     // the residual is read and the result stored by the same thread, so Y
@@ -41,12 +57,11 @@ __device__ __forceinline__ void valu_rows(const SkinnyLaunch& a, int n0, float* 
   constexpr int VEC = Elem<T>::VEC;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const T* W = reinterpret_cast<const T*>(a.W);
   const T* X = reinterpret_cast<const T*>(a.X);
   const T* wr[RB];
   const T* xr[MB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) wr[r] = W + (size_t)(n0 + r < a.N ? n0 + r : a.N - 1) * a.K;
+  for (int r = 0; r < RB; ++r) wr[r] = product_row<T>(a, n0 + r);
 #pragma unroll
   for (int t = 0; t < MB; ++t) xr[t] = X + (size_t)(t < a.M ? t : 0) * a.K;
   const int C = a.K / VEC;

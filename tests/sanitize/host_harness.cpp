@@ -30,7 +30,7 @@ int main() {
         if (B > 0) EXPECT(moe_plan_words(B, k, E) == 2 + 2 * (B * k < E ? B * k : E) + B * k);
         for (int op = -1; op <= 4; ++op)
           for (int dt = 0; dt <= 1; ++dt) {
-            const size_t n = moe_workspace_bytes(op, dt, B, 7168, E, k, 256, 128, 3072, 7168);
+            const size_t n = moe_workspace_bytes(op, dt, B, 16384, E, k, 256, 256, 3072, 7168);
             if (op == MOE_OP_BLOCK && B >= 1 && B <= 64 && E <= 512 && k <= 16 && dt == MOE_DT_BF16)
               EXPECT(n > 0 && n <= MOE_NOALLOC_SCRATCH_BYTES);
           }

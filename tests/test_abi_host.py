@@ -183,3 +183,33 @@ def test_forced_variant_scope():
     finally:
         mb.set_variant(prev)
     assert mb.set_variant(prev) == prev
+
+
+def route_latent(**kw):
+    a = dict(dt=mb.DT_BF16, B=8, d=7168, E=384, k=8, L=1024, X=A, Wr=A, Wl=A, bias=None, ld=0, ids=A, w=A,
+             plan=A, lat=A, ldt=mb.DT_BF16, lo=None, ws=A, wsb=BIG)
+    a.update(kw)
+    return lib.moe_route_latent(a["dt"], a["B"], a["d"], a["E"], a["k"], a["L"], a["X"], a["Wr"], a["Wl"],
+                                a["bias"], a["ld"], a["ids"], a["w"], a["plan"], a["lat"], a["ldt"], a["lo"],
+                                a["ws"], a["wsb"], 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), mb.EINVAL),
+    (dict(L=24), mb.EUNSUPPORTED),
+    (dict(L=8208), mb.EUNSUPPORTED),
+    (dict(E=382), mb.EUNSUPPORTED),
+    (dict(ldt=7), mb.EINVAL),
+    (dict(Wl=None), mb.EINVAL),
+    (dict(lat=MIS), mb.EINVAL),
+    (dict(B=65), mb.EUNSUPPORTED),
+    (dict(wsb=4096), mb.EWORKSPACE),
+])
+def test_route_latent_validation(kw, status):
+    assert route_latent(**kw) == status
+
+
+def test_route_latent_workspace_covers_the_latent_rows():
+    f = mb.workspace_bytes
+    assert f(mb.OP_ROUTE_LATENT, mb.DT_BF16, B=64, d=7168, E=384, k=8, N=1024) > \
+        f(mb.OP_ROUTE, mb.DT_BF16, B=64, d=7168, E=384, k=8)
