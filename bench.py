@@ -397,9 +397,23 @@ def shared_placements(cfg, sets, R, ws, args, torch, mb):
         mb.moe_block_streams(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, side, fork, join,
                              s["Ws13"], s["Ws2"], s["bias"], s["bias_ld"], topk_ids=s["ids"])
 
+    # the next block's routing-independent weights (router, shared expert)
+    # read into the cache by a small kernel on a second stream while this
+    # block runs (moe_prefetch); ordered after the block's start by an event
+    sink = torch.empty(32, dtype=torch.int32, device="cuda")
+    starts = [torch.cuda.Event() for _ in range(4)]
+
+    def prefetched(i):
+        ev = starts[i % 4]
+        ev.record()
+        side.wait_event(ev)
+        n = sets[(i + 1) % R]
+        mb.prefetch([n["Wr"], n["Ws13"], n["Ws2"]], sink, stream=side)
+        block(i)
+
     out = {}
     for label, place, step in (("gate_up_launch", "up", block), ("router_launch", "router", block),
-                               ("side_stream", "up", streams)):
+                               ("side_stream", "up", streams), ("gate_up_launch_next_prefetched", "up", prefetched)):
         prev = mb.set_shared_schedule(place)
         try:
             info = {}

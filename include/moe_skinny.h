@@ -199,6 +199,21 @@ size_t moe_workspace_status_offset(void);
  * MOE_EINVAL otherwise. */
 moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
+/* Weight prefetch (WRITEUP part 1 §4: weights that are about to be used are
+ * read into the cache by a kernel on a side stream while the running work
+ * uses little memory bandwidth).  Reads n (1..8) ranges of device memory --
+ * ptrs[i] 16-byte aligned, bytes[i] a positive multiple of 16; ptrs and
+ * bytes are HOST arrays -- with cached 128-bit loads, so the lines stay in
+ * L2 and the Infinity Cache for the next kernels that read them, in
+ * `workgroups` workgroups (1..65536) of 256 threads, each over one slice
+ * of every range, and stores the XOR of the words it read to sink[w] (uint32
+ * [workgroups], device memory): the XOR of all of sink is the XOR of every
+ * word of the ranges.  Enqueued on `stream` (typically a second stream,
+ * default priority, ordered against the block's stream by the caller's
+ * events).  MOE_EINVAL on a bad argument. */
+moe_status_t moe_prefetch(int n, const void* const* ptrs, const size_t* bytes, uint32_t* sink, int workgroups,
+                          void* stream);
+
 /* Zero-fill a workspace (with a kernel, so it may be captured in a graph). */
 moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 

@@ -42,6 +42,7 @@ SIGNATURES = {
     "moe_workspace_init": (_I, [_P, _Z, _P]),
     "moe_workspace_status_offset": (_Z, []),
     "moe_stream_read": (_I, [_P, _Z, _P, _I, _P]),
+    "moe_prefetch": (_I, [_I, _P, _P, _P, _I, _P]),
     "moe_profile_events": (_I, [_I, _P, _P]),
     "skinny_gemm": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _Z, _P]),
     "skinny_gemm_residual": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _Z, _P]),
@@ -421,3 +422,24 @@ def stream_read(src, sink, stream=None):
     a.on_gpu()
     _check(lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
                                _stream(stream)))
+
+
+def prefetch(tensors, sink, stream=None):
+    """Cached reads of up to 8 contiguous device tensors (byte sizes multiples
+    of 16) into L2 and the Infinity Cache, in sink.numel() workgroups; sink
+    (int32 [workgroups]) receives the XOR of each workgroup's words."""
+    a = _Args()
+    tensors = [t for t in tensors if t is not None]
+    if not 1 <= len(tensors) <= 8:
+        raise ValueError("1 to 8 tensors expected, got %d" % len(tensors))
+    for i, t in enumerate(tensors):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError("tensor %d: a contiguous torch.Tensor expected" % i)
+        a.tensors.append(("tensor %d" % i, t))
+    _shape("sink", sink, 1)
+    a.arr("sink", sink, tuple(sink.shape), torch.int32)
+    a.on_gpu()
+    n = len(tensors)
+    ptrs = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
+    sizes = (ctypes.c_size_t * n)(*[t.numel() * t.element_size() for t in tensors])
+    _check(lib.moe_prefetch(n, ptrs, sizes, _ptr(sink), sink.numel(), _stream(stream)))

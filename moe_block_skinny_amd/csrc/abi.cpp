@@ -495,6 +495,24 @@ moe_status_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int 
                     "stream read launch");
 }
 
+moe_status_t moe_prefetch(int n, const void* const* ptrs, const size_t* bytes, uint32_t* sink, int workgroups,
+                          void* stream) {
+  g_err[0] = 0;
+  if (n < 1 || n > kMaxPrefetch) return fail(MOE_EINVAL, "n=%d outside 1..%d", n, kMaxPrefetch);
+  if (!ptrs || !bytes) return fail(MOE_EINVAL, "ptrs or bytes null");
+  if (!aligned(sink)) return fail(MOE_EINVAL, "sink null or misaligned");
+  if (workgroups < 1 || workgroups > 65536) return fail(MOE_EINVAL, "workgroups=%d outside 1..65536", workgroups);
+  PrefetchRanges r = {};
+  r.n = n;
+  for (int i = 0; i < n; ++i) {
+    if (!aligned(ptrs[i])) return fail(MOE_EINVAL, "range %d null or misaligned", i);
+    if (bytes[i] == 0 || bytes[i] % 16) return fail(MOE_EINVAL, "range %d: %zu bytes, not a positive multiple of 16", i, bytes[i]);
+    r.ptr[i] = ptrs[i];
+    r.bytes[i] = bytes[i];
+  }
+  return hip_status(launch_prefetch(r, sink, workgroups, reinterpret_cast<hipStream_t>(stream)), "prefetch launch");
+}
+
 moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!aligned(ws)) return fail(MOE_EINVAL, "ws null or misaligned");

@@ -178,6 +178,14 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // Read-only streaming yardstick (stream.hip): `workgroups` workgroups read
 // bytes (a multiple of 16) of src; sink[w] = XOR of slice w's 32-bit words.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t st);
+// Weight prefetch (stream.hip): cached reads of up to kMaxPrefetch ranges.
+constexpr int kMaxPrefetch = 8;
+struct PrefetchRanges {
+  const void* ptr[kMaxPrefetch];
+  size_t bytes[kMaxPrefetch];   // multiples of 16
+  int n;
+};
+hipError_t launch_prefetch(const PrefetchRanges& r, uint32_t* sink, int workgroups, hipStream_t st);
 // Fused block: the workgroups it would launch (0: the fused kernel cannot
 // hold the whole grid resident, so it must not be used), and the launch.
 int moe_block_fused_grid(const ExpertLaunch& ex, int bf16, int B);

@@ -24,3 +24,48 @@ def test_stream_read_reads_every_word(nbytes, wg):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy())
     assert got == np.bitwise_xor.reduce(host)
+
+
+def test_prefetch_reads_every_range():
+    """moe_prefetch over several ranges of ragged sizes: the XOR of its sink
+    equals the XOR of every word of every range."""
+    rng = np.random.default_rng(9)
+    sizes = [16, 4096 * 3 + 32, (1 << 20) + 16 * 5, 5505024]
+    bufs = [torch.from_numpy(rng.integers(-2 ** 31, 2 ** 31 - 1, n // 4, dtype=np.int64).astype(np.int32)).cuda()
+            for n in sizes]
+    want = np.bitwise_xor.reduce(np.concatenate([b.cpu().numpy() for b in bufs]))
+    for wg in (1, 33, 512):
+        sink = torch.full((wg,), -1, dtype=torch.int32, device="cuda")
+        say("prefetch ranges", len(bufs), "workgroups", wg)
+        mb.prefetch(bufs, sink)
+        torch.cuda.synchronize()
+        assert np.bitwise_xor.reduce(sink.cpu().numpy()) == want
+
+
+def test_block_unchanged_by_a_concurrent_prefetch():
+    """A prefetch of the next block's router and shared-expert weights on a
+    second stream, running while the block runs, leaves the block's output
+    bits unchanged (it only reads)."""
+    from tests import inputs
+    from tests.test_gpu_parity import gpu_weights
+    from tests.gpu_util import dev
+    c = inputs.case("tp16_b1")
+    cfg = c.cfg
+    W13, W2, Ws13, Ws2 = gpu_weights(c)
+    X, Wr = dev(c.X), dev(c.Wr)
+    ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                         I=cfg.I, Is=cfg.Is))
+    ref = torch.empty((cfg.B, cfg.d), dtype=torch.bfloat16, device="cuda")
+    mb.moe_block(X, Wr, cfg.k, W13, W2, ref, ws, Ws13, Ws2)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    sink = torch.empty(64, dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        out = torch.full_like(ref, float("nan"))
+        ev = torch.cuda.Event()
+        ev.record()
+        side.wait_event(ev)
+        mb.prefetch([Wr, Ws13, Ws2], sink, stream=side)
+        mb.moe_block(X, Wr, cfg.k, W13, W2, out, ws, Ws13, Ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
