@@ -345,8 +345,15 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   // (w, 2nw-1-w, 2nw+w, ...) so their token totals come out close
   __shared__ int s_next;
   if (wave == 0) {
-    if constexpr (PAIRED) order_entries_by_tiles(a, p, ne, s_order);
-    else order_entries(a, p, ne, s_order);
+    if constexpr (PAIRED) {
+      order_entries_by_tiles(a, p, ne, s_order);
+    } else if (ne <= nw) {
+      // one entry per wave at most: the order only says which wave takes
+      // which entry, and each entry writes its own rows of s_y
+      for (int i = threadIdx.x; i < ne; i += 64) s_order[i] = i;
+    } else {
+      order_entries(a, p, ne, s_order);
+    }
     if ((threadIdx.x & 63) == 0) s_next = nw;
   }
   __syncthreads();

@@ -676,6 +676,13 @@ __device__ __forceinline__ void down_valu_pipe(const ExpertLaunch& a, const Plan
   auto view = [&](int j) { return wave_uniform(expert_view<T>(a, p, s_order[pos(j)])); };
   ExpertView v = view(0);
   u32x4 b0[R], b1[R];
+  if (pos(1) >= ne) {
+    // one entry: nothing to prefetch (re-requesting its rows as the "next"
+    // entry doubled the loads a compute unit had to take in at batch 1)
+    load(v, b0);
+    products(v, b0);
+    return;
+  }
   load(v, b0);
   for (int j = 0;;) {
     // past the last entry the "next" loads re-read this entry's rows (cached)
