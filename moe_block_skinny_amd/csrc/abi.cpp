@@ -213,7 +213,7 @@ ExpertWs expert_ws(int B, int k, int I, int Is) {
 // the fused barrier lines in the header, then h, ids, weights and plan.
 struct BlockWs {
   SkinnyWs route;
-  size_t route_off, ffn_h, ids, w, plan, sync, up_part, ht, side_h, side_y, total;
+  size_t route_off, ffn_h, ids, w, plan, ready, sync, up_part, ht, side_h, side_y, total;
   int hld;
 };
 
@@ -232,6 +232,9 @@ BlockWs block_ws(int bf16, int B, int d, int E, int k, int I, int Is) {
   o = up(o + (size_t)B * k * 4);
   b.plan = o;
   o = up(o + (size_t)moe_plan_words(B, k, E) * 4);
+  // the per-token selection's ready words (B*k <= 64 when used)
+  b.ready = o;
+  o = up(o + (size_t)B * k * 4);
   // the gate/up launch's K-slice partial sums (matrix shape, B > 8): at most
   // one task per workgroup of its grid (512) when tiles are cut, so at most
   // 256 cut tiles of 2 slices x 4 token tiles x 4 KB
@@ -338,12 +341,14 @@ moe_status_t run_route(int dt, int B, int d, int E, int k, const void* X, const 
                        const float* bias, int bias_ld, int32_t* ids, float* w, int32_t* plan,
                        float* logits_out, char* ws, hipStream_t st, char* desc, size_t dl,
                        const ExpertLaunch* shared = nullptr, int finish = 1, const float** logits = nullptr,
-                       int plan_by_consumer = 0) {
+                       int plan_by_consumer = 0, int32_t* clear = nullptr, int clear_n = 0) {
   int v;
   moe_status_t s = resolve_skinny(dt == MOE_DT_BF16, B, d, &v);
   if (s) return s;
   SkinnyLaunch a = route_launch(dt, v, B, d, E, k, X, Wr, bias, bias_ld, ids, w, plan, logits_out, ws, finish);
   a.plan_by_consumer = plan_by_consumer && v == VAR_MFMA;
+  a.clear = clear;
+  a.clear_n = clear_n;
   if (shared) a.ex = *shared;
   if (logits) *logits = a.logits;
   return hip_status(launch_skinny(a, st, desc, dl), "moe_route launch");
@@ -823,8 +828,16 @@ moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, c
     ex.ids_out = ids;
     ex.w_out = tw;
     ex.plan_out = plan;
+    // from batch 2 each token is selected once, by one gate/up workgroup,
+    // and the others wait for it (the router launch clears the words);
+    // at batch 1 every workgroup selects the one token itself (no wait)
+    if (B >= 2) {
+      ex.ready = reinterpret_cast<int32_t*>(w + L.ready);
+      ex.status = reinterpret_cast<uint32_t*>(w + moe_workspace_status_offset());
+      ex.spin_limit = 1 << 20;   // about a second of polling
+    }
     if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, st, d1,
-                       sizeof d1, in_router ? &ex : nullptr, 0, &ex.logits)))
+                       sizeof d1, in_router ? &ex : nullptr, 0, &ex.logits, 0, ex.ready, ex.ready ? B * k : 0)))
       return s;
   } else {
     // the vector router launch carries the shared expert's vector gate/up;

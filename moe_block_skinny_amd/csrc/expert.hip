@@ -74,14 +74,17 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     PlanView p;
     int task0 = blockIdx.x;
     if (here) {
+      __shared__ TopkScratch s_tk[kUpWaves];
+      __shared__ int32_t s_ids[64];
+      __shared__ float s_w[64];
+      // per-token selection: this workgroup's token first (before its
+      // shared tiles), the wait for every token's after them
+      if (a.ready) select_own_token(a, s_tk, s_ids, s_w);
       for (; task0 < tiles_s; task0 += gridDim.x) {
         up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
         __syncthreads();
       }
-      __shared__ TopkScratch s_tk[kUpWaves];
-      __shared__ int32_t s_ids[64];
-      __shared__ float s_w[64];
-      p = route_here<false>(a, s_plan, s_tk, s_ids, s_w);
+      p = a.ready ? wait_token_plan(a, s_plan, s_tk, s_ids) : route_here<false>(a, s_plan, s_tk, s_ids, s_w);
     } else {
       p = stage_plan(a, s_plan);
     }

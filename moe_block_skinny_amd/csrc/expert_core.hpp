@@ -136,6 +136,62 @@ __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s
   return plan_view(a, s_plan);
 }
 
+// Routing inside the gate/up launch with one selection per token (B >= 2,
+// B*k <= 64): workgroup t < B selects token t's top-k with one wave (the
+// same function as route_here, hence the same bits), stores its ids and
+// weights for the down launch and the caller, and id + 1 of each slot to
+// a.ready with device-coherent stores (the router launch zeroed the words).
+// Selecting all B tokens in every workgroup made the routing ALU-bound at
+// batch 8 (1024 workgroups x 8 selections: 8-17 us before the first routed
+// weight request).
+__device__ __forceinline__ void select_own_token(const ExpertLaunch& a, TopkScratch* s_tk, int32_t* s_ids,
+                                                 float* s_w) {
+  const int t = blockIdx.x, lane = threadIdx.x & 63;
+  if (t >= a.B || (threadIdx.x >> 6) != 0) return;
+  float lv[kNI];
+  load_logit_row<false>(a.logits, t, a.E, lv);
+  topk_wave(lv, a.E, a.k, s_tk[0], s_ids, s_w, nullptr, nullptr);
+  wave_lds_sync();
+  if (lane < a.k) {
+    const int s = t * a.k + lane, e = s_ids[lane];
+    a.ids_out[s] = e;
+    a.w_out[s] = s_w[lane];
+    __hip_atomic_store(a.ready + s, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Every workgroup: wave 0 polls the B*k ready words (one device-coherent
+// load per lane) until none is zero, takes the ids from them (each word
+// carries its own id, so nothing else needs ordering) and builds the plan
+// in LDS -- the last workgroup also stores it for the down launch.  A
+// workgroup waits only for workgroups of lower index, which were dispatched
+// before it.  After spin_limit polls it gives up, sets *status and plans
+// with the ids it has (clamped into range).  Ends with a barrier.
+__device__ __forceinline__ PlanView wait_token_plan(const ExpertLaunch& a, int32_t* s_plan, TopkScratch* s_tk,
+                                                    int32_t* s_ids) {
+  const int lane = threadIdx.x & 63;
+  const int ns = a.B * a.k;
+  if ((threadIdx.x >> 6) == 0) {
+    int v = 1;
+    for (int n = 0;; ++n) {
+      v = lane < ns ? ld_coherent_i32(a.ready + lane) : 1;
+      if (__ballot(v == 0) == 0ull) break;
+      if (n >= a.spin_limit) {
+        if (lane == 0) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const int e = v - 1;
+    if (lane < ns) s_ids[lane] = (e >= 0 && e < a.E) ? e : 0;
+    wave_lds_sync();
+    plan_wave(s_ids, ns, a.E, reinterpret_cast<int*>(s_tk), s_plan,
+              blockIdx.x == gridDim.x - 1 ? a.plan_out : nullptr);
+  }
+  __syncthreads();
+  return plan_view(a, s_plan);
+}
+
 // Entry e_idx of the plan: a routed expert (e_idx < n) or the shared one.
 struct ExpertView {
   int m;              // tokens

@@ -58,6 +58,13 @@ struct ExpertLaunch {
   // (up_counter, zero on entry and left at zero)
   float* up_part;
   uint32_t* up_counter;
+  // routing inside the gate/up launch with one selection per token (B >= 2):
+  // workgroup t < B selects token t and stores id + 1 of each of its slots
+  // to ready [B][k] (zeroed by the router launch); every workgroup waits for
+  // all of them.  A wait that outlasts spin_limit polls sets *status.
+  int32_t* ready;
+  uint32_t* status;
+  int spin_limit;
 };
 
 // Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored
@@ -112,6 +119,10 @@ struct SkinnyLaunch {
   int L;
   void* latent_out;
   int latent_bf16;
+  // words the launch zeroes before the gate/up launch uses them (ready of the
+  // gate/up launch's per-token selection), or null
+  int32_t* clear;
+  int clear_n;
 };
 
 // The whole block in one launch (fused kernel, small batch on the vector

@@ -248,6 +248,8 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   // the product's wave partials, or the shared gate/up's pair exchange
   // (8 pair slots of 2 x kPartStride floats)
   __shared__ float s_red[16 * RB * MB > 16 * kPartStride ? 16 * RB * MB : 16 * kPartStride];
+  if (ROUTER && a.clear && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.clear_n; i += blockDim.x) a.clear[i] = 0;
   if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
     shared_up_task<T>(a.ex, blockIdx.x - a.router_wgs, s_red);
     return;

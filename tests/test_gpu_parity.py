@@ -374,6 +374,7 @@ def run_block(c, W13, W2, Ws13, Ws2, ws=None):
     bias = None if c.bias is None else dev(c.bias)
     mb.moe_block(dev(c.X), dev(c.Wr), cfg.k, W13, W2, out, ws, Ws13, Ws2, bias, c.bias_ld, ids, w)
     torch.cuda.synchronize()
+    assert mb.workspace_status(ws) == 0   # no in-launch wait gave up
     return out, ids, w
 
 
@@ -418,6 +419,28 @@ def test_block_equals_composed_calls_and_is_deterministic(name):
     mb.moe_combine(Y, w, True, out3)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,k,E", [(2, 8, 64), (3, 6, 96), (16, 4, 128), (64, 1, 384)])
+def test_block_per_token_selection(B, k, E):
+    """From batch 2 on the vector shape (B*k <= 64) each token's top-k is
+    selected once, by one gate/up workgroup, and every workgroup waits for
+    all tokens before it plans: ids bit-exact, weights within 1e-5, output
+    within the stated bar, the status word clear, and a second call on the
+    same workspace gives the same bits (the router launch clears the words
+    the selections publish)."""
+    cfg = synth.MoEConfig("select_b%d_k%d" % (B, k), B, 1024, E, k, 64, 64, "bf16", "gumbel")
+    c = inputs.Case(cfg)
+    W13, W2, Ws13, Ws2 = gpu_weights(c)
+    ref = c.oracle_block()
+    ws = ws_for(mb.OP_BLOCK, mb.DT_BF16, B=B, d=cfg.d, E=E, k=k, I=cfg.I, Is=cfg.Is)
+    out1, ids1, w1 = run_block(c, W13, W2, Ws13, Ws2, ws=ws)
+    out2, ids2, _ = run_block(c, W13, W2, Ws13, Ws2, ws=ws)
+    say("per-token selection B=%d k=%d E=%d:" % (B, k, E), mb.last_variant())
+    assert np.array_equal(host(ids1), c.ids) and np.array_equal(host(ids2), c.ids)
+    assert np.max(np.abs(host(w1) - c.w)) <= 1e-5
+    check_block_output(host(out1), ref["out"])
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
 def test_block_batch_invariance_on_gpu():
