@@ -252,12 +252,9 @@ __global__ __launch_bounds__(256) void expert_down_kernel(ExpertLaunch a) {
     if constexpr (PATHS != kPathValu && sizeof(T) == 2) {
       if (use_mfma<PATHS>(v.m)) {
         constexpr int JM = kMaxInter / 32;
-        const int J = v.I / 32;
-        const int row = lane & 15, kq = lane >> 4;
-        const bf16_t* wr = reinterpret_cast<const bf16_t*>(v.W2) + (size_t)(r0 + row < a.d ? r0 + row : a.d - 1) * v.I;
+        const int J = wave_uniform(v.I / 32);
         u32x4 wv[JM];
-#pragma unroll
-        for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
+        load_w2_operands(reinterpret_cast<const bf16_t*>(v.W2), v.I, r0, a.d, J, wv);
         if (staged != e_idx) {
           __syncthreads();   // the previous entry's h reads are done
           stage_h_entry(a, p.slots, v, s_h);

@@ -273,13 +273,83 @@ __device__ __forceinline__ uint16_t* h_lo(const ExpertLaunch& a) {
   return reinterpret_cast<uint16_t*>(a.h) + (size_t)h_rows(a) * a.hld;
 }
 
+// K order of the matrix-shape down (the same for its W2 operands and the
+// tiled copy of h, so the products are unchanged): column i of a pair of K
+// steps (i < I rounded down to 64) sits in step 2 (i / 64) + (i / 8) % 2,
+// lane group (i / 16) % 4 -- so that one load of 8 W2 rows x 128 bytes (full
+// lines) and a DPP row shift give every lane its operand (load_w2_operands);
+// an odd last step keeps the plain order: step i / 32, group (i / 8) % 4.
+__device__ __forceinline__ void down_k_slot(int i, int I, int& j, int& kq) {
+  if (i < (I & ~63)) {
+    j = ((i >> 6) << 1) | ((i >> 3) & 1);
+    kq = (i >> 4) & 3;
+  } else {
+    j = i >> 5;
+    kq = (i >> 3) & 3;
+  }
+}
+
 // Element (token t of entry v, column i) of the tiled copy: within a tile,
-// K step j = i / 32, lane kq * 16 + row (kq = i / 8 % 4, row = t % 16) holds
-// the 8 values the matrix operand takes from that lane.  hld is a multiple
-// of 32 for bf16 weights.
+// K step j, lane kq * 16 + row (down_k_slot; row = t % 16) holds the 8
+// values the matrix operand takes from that lane.  hld is a multiple of 32
+// for bf16 weights.
 __device__ __forceinline__ size_t ht_index(const ExpertLaunch& a, const ExpertView& v, int t, int i) {
-  const int j = i >> 5, kq = (i >> 3) & 3, e8 = i & 7;
-  return (size_t)(v.hbase + (t & ~15)) * a.hld + (size_t)(((j * 64 + kq * 16 + (t & 15)) << 3) + e8);
+  int j, kq;
+  down_k_slot(i, v.I, j, kq);
+  return (size_t)(v.hbase + (t & ~15)) * a.hld + (size_t)(((j * 64 + kq * 16 + (t & 15)) << 3) + (i & 7));
+}
+
+// MFMA A operands of W2 rows r0 .. r0+15 (rows from r_end on re-read row
+// r_end - 1 and are not stored) for the J = I / 32 K steps, in the order of
+// down_k_slot.  Per pair of steps one instruction loads rows 0-7 (lane l: row
+// l % 8, columns 8 (l / 8) .. +7 of the pair's 64) and one rows 8-15, each 8
+// full 128-byte lines; lane l = R + 16 g then holds row R's columns 16 g ..
+// +7 (R < 8: first step) or 16 g + 8 .. +7 (R >= 8: second step), and takes
+// the other step's from lane l +- 8 (a DPP row shift), as the gate/up's
+// operands do.  (16 rows x 64 bytes per instruction -- half lines -- streamed
+// at ~5.5 TB/s where full lines reach ~6.9.)  An odd last step is loaded as
+// 16 rows x 64 bytes in the plain order.
+constexpr int kDownJM = kMaxInter / 32;
+__device__ __forceinline__ void load_w2_operands(const bf16_t* W2, int I, int r0, int r_end, int J,
+                                                 u32x4 (&wv)[kDownJM]) {
+  const int lane = threadIdx.x & 63;
+  const int P = J >> 1;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 va[kDownJM / 2], vb[kDownJM / 2];
+  if (P > 0) {
+    const int rl = r0 + (lane & 7), rh = r0 + 8 + (lane & 7);
+    const bf16_t* pl = W2 + (size_t)(rl < r_end ? rl : r_end - 1) * I + (lane >> 3) * 8;
+    const bf16_t* ph = W2 + (size_t)(rh < r_end ? rh : r_end - 1) * I + (lane >> 3) * 8;
+#pragma unroll
+    for (int p = 0; p < kDownJM / 2; ++p) {
+      const int pc = p < P ? p : P - 1;
+      va[p] = ld128_stream(pl + (size_t)pc * 64);
+      vb[p] = ld128_stream(ph + (size_t)pc * 64);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < kDownJM / 2; ++p) va[p] = vb[p] = zero;
+  }
+  u32x4 vt = zero;
+  if (J & 1) {
+    const int r = r0 + (lane & 15);
+    vt = ld128_stream(W2 + (size_t)(r < r_end ? r : r_end - 1) * I + (size_t)(J - 1) * 32 + (lane >> 4) * 8);
+  }
+  const bool low = (lane & 15) < 8;
+#pragma unroll
+  for (int p = 0; p < kDownJM / 2; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b_up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)vb[p][e], 0x118, 0xf, 0xf, false);  // row_shr:8
+      const uint32_t a_dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)va[p][e], 0x108, 0xf, 0xf, false);  // row_shl:8
+      wv[2 * p][e] = low ? va[p][e] : b_up;
+      wv[2 * p + 1][e] = low ? a_dn : vb[p][e];
+    }
+  if (J & 1) {
+#pragma unroll
+    for (int j = 0; j < kDownJM; ++j)
+      if (j == J - 1) wv[j] = vt;
+  }
 }
 
 // h of token t (slot row sr) of entry v, column i: to the slot rows, or,
@@ -848,7 +918,6 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
   // rows from r_end on (past d, or another workgroup's tile) re-read the
   // last row of the range (cached) and are not stored
-  const bf16_t* wr = W2 + (size_t)(r0 + row < r_end ? r0 + row : r_end - 1) * v.I;
   const int J = wave_uniform(v.I / 32);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   constexpr int JH = JM / 2;
@@ -907,8 +976,7 @@ __device__ __forceinline__ void down_mfma(const ExpertLaunch& a, const int32_t* 
   {
     u32x4 hv[JH], lv[JH];
     load_half(ok0, hh0, hl0, 0, hv, lv);
-#pragma unroll
-    for (int j = 0; j < JM; ++j) wv[j] = ld128_stream(wr + (size_t)((j < J ? j : J - 1) * 4 + kq) * 8);
+    load_w2_operands(W2, v.I, r0, r_end, J, wv);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mul_half(ok0, 0, wv, hv, lv, acc);
     if (JH < J) {
@@ -955,10 +1023,6 @@ __device__ __forceinline__ void down_mfma_duo(const ExpertLaunch& a, const int32
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, kq = lane >> 4;
   const bf16_t* W2 = reinterpret_cast<const bf16_t*>(v.W2);
-  const int ra = r0 + row < r_end ? r0 + row : r_end - 1;
-  const int rb = r0 + 16 + row < r_end ? r0 + 16 + row : r_end - 1;
-  const bf16_t* wa = W2 + (size_t)ra * v.I;
-  const bf16_t* wb = W2 + (size_t)rb * v.I;
   const int J = wave_uniform(v.I / 32);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   auto load_h = [&](int nt, u32x4 (&hv)[JM], u32x4 (&lv)[JM]) {
@@ -1001,12 +1065,8 @@ __device__ __forceinline__ void down_mfma_duo(const ExpertLaunch& a, const int32
   u32x4 hA[JM], lA[JM], hB[JM], lB[JM];
   load_h(0, hA, lA);
   u32x4 wva[JM], wvb[JM];
-#pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const size_t off = (size_t)((j < J ? j : J - 1) * 4 + kq) * 8;
-    wva[j] = ld128_stream(wa + off);
-    wvb[j] = ld128_stream(wb + off);
-  }
+  load_w2_operands(W2, v.I, r0, r_end, J, wva);
+  load_w2_operands(W2, v.I, r0 + 16, r_end, J, wvb);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (nt % 2 == 0) {
@@ -1059,14 +1119,17 @@ __device__ __forceinline__ void down_mfma_lds(const ExpertLaunch& a, const int32
   for (int nt = 0; nt < NT; ++nt) {
     const int t = nt * 16 + row;
     const bool ok = t < v.m;
-    const unsigned char* hh = s_h + (size_t)(ok ? t : 0) * kHRowBytes + kq * 16;
+    const unsigned char* hh = s_h + (size_t)(ok ? t : 0) * kHRowBytes;
     const unsigned char* hl = hh + (size_t)kMaxB * kHRowBytes;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < JM; ++j) {
       if (j < J) {
-        const u32x4 hv = ok ? *reinterpret_cast<const u32x4*>(hh + j * 64) : zero;
-        const u32x4 lv = ok ? *reinterpret_cast<const u32x4*>(hl + j * 64) : zero;
+        // the K order of the W2 operands (down_k_slot): step j of a pair
+        // takes columns 64 (j / 2) + 16 kq + 8 (j % 2) .. +7
+        const int off = j < (J & ~1) ? (j >> 1) * 128 + kq * 32 + (j & 1) * 16 : j * 64 + kq * 16;
+        const u32x4 hv = ok ? *reinterpret_cast<const u32x4*>(hh + off) : zero;
+        const u32x4 lv = ok ? *reinterpret_cast<const u32x4*>(hl + off) : zero;
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
                                                       __builtin_bit_cast(bf16x8, hv), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[j]),
