@@ -179,12 +179,15 @@ typedef enum {
  * Returns MOE_EINVAL for an unknown kernel or only one NULL event. */
 moe_status_t moe_profile_events(int kernel, void* start_event, void* stop_event);
 
-/* Byte offset in ws of the fused schedule's barrier status word (a uint32,
- * inside the workspace header, the same for every op and size).  It reads 0
- * unless a grid-wide barrier of a fused moe_block call gave up waiting (the
- * call's outputs are then invalid); no call clears it, moe_workspace_init
- * does.  The fused launch is cooperative, so the runtime refuses it when the
- * grid cannot be resident at once, and the word is not expected to move. */
+/* Byte offset in ws of the status word of moe_block's in-launch waits (a
+ * uint32, inside the workspace header, the same for every op and size).  It
+ * reads 0 unless a wait gave up (the call's outputs are then invalid): a
+ * grid-wide barrier of the fused schedule, or, from B = 2 in the small-batch
+ * schedule, a gate/up workgroup's wait for the tokens' ids.  No call clears
+ * it; moe_workspace_init does.  The fused launch is cooperative (the runtime
+ * refuses it when the grid cannot be resident at once), and the gate/up
+ * workgroups wait only for workgroups of lower index, dispatched before
+ * them, so the word is not expected to move. */
 size_t moe_workspace_status_offset(void);
 
 /* Measurement yardstick, not part of the block (WRITEUP part 1 §4: small-
@@ -324,11 +327,15 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
  * device reports room for one workgroup per compute unit.
  * By default, and outside that scope, three launches (schedule
  * "launches"); with B*k <= 64:
- *   1. router scoring only (logits + bias to ws);
- *   2. gate/up + SwiGLU: every workgroup selects the top-k of all tokens
- *      and builds the plan itself (no handshake between workgroups); the
- *      shared expert's tiles, which need no routing, go first; one
- *      workgroup stores topk_ids, topk_w and the plan;
+ *   1. router scoring only (logits + bias to ws; from B = 2 it also
+ *      clears the words step 2 publishes ids in);
+ *   2. gate/up + SwiGLU: at B = 1 every workgroup selects the token's top-k
+ *      and builds the plan itself; from B = 2 workgroup t selects token t
+ *      once, stores its topk_ids / topk_w and publishes its ids in ws, and
+ *      every workgroup waits for all tokens' ids (bounded polling; a wait
+ *      that gives up sets the status word) and builds the plan; the shared
+ *      expert's tiles, which need no routing, go first; one workgroup stores
+ *      the plan;
  *   3. down projection of every expert fused with the weighted combine: the
  *      per-slot outputs never leave the chip.
  * Otherwise, on the vector-ALU shape: 1. router scoring + top-k + plan
@@ -338,10 +345,12 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
  * finish launch that adds the slices and the bias and stores topk_ids and
  * topk_w; 3. gate/up + SwiGLU, every workgroup building the plan from the
  * ids, the shared expert one more entry, the heaviest token tiles cut in two
- * K halves; 4. down + combine, reading h from a tiled copy in ws.
+ * K halves; 4. down + combine, reading h from a tiled copy in ws (in the
+ * down's K order: see the tiled copy's layout).
  * Same scope and results as moe_route, moe_expert_ffn and moe_combine in
  * sequence (bit for bit with the vector-ALU shapes; with the matrix-core
- * shape the gate/up's K splits differ, within fp32 rounding).  topk_ids /
+ * shape the gate/up's K splits and the down's K order differ, within fp32
+ * rounding).  topk_ids /
  * topk_w are optional outputs (NULL: kept in ws). */
 moe_status_t moe_block(int dtype, int B, int d, int E, int k, int I, int Is, const void* X,
                        const void* Wr, const float* bias, int bias_ld, const void* W13,
