@@ -131,7 +131,10 @@ __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s
     }
   }
   __syncthreads();
-  if (wave == 0) plan_wave(s_ids, B * k, E, reinterpret_cast<int*>(s_tk), s_plan, writer ? a.plan_out : nullptr);
+  if (wave == 0) {
+    if (B == 1) plan_one_token(s_ids, k, s_plan, writer ? a.plan_out : nullptr);
+    else plan_wave(s_ids, B * k, E, reinterpret_cast<int*>(s_tk), s_plan, writer ? a.plan_out : nullptr);
+  }
   __syncthreads();
   return plan_view(a, s_plan);
 }

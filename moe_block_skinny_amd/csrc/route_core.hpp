@@ -194,6 +194,27 @@ __device__ __forceinline__ void plan_wave(const int32_t* ids, int nslot, int E, 
   }
 }
 
+// The plan of one token (B = 1, nslot = k <= E, ids ascending and distinct,
+// as topk_wave leaves them): n = k, active = ids, offs = 0..k, slots =
+// 0..k-1 -- what plan_wave computes for it, without the sort.  One wave;
+// writes P and, when non-null, P2.
+__device__ __forceinline__ void plan_one_token(const int32_t* ids, int k, int32_t* P, int32_t* P2) {
+  const int lane = threadIdx.x & 63;
+  for (int q = 0; q < 2; ++q) {
+    int32_t* D = q ? P2 : P;
+    if (!D) continue;
+    if (lane < k) {
+      D[1 + lane] = ids[lane];
+      D[1 + k + lane] = lane;
+      D[2 + 2 * k + lane] = lane;
+    }
+    if (lane == 0) {
+      D[0] = k;
+      D[1 + 2 * k] = k;
+    }
+  }
+}
+
 // LDS scratch of plan_block.
 struct PlanScratch {
   unsigned long long mask[kMaxE];   // bit t: token t chose expert e
