@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
         up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
         __syncthreads();
       }
-      p = a.ready ? wait_token_plan(a, s_plan, s_tk, s_ids) : route_here<false>(a, s_plan, s_tk, s_ids, s_w);
+      p = a.ready ? wait_token_plan(a, s_plan, s_tk, s_ids) : route_here<false, 1>(a, s_plan, s_tk, s_ids, s_w);
     } else {
       p = stage_plan(a, s_plan);
     }

@@ -107,10 +107,12 @@ __device__ __forceinline__ PlanView plan_from_ids(const ExpertLaunch& a, int32_t
 // (at most kTopkWaves).  The last workgroup of the grid also stores
 // ids, weights and plan for the down launch and the caller.  Ends with a
 // barrier.  SAME_LAUNCH: the logits were stored in this launch (fused block).
-template <bool SAME_LAUNCH>
+// QB: tokens a wave requests logits for before selecting (one memory round
+// trip per QB tokens); the gate/up launch selects here only at batch 1 and
+// takes QB = 1, which also keeps one copy of the selection code.
+template <bool SAME_LAUNCH, int QB = 2>
 __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s_plan, TopkScratch* s_tk,
                                                int32_t* s_ids, float* s_w) {
-  constexpr int QB = 2;
   const int nw = (blockDim.x >> 6) < kTopkWaves ? (blockDim.x >> 6) : kTopkWaves;
   const int wave = threadIdx.x >> 6;
   const bool writer = blockIdx.x == gridDim.x - 1;
