@@ -466,6 +466,8 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
   // with MFMA tasks: two workgroups per CU, walking the task list
   const int cap = paths == kPathValu ? 4 * kCUs : 2 * kCUs;
   if (g > cap) g = cap;
+  // with the per-token selection, workgroup t selects token t: at least B
+  if (a.ready && g < a.B) g = a.B;
   if (g < 1) g = 1;
   const dim3 grid(g), block(kUpWaves * 64);
   if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), grid, block, 0, st, a);
