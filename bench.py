@@ -76,8 +76,9 @@ def parse():
     ap.add_argument("--kernel-steps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU timing (single thread, all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused"],
-                    help="moe_block schedule: one fused launch where it applies, or three launches")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused", "router_in_up"],
+                    help="moe_block schedule: one fused launch where it applies, three launches, or "
+                         "(B <= 2) two with the router rows in the gate/up launch")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs (one captured block per weight set) instead of plain "
                          "launches; every replay is first checked against the plain launch's bits")
@@ -273,7 +274,7 @@ KERNEL_SYMBOL = {"route": "skinny_valu_kernel / skinny_mfma_kernel + route_finis
                  "block": "moe_block_kernel"}
 
 
-def launch_bytes(cfg, n, esz, bias_b, route_in_up):
+def launch_bytes(cfg, n, esz, bias_b, route_in_up, rows_in_up=False):
     """Algorithmic HBM bytes of each launch of the block, for n distinct
     routed experts: the weights it streams (once), the activations it must
     read and the results it must write.  Workspace traffic between launches
@@ -281,7 +282,10 @@ def launch_bytes(cfg, n, esz, bias_b, route_in_up):
     the producer's output and the consumer's input; the completion counter
     and the plan are not.  The shared expert's gate/up runs in the gate/up
     launch when that launch also selects (small batch), else in the router
-    launch (vector shape) or as an entry of the gate/up launch (matrix)."""
+    launch (vector shape) or as an entry of the gate/up launch (matrix).
+    With the router rows inside the gate/up launch (rows_in_up: two
+    launches) that launch also streams the router weights and its logits
+    never leave it."""
     B, d, E, k, I, Is = cfg.B, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is
     x = B * d * esz
     shared_up = 2 * Is * d * esz + B * Is * 4 if Is else 0
@@ -298,6 +302,9 @@ def launch_bytes(cfg, n, esz, bias_b, route_in_up):
     down = n * d * I * esz + B * k * I * 4 + B * k * 4 + B * d * esz
     if Is:
         down += d * Is * esz + B * Is * 4
+    if rows_in_up:
+        up += E * d * esz + bias_b - B * E * 4   # router weights in, no logits read back
+        return {"expert_up": up, "expert_down_combine": down}
     return {"route": route, "expert_up": up, "expert_down_combine": down}
 
 
@@ -327,6 +334,7 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
     variant = mb.last_variant()
     fused = "fused" in variant
     route_in_up = "top-k/plan" in variant
+    rows_in_up = "rows in the gate/up launch" in variant
     # algorithmic bytes per set: every selected expert's weights once, the
     # router and shared expert, x (and bias) read once, out written once
     per_set = []
@@ -334,13 +342,14 @@ def run_moe(name, args, torch, mb, synth, with_roofline):
         n = int(torch.unique(s["ids"]).numel())
         bias_b = 0 if s["bias"] is None else s["bias"].numel() * 4
         b = cfg.E * cfg.d * esz + n * expert_bytes + shared_bytes + 2 * cfg.B * cfg.d * esz + bias_b
-        per_set.append((n, b, launch_bytes(cfg, n, esz, bias_b, route_in_up)))
+        per_set.append((n, b, launch_bytes(cfg, n, esz, bias_b, route_in_up, rows_in_up)))
     avg_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
     avg_n = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
     kern, kbytes = {}, {}
     launches = ((("block", mb.KERNEL_BLOCK),) if fused else
-                (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP),
-                 ("expert_down_combine", mb.KERNEL_EXPERT_DOWN)))
+                ((("expert_up", mb.KERNEL_EXPERT_UP),) if rows_in_up else
+                 (("route", mb.KERNEL_ROUTE), ("expert_up", mb.KERNEL_EXPERT_UP))) +
+                (("expert_down_combine", mb.KERNEL_EXPERT_DOWN),))
     nk = max(1, args.kernel_steps)
     for lname, kid in launches:
         kern[lname] = kernel_times(step, kid, nk, torch, mb)

@@ -119,13 +119,23 @@ const char* moe_last_variant(void);
  * setting. */
 int moe_set_variant(int variant);
 
-/* Schedule of moe_block: MOE_SCHEDULE_AUTO (currently three launches: on
- * MI355X the fused launch's two grid-wide barriers cost more than the kernel
- * boundaries they replace), MOE_SCHEDULE_LAUNCHES (three launches) or
- * MOE_SCHEDULE_FUSED (one launch; MOE_EUNSUPPORTED outside its scope).  Also set by the MOE_BLOCK_SCHEDULE environment
- * variable (auto, launches, fused).  Both schedules give identical bits.
- * Returns the previous setting. */
-typedef enum { MOE_SCHEDULE_AUTO = 0, MOE_SCHEDULE_LAUNCHES = 1, MOE_SCHEDULE_FUSED = 2 } moe_schedule_t;
+/* Schedule of moe_block: MOE_SCHEDULE_AUTO (MOE_SCHEDULE_ROUTER_IN_UP where
+ * it applies, else three launches: on MI355X the fused launch's two
+ * grid-wide barriers cost more than the kernel boundaries they replace),
+ * MOE_SCHEDULE_LAUNCHES (three launches), MOE_SCHEDULE_FUSED (one launch;
+ * MOE_EUNSUPPORTED outside its scope) or MOE_SCHEDULE_ROUTER_IN_UP (at
+ * B <= 2 in the small-batch schedule with the shared expert's gate/up in the
+ * gate/up launch, two launches: the router rows run in the gate/up launch,
+ * whose other workgroups wait for the logits; elsewhere three launches).  Also set by
+ * the MOE_BLOCK_SCHEDULE environment variable (auto, launches, fused,
+ * router_in_up).  All schedules give identical bits.  Returns the previous
+ * setting. */
+typedef enum {
+  MOE_SCHEDULE_AUTO = 0,
+  MOE_SCHEDULE_LAUNCHES = 1,
+  MOE_SCHEDULE_FUSED = 2,
+  MOE_SCHEDULE_ROUTER_IN_UP = 3
+} moe_schedule_t;
 int moe_set_block_schedule(int schedule);
 
 /* Where moe_block runs the shared expert's gate/up in the small-batch
@@ -325,7 +335,15 @@ moe_status_t moe_combine(int dtype, int B, int d, int k, const float* Yslot, con
  * down projection with the weighted combine.  The barrier words live in ws
  * (count words return to zero after every call).  Used only when the
  * device reports room for one workgroup per compute unit.
- * By default, and outside that scope, three launches (schedule
+ * By default at B <= 2 (B*k <= 64, vector shape, the shared expert's
+ * gate/up not placed in the router launch), TWO launches (schedule
+ * "router_in_up"): the gate/up launch's first workgroups score the router
+ * rows, with the router launch's split of K, and store each logit's order
+ * key in ws (16 copies); the others run the shared expert's tiles, poll the
+ * keys (bounded; a wait that gives up sets the status word), select every
+ * token's top-k and build the plan, then run the routed gate/up; the down +
+ * combine launch (3. below) zeroes the keys again.
+ * Otherwise, and outside that scope, three launches (schedule
  * "launches"); with B*k <= 64:
  *   1. router scoring only (logits + bias to ws; from B = 2 it also
  *      clears the words step 2 publishes ids in);

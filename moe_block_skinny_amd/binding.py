@@ -22,8 +22,9 @@ VARIANT_AUTO, VARIANT_GEMV, VARIANT_SPLITK, VARIANT_MFMA = range(4)
 OP_SKINNY_GEMM, OP_ROUTE, OP_EXPERT_FFN, OP_BLOCK, OP_ROUTE_LATENT = range(5)
 KERNEL_ROUTE, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_SKINNY, KERNEL_BLOCK, KERNEL_STREAM = range(7)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "splitk": VARIANT_SPLITK, "mfma": VARIANT_MFMA}
-SCHEDULE_AUTO, SCHEDULE_LAUNCHES, SCHEDULE_FUSED = range(3)
-SCHEDULES = {"auto": SCHEDULE_AUTO, "launches": SCHEDULE_LAUNCHES, "fused": SCHEDULE_FUSED}
+SCHEDULE_AUTO, SCHEDULE_LAUNCHES, SCHEDULE_FUSED, SCHEDULE_ROUTER_IN_UP = range(4)
+SCHEDULES = {"auto": SCHEDULE_AUTO, "launches": SCHEDULE_LAUNCHES, "fused": SCHEDULE_FUSED,
+             "router_in_up": SCHEDULE_ROUTER_IN_UP}
 SHARED_AUTO, SHARED_IN_UP, SHARED_IN_ROUTER = range(3)
 SHARED_SCHEDULES = {"auto": SHARED_AUTO, "up": SHARED_IN_UP, "router": SHARED_IN_ROUTER}
 

@@ -80,6 +80,7 @@ int schedule() {
     if (e) {
       if (!strcmp(e, "launches")) f = MOE_SCHEDULE_LAUNCHES;
       else if (!strcmp(e, "fused")) f = MOE_SCHEDULE_FUSED;
+      else if (!strcmp(e, "router_in_up")) f = MOE_SCHEDULE_ROUTER_IN_UP;
     }
     int expect = -1;
     g_sched.compare_exchange_strong(expect, f);
@@ -154,11 +155,17 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant, bool router = 
 // counter.  The header holds the router's completion counter (word 0), one
 // arrival counter per 64-row group of the MFMA product (words 32.., for
 // N <= 63488), then the fused block's barrier lines (2 count lines, 2 x
-// kBlockMaxGrid flag lines, a status line).
+// kBlockMaxGrid flag lines, a status line), then the logit keys of the
+// router rows inside the gate/up launch (kKeyCopies copies of [B][E] words,
+// B <= 2).
 constexpr size_t kCounterBytes = 4096;
 constexpr size_t kSyncOff = kCounterBytes;
 constexpr size_t kSyncBytes = (size_t)(3 + 2 * kBlockMaxGrid) * kFlagStride * 4;
-constexpr size_t kHeaderBytes = (kSyncOff + kSyncBytes + kAlign - 1) / kAlign * kAlign;
+constexpr int kKeysMaxB = 2;
+constexpr size_t kKeysOff = kSyncOff + kSyncBytes;
+constexpr size_t kKeysBytes = (size_t)kKeyCopies * kKeyStride * 4;
+static_assert(kKeysMaxB * kMaxE <= kKeyStride, "a copy of the keys holds B * E words");
+constexpr size_t kHeaderBytes = (kKeysOff + kKeysBytes + kAlign - 1) / kAlign * kAlign;
 
 // Skinny product / router: after the header, the router logits fp32 [B][N]
 // (router only) and, where the MFMA shape may run with K slices (bf16), the
@@ -454,7 +461,7 @@ int moe_set_shared_schedule(int sched) {
 
 int moe_set_block_schedule(int sched) {
   const int prev = schedule();
-  if (sched < MOE_SCHEDULE_AUTO || sched > MOE_SCHEDULE_FUSED) return prev;
+  if (sched < MOE_SCHEDULE_AUTO || sched > MOE_SCHEDULE_ROUTER_IN_UP) return prev;
   g_sched.store(sched);
   return prev;
 }
@@ -824,21 +831,35 @@ moe_status_t block_run(const BlockArgs& A, int v, int force, const BlockWs& L, c
     // (one pass over x), or on the side stream
     const int ssched = shared_schedule();
     const bool in_router = Ws13 && !side && ssched == MOE_SHARED_IN_ROUTER;
+    // AUTO takes it where it applies: 22.6 -> 20.8 us at batch 1
+    const bool router_in_up = (sched == MOE_SCHEDULE_ROUTER_IN_UP || sched == MOE_SCHEDULE_AUTO) && B <= kKeysMaxB &&
+                              !in_router && !side;
     ex.skip_shared = (in_router || side) ? 1 : 0;
     ex.ids_out = ids;
     ex.w_out = tw;
     ex.plan_out = plan;
-    // from batch 2 each token is selected once, by one gate/up workgroup,
-    // and the others wait for it (the router launch clears the words);
-    // at batch 1 every workgroup selects the one token itself (no wait)
-    if (B >= 2) {
-      ex.ready = reinterpret_cast<int32_t*>(w + L.ready);
-      ex.status = reinterpret_cast<uint32_t*>(w + moe_workspace_status_offset());
-      ex.spin_limit = 1 << 20;   // about a second of polling
+    ex.status = reinterpret_cast<uint32_t*>(w + moe_workspace_status_offset());
+    ex.spin_limit = 1 << 20;   // about a second of polling
+    if (router_in_up) {
+      // the router rows in the gate/up launch itself (two launches): its
+      // first workgroups score them and store the logits' keys in the
+      // header, every gate/up workgroup waits for them and selects both
+      // tokens itself; the down launch zeroes the keys again
+      ex.Wr = Wr;
+      ex.rbias = bias;
+      ex.rbias_ld = bias_ld;
+      ex.router_wgs = (E + kRouterRowsInUp - 1) / kRouterRowsInUp;
+      ex.lkeys = reinterpret_cast<uint32_t*>(w + kKeysOff);
+      snprintf(d1, sizeof d1, "rows in the gate/up launch, %d workgroups", ex.router_wgs);
+    } else {
+      // from batch 2 each token is selected once, by one gate/up workgroup,
+      // and the others wait for it (the router launch clears the words);
+      // at batch 1 every workgroup selects the one token itself (no wait)
+      if (B >= 2) ex.ready = reinterpret_cast<int32_t*>(w + L.ready);
+      if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, st, d1,
+                         sizeof d1, in_router ? &ex : nullptr, 0, &ex.logits, 0, ex.ready, ex.ready ? B * k : 0)))
+        return s;
     }
-    if ((s = run_route(dtype, B, d, E, k, X, Wr, bias, bias_ld, ids, tw, plan, nullptr, w + L.route_off, st, d1,
-                       sizeof d1, in_router ? &ex : nullptr, 0, &ex.logits, 0, ex.ready, ex.ready ? B * k : 0)))
-      return s;
   } else {
     // the vector router launch carries the shared expert's vector gate/up;
     // otherwise it is a task of the gate/up launch
@@ -936,11 +957,10 @@ moe_status_t moe_block_noalloc(int dtype, int B, int d, int E, int k, int I, int
   char* w = nullptr;
   if ((s = hip_status(noalloc_scratch(reinterpret_cast<void**>(&w)), "scratch address"))) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // the scratch keeps the last call's contents: the counter words every
+  // the scratch keeps the last call's contents: the header words every
   // launch expects at zero are cleared first (a kernel, so the call may be
   // captured in a graph)
-  if ((s = hip_status(launch_fill_zero(w, kCounterBytes + 2 * kFlagStride * 4, st), "scratch counters")))
-    return s;
+  if ((s = hip_status(launch_fill_zero(w, kHeaderBytes, st), "scratch header"))) return s;
   return block_run(a, v, force, L, w, st);
 }
 

@@ -67,12 +67,21 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
   const int tiles_r = (a.I + PPT - 1) / PPT;
   const int tiles_s = (a.Ws13 && !a.skip_shared) ? (a.Is + PPT - 1) / PPT : 0;
   if constexpr (PATHS == kPathValu) {
+    // With the router rows in this launch, its first router_wgs workgroups
+    // score them and leave; the others are the gate/up workgroups
+    if (a.router_wgs && (int)blockIdx.x < a.router_wgs) {
+      __shared__ float s_rr[kRouterPlayedWaves * kRouterRowsInUp * 2];
+      router_rows_in_up<T, kUpWaves>(a, blockIdx.x, s_rr);
+      return;
+    }
+    const int G = (int)gridDim.x - a.router_wgs;   // gate/up workgroups
     // Tasks: with routing here, the shared expert's tiles first -- they
-    // need no plan and keep HBM busy while the routed workgroups select --
-    // then the routed tiles; otherwise the routed tiles, then the shared ones.
-    const bool here = a.logits != nullptr;
+    // need no plan and keep HBM busy while the routed workgroups select (and,
+    // with the router rows here, while those are scored) -- then the routed
+    // tiles; otherwise the routed tiles, then the shared ones.
+    const bool here = a.logits != nullptr || a.lkeys != nullptr;
     PlanView p;
-    int task0 = blockIdx.x;
+    int task0 = (int)blockIdx.x - a.router_wgs;
     if (here) {
       __shared__ TopkScratch s_tk[kUpWaves];
       __shared__ int32_t s_ids[64];
@@ -80,7 +89,12 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       // per-token selection: this workgroup's token first (before its
       // shared tiles), the wait for every token's after them
       if (a.ready) select_own_token(a, s_tk, s_ids, s_w);
-      for (; task0 < tiles_s; task0 += gridDim.x) {
+      // with the router rows here, a workgroup that has no shared tile would
+      // poll the keys for the ~2 us the router workgroups take, and its
+      // loads would only queue with theirs: it sleeps ~1.8 us first (64 x
+      // 64 cycles; polling from the start cost ~0.5 us at batch 1)
+      if (a.lkeys && task0 >= tiles_s) __builtin_amdgcn_s_sleep(64);
+      for (; task0 < tiles_s; task0 += G) {
         up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
         __syncthreads();
       }
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     }
     const int first = here ? tiles_s : 0;                    // first routed task
     const int total = first + p.n * tiles_r + (here ? 0 : tiles_s);
-    for (int task = task0; task < total; task += gridDim.x) {
+    for (int task = task0; task < total; task += G) {
       const int rt = task - first;
       const bool routed = rt < p.n * tiles_r;
       const ExpertView v = routed ? expert_view<T>(a, p, rt / tiles_r) : shared_view(a);
@@ -298,6 +312,12 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   const int rt = (PIPE || PAIRED) ? a.down_rows : RT;
   float* s_y = s_dyn;
   float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
+  // the router rows' keys of the gate/up launch, zero again for the next call
+  if (a.lkeys) {
+    const int n = a.B * a.E;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kKeyCopies * n; i += gridDim.x * blockDim.x)
+      a.lkeys[(i / n) * kKeyStride + i % n] = 0u;
+  }
   // The gate weights, (PIPE) h and the plan are requested together, into
   // registers, and written to LDS once all have arrived: one memory round
   // trip before the first W2 request instead of one per array.  h goes to
@@ -468,15 +488,17 @@ hipError_t launch_expert_up(const ExpertLaunch& a, hipStream_t st, char* desc, s
   if (g > cap) g = cap;
   // with the per-token selection, workgroup t selects token t: at least B
   if (a.ready && g < a.B) g = a.B;
+  // router workgroups ahead of the gate/up ones, the whole grid resident
+  if (a.router_wgs && g > cap - a.router_wgs) g = cap - a.router_wgs;
   if (g < 1) g = 1;
-  const dim3 grid(g), block(kUpWaves * 64);
+  const dim3 grid(g + a.router_wgs), block(kUpWaves * 64);
   if (!a.bf16) launch(K_EXPERT_UP, (expert_up_kernel<float, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathValu) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathValu>), grid, block, 0, st, a);
   else if (paths == kPathMfma) launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathMfma>), grid, block, 0, st, a);
   else launch(K_EXPERT_UP, (expert_up_kernel<bf16_t, kPathBoth>), grid, block, 0, st, a);
   if (desc)
-    snprintf(desc, desc_len, "up grid=%d%s%s force=%d", g, a.skip_shared ? " routed-only" : "",
-             a.logits ? " +top-k/plan" : "", a.force);
+    snprintf(desc, desc_len, "up grid=%d%s%s%s force=%d", g, a.skip_shared ? " routed-only" : "",
+             a.router_wgs ? " +router rows" : "", (a.logits || a.lkeys) ? " +top-k/plan" : "", a.force);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 #include "internal.hpp"
 #include "mfma_core.hpp"
 #include "route_core.hpp"
+#include "skinny_core.hpp"
 
 namespace moe {
 
@@ -100,9 +101,66 @@ __device__ __forceinline__ PlanView plan_from_ids(const ExpertLaunch& a, int32_t
   return plan_view(a, s_plan);
 }
 
+// ---- router rows inside the gate/up launch (B <= 2) ------------------------
+
+// The router launch's workgroups have 16 waves; its logits' bits depend on
+// that split of K alone (not on rows or tokens per workgroup), so the gate/up
+// launch's 4-wave router workgroups play 16 waves.
+constexpr int kRouterPlayedWaves = 16;
+
+// Router workgroup r of the gate/up launch: rows r * kRouterRowsInUp .. of
+// x . Wr^T (+ bias), each logit's order key (ord_key; a NaN's kept nonzero)
+// stored device-coherent to every copy of lkeys for the gate/up workgroups
+// (hundreds of workgroups polling one copy queue at the lines' memory
+// channel, and the stores behind them: one copy cost ~1 us at batch 1).
+// s_rr: kRouterPlayedWaves * kRouterRowsInUp * 2 floats.
+template <typename T, int NR>
+__device__ __forceinline__ void router_rows_in_up(const ExpertLaunch& a, int r, float* s_rr) {
+  const RowsSrc src = {a.X, a.Wr, a.B, a.E, a.d};
+  auto fin = [&](int t, int n, float v) {
+    if (a.rbias) v += a.rbias[(size_t)t * a.rbias_ld + n];
+    uint32_t key = ord_key(v);
+    if (key == 0u) key = ord_key(__builtin_nanf(""));
+#pragma unroll
+    for (int c = 0; c < kKeyCopies; ++c)
+      __hip_atomic_store(a.lkeys + c * kKeyStride + t * a.E + n, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const int n0 = r * kRouterRowsInUp;
+  if (a.B <= 1) valu_rows_as<T, kRouterRowsInUp, 1, 1, kRouterPlayedWaves, NR>(src, n0, s_rr, fin);
+  else valu_rows_as<T, kRouterRowsInUp, 2, 1, kRouterPlayedWaves, NR>(src, n0, s_rr, fin);
+}
+
+// Token t's logits as topk_wave takes them, from the keys the router
+// workgroups of this launch store: the wave polls its experts' keys in the
+// workgroup's copy until none is zero.  After spin_limit polls it gives up,
+// sets *status and takes the keys as they are.
+__device__ __forceinline__ void wait_logit_keys(const ExpertLaunch& a, int t, float (&lv)[kNI]) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* kp = a.lkeys + (blockIdx.x % kKeyCopies) * kKeyStride + t * a.E;
+  uint32_t key[kNI];
+  for (int n = 0;; ++n) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      const int e = lane + 64 * i;
+      key[i] = e < a.E ? __hip_atomic_load(kp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+      all = all && key[i] != 0u;
+    }
+    if (__ballot(!all) == 0ull) break;
+    if (n >= a.spin_limit) {
+      if (lane == 0) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int i = 0; i < kNI; ++i) lv[i] = key_value(key[i]);
+}
+
 // Routing inside the gate/up launch (B*k <= 64): the workgroup selects the
-// top-k of all B tokens from the router's logits [B][E] (bias included) and
-// builds the plan in LDS -- the same functions, hence the same bits, as the
+// top-k of all B tokens from the router's logits [B][E] (bias included), or
+// from their keys when the router rows run in this launch, and builds the
+// plan in LDS -- the same functions, hence the same bits, as the
 // router's finishing workgroup.  s_tk: one TopkScratch per selecting wave
 // (at most kTopkWaves).  The last workgroup of the grid also stores
 // ids, weights and plan for the down launch and the caller.  Ends with a
@@ -122,7 +180,8 @@ __device__ __forceinline__ PlanView route_here(const ExpertLaunch& a, int32_t* s
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int t = t0 + nw * q;
-      load_logit_row<SAME_LAUNCH>(a.logits, t < B ? t : B - 1, E, lv[q]);
+      if (a.lkeys) wait_logit_keys(a, t < B ? t : B - 1, lv[q]);
+      else load_logit_row<SAME_LAUNCH>(a.logits, t < B ? t : B - 1, E, lv[q]);
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {

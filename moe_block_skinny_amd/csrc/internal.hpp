@@ -11,6 +11,14 @@ namespace moe {
 
 enum Variant { VAR_AUTO = 0, VAR_GEMV = 1, VAR_SPLITK = 2, VAR_MFMA = 3 };
 
+// Router rows per workgroup when the router product runs inside the gate/up
+// launch (ExpertLaunch::router_wgs), and the copies of the logit keys it
+// stores: gate/up workgroup g polls copy g % kKeyCopies, kKeyStride words
+// apart (B <= 2 tokens of E <= 512 experts each).
+constexpr int kRouterRowsInUp = 2;
+constexpr int kKeyCopies = 16;
+constexpr int kKeyStride = 1024;
+
 // Expert FFN stage over the routing plan.  h is fp32 [B*k + B][Imax]:
 // routed slot s = t*k + j at row s, shared-expert token t at row B*k + t.
 struct ExpertLaunch {
@@ -65,6 +73,18 @@ struct ExpertLaunch {
   int32_t* ready;
   uint32_t* status;
   int spin_limit;
+  // router rows inside the gate/up launch (B <= 2, vector shape): the first
+  // router_wgs workgroups each score kRouterRowsInUp rows of Wr [E][d] (+
+  // rbias [B][rbias_ld]) with the router launch's arithmetic and store each
+  // logit's order key (never zero) to every copy of lkeys [kKeyCopies]
+  // [kKeyStride] (a copy: [B][E]) with device-coherent stores; the other
+  // workgroups poll the keys they need in their copy.  lkeys is zero on
+  // entry, and the down + combine launch zeroes it again.
+  const void* Wr;
+  const float* rbias;
+  int rbias_ld;
+  int router_wgs;
+  uint32_t* lkeys;
 };
 
 // Y[t][n] = sum_c X[t][c] W[n][c] for t < M, n < N, over K; either stored

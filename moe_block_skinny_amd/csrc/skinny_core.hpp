@@ -105,4 +105,85 @@ __device__ __forceinline__ void valu_rows(const SkinnyLaunch& a, int n0, float* 
   }
 }
 
+// valu_rows<T, RB, MB, U> of a workgroup of NV waves, computed by one of NR
+// waves (NV a multiple of NR) with the same bits: wave w plays waves w,
+// w + NR, w + 2 NR, ...; each played wave keeps its own sums over its own
+// blocks in its own order, is reduced on its own, and the NV sums meet in
+// LDS in wave order as in valu_rows.  The played waves' loads of one block
+// group go out together.  Rows n0 .. n0 + RB - 1 of W [N][K] against the M
+// rows of X [M][K]; fin(t, n, v) takes each result (threads < RB * MB).
+// s_red holds NV * RB * MB floats.  Ends after a barrier.
+struct RowsSrc {
+  const void* X;
+  const void* W;
+  int M, N, K;
+};
+
+template <typename T, int RB, int MB, int U, int NV, int NR, typename Fin>
+__device__ __forceinline__ void valu_rows_as(const RowsSrc& s, int n0, float* s_red, Fin&& fin) {
+  static_assert(NV % NR == 0, "whole played waves per wave");
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int J = NV / NR;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const T* X = reinterpret_cast<const T*>(s.X);
+  const T* wr[RB];
+  const T* xr[MB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    wr[r] = reinterpret_cast<const T*>(s.W) + (size_t)(n0 + r < s.N ? n0 + r : s.N - 1) * s.K;
+#pragma unroll
+  for (int t = 0; t < MB; ++t) xr[t] = X + (size_t)(t < s.M ? t : 0) * s.K;
+  const int C = s.K / VEC;
+  float acc[J][RB][MB];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int t = 0; t < MB; ++t) acc[j][r][t] = 0.f;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // played wave v = wave + NR j takes blocks v + base + u NV (base = 0,
+  // NV U, ...; u < U), as wave v of valu_rows; a block group none of this
+  // wave's played waves has is skipped (a played wave past the range adds
+  // zero products, which leave its sums as they are)
+  for (int base = 0; (wave + base) * 64 < C; base += NV * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if ((wave + base + u * NV) * 64 >= C) break;
+      u32x4 wv[J][RB], xv[J][MB];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = (wave + NR * j + base + u * NV) * 64 + lane;
+        const bool ok = c < C;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wv[j][r] = ok ? ld128_stream(wr[r] + (size_t)c * VEC) : zero;
+#pragma unroll
+        for (int t = 0; t < MB; ++t) xv[j][t] = (ok && t < s.M) ? ld128(xr[t] + (size_t)c * VEC) : zero;
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int t = 0; t < MB; ++t) acc[j][r][t] = dot_chunk(wv[j][r], xv[j][t], acc[j][r][t], T());
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        const float v = group_sum<64>(acc[j][r][t]);
+        if (lane == 0) s_red[((wave + NR * j) * RB + r) * MB + t] = v;
+      }
+  __syncthreads();
+  if (threadIdx.x < RB * MB) {
+    const int r = threadIdx.x / MB, t = threadIdx.x % MB, n = n0 + r;
+    float v = 0.f;
+    for (int w = 0; w < NV; ++w) v += s_red[(w * RB + r) * MB + t];
+    if (n < s.N && t < s.M) fin(t, n, v);
+  }
+}
+
 }  // namespace moe
