@@ -37,6 +37,15 @@ Also on the line:
   cpu_baseline: the CPU oracle timed on this host on a bounded sample of the
                 headline workload, single-threaded and on all cores
                 (OpenMP over tokens), with the CPU model and affinity mask.
+
+--timeline (with tp16_b1, tp16_b8 or tp8_b64): instead of timing, run the
+instrumented library (libmoe_skinny_stamps.so, built by build()) and print
+one JSON line with the per-workgroup clock stamps of --trials single blocks
+(each launched alone after every weight set was run once): per launch and
+stamp point the min / p10 / median / p90 / max in µs from the block's first
+workgroup start, and for the gate/up launch the end times by CU slot (the
+grid's first, second, ... 256 workgroups) and whether workgroups g and
+g + 256 ran on the same CU.
 """
 from __future__ import annotations
 
@@ -79,6 +88,8 @@ def parse():
     ap.add_argument("--schedule", default="auto", choices=["auto", "launches", "fused", "router_in_up"],
                     help="moe_block schedule: one fused launch where it applies, three launches, or "
                          "(B <= 2) two with the router rows in the gate/up launch")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup clock stamps of single blocks (instrumented library)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs (one captured block per weight set) instead of plain "
                          "launches; every replay is first checked against the plain launch's bits")
@@ -697,6 +708,111 @@ def cpu_baseline_gemm(kind, B, args):
                 cpu_model=model, affinity=_ranges(aff), host_cpus=os.cpu_count())
 
 
+# ---------------------------------------------------------------- timeline
+
+# stamp points of each instrumented launch (slot -> name); the gate/up's
+# meaning depends on its shape (vector: routing inside; matrix: plan from ids)
+TIMELINE_POINTS = {
+    "route": {0: "start", 1: "product done"},
+    "route_finish": {0: "start", 1: "selected"},
+    "expert_up": {0: "start", 1: "router rows scored / shared tiles done (vector); plan built (matrix)",
+                  2: "plan ready (vector); tasks listed (matrix)", 3: "first routed task done", 4: "end"},
+    "expert_down_combine": {0: "start", 1: "staged", 2: "products done", 3: "end"},
+}
+
+
+def run_timeline(name, args, torch, mb, synth):
+    """Per-workgroup clock stamps of `args.trials` single blocks (see the
+    module docstring).  The stamps are the 100 MHz constant clock."""
+    import ctypes
+
+    import numpy as np
+
+    from moe_block_skinny_amd import build as hip_build
+
+    stamps_lib = mb.load(hip_build.LIB_STAMPS)
+    for f in (stamps_lib.moe_stamps_route, stamps_lib.moe_stamps_expert):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    prod, mb.lib = mb.lib, stamps_lib
+    try:
+        cfg = synth.CONFIGS[name]
+        R = 2
+        sets = moe_sets(cfg, R, args.seed, torch)
+        ws = mb.workspace(mb.workspace_bytes(mb.OP_BLOCK, mb.DT_BF16, B=cfg.B, d=cfg.d, E=cfg.E, k=cfg.k,
+                                             I=cfg.I, Is=cfg.Is))
+
+        def step(i):
+            s = sets[i % R]
+            mb.moe_block(s["X"], s["Wr"], cfg.k, s["W13"], s["W2"], s["out"], ws, s["Ws13"], s["Ws2"],
+                         s["bias"], s["bias_ld"], topk_ids=s["ids"])
+
+        for i in range(max(R, args.warmup)):
+            step(i)
+        torch.cuda.synchronize()
+        shape = (4, 1024, 8)   # [kernel][workgroup][slot]
+        reps = []
+        for rep in range(args.trials):
+            for f in (stamps_lib.moe_stamps_route, stamps_lib.moe_stamps_expert):
+                if f(None, 1):
+                    raise RuntimeError("clearing the stamps failed")
+            torch.cuda.synchronize()
+            step(rep)
+            torch.cuda.synchronize()
+            tabs = []
+            for f in (stamps_lib.moe_stamps_route, stamps_lib.moe_stamps_expert):
+                t = np.zeros(shape, np.uint64)
+                if f(t.ctypes.data, 0):
+                    raise RuntimeError("reading the stamps failed")
+                tabs.append(t.astype(np.int64))
+            # route and finish from the router's file, gate/up and down from the experts'
+            reps.append(np.stack([tabs[0][0], tabs[0][1], tabs[1][2], tabs[1][3]]))
+        variant = mb.last_variant()
+    finally:
+        mb.lib = prod
+
+    def q(v):
+        v = np.sort(np.asarray(v, float))
+        return {"n": int(len(v)), "min": round(v[0], 2), "p10": round(float(np.percentile(v, 10)), 2),
+                "med": round(float(np.median(v)), 2), "p90": round(float(np.percentile(v, 90)), 2),
+                "max": round(v[-1], 2)} if len(v) else None
+
+    names = ("route", "route_finish", "expert_up", "expert_down_combine")
+    pooled = {n: {pt: [] for pt in TIMELINE_POINTS[n]} for n in names}
+    slots, pairs, tasks = {}, [], {}
+    for st in reps:
+        live = [st[kk, :, 0] > 0 for kk in range(4)]
+        t0 = min(st[kk, live[kk], 0].min() for kk in range(4) if live[kk].any())
+        for kk, n in enumerate(names):
+            for pt in TIMELINE_POINTS[n]:
+                sel = live[kk] & (st[kk, :, pt] > 0)
+                pooled[n][pt] += list((st[kk, sel, pt] - t0) / 100.0)
+        up = st[2]
+        g = np.nonzero(live[2] & (up[:, 4] > 0))[0]
+        for w in g:
+            key = "slot %d" % (w // 256)
+            slots.setdefault(key, []).append((up[w, 4] - t0) / 100.0)
+        # HW_ID: CU id bits 8-11, shader array bit 12, engine bits 13-15; XCC_ID above
+        cu = (up[:, 7] >> 32) * 256 + ((up[:, 7] >> 8) & 0xff)
+        pairs += [bool(cu[w] == cu[w + 256]) for w in g if w + 256 < 1024 and up[w + 256, 4] > 0]
+        # matrix-shape gate/up: its first task's duration by token tiles, cut
+        # or whole, and CU slot (stamp 6: tokens | cut << 16 | ...)
+        for w in g:
+            info = int(up[w, 6])
+            if info and up[w, 3] > 0:
+                m, cut = info & 0xffff, (info >> 16) & 1
+                key = "%d token tile%s, %s, slot %d" % ((m + 15) // 16, "" if m <= 16 else "s", "cut" if cut else "whole",
+                                                          w // 256)
+                tasks.setdefault(key, []).append((up[w, 3] - up[w, 2]) / 100.0)
+    out = {n: {TIMELINE_POINTS[n][pt]: q(v) for pt, v in pooled[n].items() if v} for n in names}
+    out = {n: v for n, v in out.items() if v}
+    return {"workload": name, "variant": variant, "blocks": len(reps),
+            "unit": "µs from the block's first workgroup start (100 MHz clock)",
+            "points": out, "expert_up_end_by_cu_slot": {k: q(v) for k, v in sorted(slots.items())},
+            "expert_up_g_and_g256_same_cu": round(sum(pairs) / len(pairs), 4) if pairs else None,
+            "expert_up_first_task_us": {k: q(v) for k, v in sorted(tasks.items())}}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -713,6 +829,13 @@ def main():
     from moe_block_skinny_amd import synth
 
     torch.cuda.set_device(0)
+    if args.timeline:
+        if args.workload not in synth.CONFIGS or synth.CONFIGS[args.workload].dtype != "bf16":
+            print("--timeline takes a bf16 block workload (tp16_b1, tp16_b8, tp8_b64)", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"timeline": run_timeline(args.workload, args, torch, mb, synth)}, ensure_ascii=False),
+              flush=True)
+        return
     t_start = time.perf_counter()
     cpu = None
     dtype = "bf16"

@@ -1,10 +1,13 @@
 """Build the gfx950 shared library libmoe_skinny.so in-tree with hipcc.
 
-    python -m moe_block_skinny_amd.build
+    python -m moe_block_skinny_amd.build [--stamps]
 
 Every .hip / .cpp file under csrc/ is compiled for gfx950 only (no other
 target, no CUDA path) and linked into one C-ABI shared library.  All device
-code is built with packed-fp32 instructions disabled.
+code is built with packed-fp32 instructions disabled.  With stamps=True the
+same sources are built with -DMOE_STAMPS into libmoe_skinny_stamps.so: the
+instrumented library whose kernels record per-workgroup clock stamps
+(`bench.py --timeline`); nothing else loads it.
 """
 from __future__ import annotations
 
@@ -19,6 +22,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_skinny.so")
 BUILD_DIR = os.path.join(HERE, "_build")
+LIB_STAMPS = os.path.join(HERE, "libmoe_skinny_stamps.so")
+BUILD_DIR_STAMPS = os.path.join(HERE, "_build_stamps")
 
 ARCH = "gfx950"
 
@@ -57,13 +62,14 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    bdir, lib = (BUILD_DIR_STAMPS, LIB_STAMPS) if stamps else (BUILD_DIR, LIB)
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [cc] + flags() + ["-c", src, "-o", obj]
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        cmd = [cc] + flags() + (["-DMOE_STAMPS"] if stamps else []) + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -76,14 +82,14 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, stamps="--stamps" in sys.argv))

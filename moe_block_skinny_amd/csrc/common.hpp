@@ -407,4 +407,38 @@ __device__ __forceinline__ float silu(float z) {
   return z / (1.0f + __expf(-z));
 }
 
+// ---- per-workgroup clock stamps (instrumented build) ----------------------
+// Built with -DMOE_STAMPS (libmoe_skinny_stamps.so, `bench.py --timeline`),
+// thread 0 of workgroup g < kStampWGs of a stamped kernel writes the 100 MHz
+// constant clock (s_memrealtime) or a value to slot s of row g of that
+// kernel's table: a launch's timeline per workgroup, without a profiler.
+// Every translation unit holds its own tables; moe_stamps_route (skinny.hip)
+// and moe_stamps_expert (expert.hip) copy or clear them.  Without
+// MOE_STAMPS the macros are empty and no table exists.
+constexpr int kStampWGs = 1024, kStampSlots = 8;
+enum StampKernel { ST_ROUTE = 0, ST_FINISH = 1, ST_UP = 2, ST_DOWN = 3, ST_KERNELS = 4 };
+#ifdef MOE_STAMPS
+static __device__ unsigned long long g_stamps[ST_KERNELS * kStampWGs * kStampSlots];
+__device__ __forceinline__ unsigned long long* stamp_cell(int k, int slot) {
+  return &g_stamps[((size_t)k * kStampWGs + blockIdx.x) * kStampSlots + slot];
+}
+#define MOE_STAMP_VAL(k, slot, v)                                                        \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStampWGs) *stamp_cell((k), (slot)) = \
+        (unsigned long long)(v);                                                          \
+  } while (0)
+#define MOE_STAMP(k, slot) MOE_STAMP_VAL((k), (slot), __builtin_amdgcn_s_memrealtime())
+// the CU the workgroup runs on: HW_ID (wave, SIMD, CU, shader array and
+// engine ids) in the low word, XCC_ID in the high word
+#define MOE_STAMP_CU(k, slot)                                                                          \
+  MOE_STAMP_VAL((k), (slot), (unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 4) |           \
+                                 ((unsigned long long)__builtin_amdgcn_s_getreg((15 << 11) | 20) << 32))
+#else
+#define MOE_STAMP_VAL(k, slot, v) \
+  do {                            \
+  } while (0)
+#define MOE_STAMP(k, slot) MOE_STAMP_VAL(k, slot, 0)
+#define MOE_STAMP_CU(k, slot) MOE_STAMP_VAL(k, slot, 0)
+#endif
+
 }  // namespace moe

@@ -66,12 +66,21 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
   const int wave = threadIdx.x >> 6;
   const int tiles_r = (a.I + PPT - 1) / PPT;
   const int tiles_s = (a.Ws13 && !a.skip_shared) ? (a.Is + PPT - 1) / PPT : 0;
+  // stamps (instrumented build): 0 start; 1 router rows scored or shared
+  // tiles done (vector shape), plan built (matrix shape); 2 plan ready
+  // (vector), tasks listed (matrix); 3 first routed task done; 4 end;
+  // 5 routed tasks | shared tasks << 16; 6 first matrix task: tokens |
+  // cut << 16 | slice << 17 | shared << 20; 7 the CU
+  MOE_STAMP(ST_UP, 0);
+  MOE_STAMP_CU(ST_UP, 7);
+  [[maybe_unused]] int n_routed = 0, n_shared = 0;
   if constexpr (PATHS == kPathValu) {
     // With the router rows in this launch, its first router_wgs workgroups
     // score them and leave; the others are the gate/up workgroups
     if (a.router_wgs && (int)blockIdx.x < a.router_wgs) {
       __shared__ float s_rr[kRouterPlayedWaves * kRouterRowsInUp * 2];
       router_rows_in_up<T, kUpWaves>(a, blockIdx.x, s_rr);
+      MOE_STAMP(ST_UP, 1);
       return;
     }
     const int G = (int)gridDim.x - a.router_wgs;   // gate/up workgroups
@@ -97,11 +106,14 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       for (; task0 < tiles_s; task0 += G) {
         up_valu_dispatch<T, 2>(a, nullptr, shared_view(a), task0 * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
         __syncthreads();
+        ++n_shared;
       }
+      MOE_STAMP(ST_UP, 1);
       p = a.ready ? wait_token_plan(a, s_plan, s_tk, s_ids) : route_here<false, 1>(a, s_plan, s_tk, s_ids, s_w);
     } else {
       p = stage_plan(a, s_plan);
     }
+    MOE_STAMP(ST_UP, 2);
     const int first = here ? tiles_s : 0;                    // first routed task
     const int total = first + p.n * tiles_r + (here ? 0 : tiles_s);
     for (int task = task0; task < total; task += G) {
@@ -111,12 +123,14 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
       const int tile = routed ? rt % tiles_r : rt - p.n * tiles_r;
       up_valu_dispatch<T, 2>(a, p.slots, v, tile * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
       __syncthreads();  // s_red is reused by the next task
+      if (n_routed++ == 0) MOE_STAMP(ST_UP, 3);
     }
   } else {
     __shared__ __align__(16) unsigned char s_x[MfmaX<4, kUpMfmaChunks>::kLdsBytes];
     __shared__ int s_tstart[kMaxE + 2];
     static_assert(sizeof(s_x) >= kPlanFromIdsBytes, "plan scratch fits the activation buffer");
     const PlanView p = a.ids_in ? plan_from_ids(a, s_plan, s_x) : stage_plan(a, s_plan);
+    MOE_STAMP(ST_UP, 1);
     const int ne = p.n + (tiles_s > 0 ? 1 : 0);   // routed entries, then the shared one
     const int tiles_m = (a.I + kUpPairsMfma - 1) / kUpPairsMfma;
     const int tiles_ms = (a.Is + kUpPairsMfma - 1) / kUpPairsMfma;
@@ -203,6 +217,7 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
     __syncthreads();
     const int total = s_tstart[ne];
     const int smin = s_use_split;
+    MOE_STAMP(ST_UP, 2);
     const int J = a.d / 32, nch = (J + kChunk - 1) / kChunk;
     for (int task = blockIdx.x; task < total; task += gridDim.x) {
       // entry of the task: the last e with s_tstart[e] <= task
@@ -230,12 +245,17 @@ __global__ __launch_bounds__(kUpWaves * 64, PATHS == kPathValu ? 4 : 2) void exp
           sl.counter = a.up_counter + s_cbase[e] + tile;
         }
         up_mfma_dispatch<T>(a, p.slots, v, tile * kUpPairsMfma, s_x, sl);
+        if (n_routed == 0)
+          MOE_STAMP_VAL(ST_UP, 6, v.m | (sl.split > 1) << 16 | sl.slice << 17 | (e >= p.n) << 20);
       } else {
         up_valu_dispatch<T, 2>(a, p.slots, v, local * PPT + wave % PPT, wave / PPT, wave % PPT, s_red);
       }
       __syncthreads();  // s_red / s_x are reused by the next task
+      if (n_routed++ == 0) MOE_STAMP(ST_UP, 3);
     }
   }
+  MOE_STAMP(ST_UP, 4);
+  MOE_STAMP_VAL(ST_UP, 5, n_routed | n_shared << 16);
 }
 
 // ---- down projection -> Yslot ----------------------------------------------
@@ -312,6 +332,10 @@ void expert_down_combine_kernel(ExpertLaunch a) {
   const int rt = (PIPE || PAIRED) ? a.down_rows : RT;
   float* s_y = s_dyn;
   float* s_h = s_dyn + (size_t)(a.B * a.k + a.B) * rt;
+  // stamps (instrumented build): 0 start, 1 staged, 2 products done, 3 end,
+  // 7 the CU
+  MOE_STAMP(ST_DOWN, 0);
+  MOE_STAMP_CU(ST_DOWN, 7);
   // the router rows' keys of the gate/up launch, zero again for the next call
   if (a.lkeys) {
     const int n = a.B * a.E;
@@ -357,6 +381,7 @@ void expert_down_combine_kernel(ExpertLaunch a) {
     for (int i = threadIdx.x + kHRegs * nt_; i < n4; i += nt_)
       reinterpret_cast<f32x4*>(s_h)[i] = reinterpret_cast<const f32x4*>(a.h)[i];
   }
+  MOE_STAMP(ST_DOWN, 1);
   const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * rt;
   const YSink sink = {s_y, 1, r0, rt};
@@ -407,6 +432,7 @@ void expert_down_combine_kernel(ExpertLaunch a) {
     }
   }
   __syncthreads();
+  MOE_STAMP(ST_DOWN, 2);
   const int has_shared = a.Ws13 ? 1 : 0;
   for (int idx = threadIdx.x; idx < a.B * rt; idx += blockDim.x) {
     const int t = idx / rt, r = idx % rt;
@@ -419,6 +445,7 @@ void expert_down_combine_kernel(ExpertLaunch a) {
     if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[o] = f32_to_bf16(v);
     else reinterpret_cast<float*>(a.out)[o] = v;
   }
+  MOE_STAMP(ST_DOWN, 3);
 }
 
 // ---- the shared expert alone (side stream) ---------------------------------
@@ -598,3 +625,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 }  // namespace moe
+
+#ifdef MOE_STAMPS
+// Instrumented build: copy (out != null) or clear the clock stamps of this
+// file's kernels (the gate/up and down + combine launches).
+extern "C" int moe_stamps_expert(void* out, int clear) {
+  static unsigned long long zeros[moe::ST_KERNELS * moe::kStampWGs * moe::kStampSlots];
+  if (clear) return (int)hipMemcpyToSymbol(HIP_SYMBOL(moe::g_stamps), zeros, sizeof zeros);
+  return (int)hipMemcpyFromSymbol(out, HIP_SYMBOL(moe::g_stamps), sizeof zeros);
+}
+#endif

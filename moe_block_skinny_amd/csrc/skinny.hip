@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
   __shared__ float s_w[kMaxB * kMaxK];
   __shared__ __align__(16) float s_lg[kFinishWaves][kMaxE];
   __shared__ int s_last;
+  MOE_STAMP(ST_FINISH, 0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x;
   const int E = a.N - a.L, k = a.k;   // router rows; the partial rows hold all N
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void route_finish_kernel(SkinnyL
       for (int i = 0; i < 4; ++i) finish_value(a, t, E + c + i, sum[i]);
     }
   }
+  MOE_STAMP(ST_FINISH, 1);
   if (a.plan_by_consumer) return;   // the gate/up launch builds the plan from the ids
   if (!arrive_last(a.done_counter, gridDim.x, &s_last)) return;
   {
@@ -248,6 +250,7 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   // the product's wave partials, or the shared gate/up's pair exchange
   // (8 pair slots of 2 x kPartStride floats)
   __shared__ float s_red[16 * RB * MB > 16 * kPartStride ? 16 * RB * MB : 16 * kPartStride];
+  if (ROUTER) MOE_STAMP(ST_ROUTE, 0);
   if (ROUTER && a.clear && blockIdx.x == 0)
     for (int i = threadIdx.x; i < a.clear_n; i += blockDim.x) a.clear[i] = 0;
   if (ROUTER && (int)blockIdx.x >= a.router_wgs) {  // shared expert gate/up
@@ -255,6 +258,7 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
     return;
   }
   valu_rows<T, RB, MB, U>(a, blockIdx.x * RB, s_red);
+  if constexpr (ROUTER) MOE_STAMP(ST_ROUTE, 1);
   if constexpr (ROUTER) router_tail(a);
 }
 
@@ -319,6 +323,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
   constexpr int PPT = MfmaX<NT>::kPerThread;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row = lane & 15, kq = lane >> 4;
+  if (ROUTER) MOE_STAMP(ST_ROUTE, 0);
   const int rgi = blockIdx.x / a.ks_n, ks = blockIdx.x % a.ks_n;
   const int n0 = rgi * kMfmaRows + wave * 16;
   const int J = a.K / 32;
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void skinny_mfma_kernel(SkinnyLaun
           if (n + i < a.N && t < a.M) dst[i] = acc[nt][i];
       }
     }
+    MOE_STAMP(ST_ROUTE, 1);
     return;
   }
   if (a.ks_n == 1) {
@@ -582,3 +588,13 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
 }
 
 }  // namespace moe
+
+#ifdef MOE_STAMPS
+// Instrumented build: copy (out != null) or clear the clock stamps of this
+// file's kernels (the router launches and the router's finish launch).
+extern "C" int moe_stamps_route(void* out, int clear) {
+  static unsigned long long zeros[moe::ST_KERNELS * moe::kStampWGs * moe::kStampSlots];
+  if (clear) return (int)hipMemcpyToSymbol(HIP_SYMBOL(moe::g_stamps), zeros, sizeof zeros);
+  return (int)hipMemcpyFromSymbol(out, HIP_SYMBOL(moe::g_stamps), sizeof zeros);
+}
+#endif
