@@ -44,8 +44,8 @@ one JSON line with the per-workgroup clock stamps of --trials single blocks
 (each launched alone after every weight set was run once): per launch and
 stamp point the min / p10 / median / p90 / max in µs from the block's first
 workgroup start, and for the gate/up launch the end times by CU slot (the
-grid's first, second, ... 256 workgroups) and whether workgroups g and
-g + 256 ran on the same CU.
+grid's first, second, ... 256 workgroups), by XCD and per CU (its last
+workgroup), and whether workgroups g and g + 256 ran on the same CU.
 """
 from __future__ import annotations
 
@@ -779,7 +779,7 @@ def run_timeline(name, args, torch, mb, synth):
 
     names = ("route", "route_finish", "expert_up", "expert_down_combine")
     pooled = {n: {pt: [] for pt in TIMELINE_POINTS[n]} for n in names}
-    slots, pairs, tasks = {}, [], {}
+    slots, pairs, tasks, xcds, cu_ends = {}, [], {}, {}, []
     for st in reps:
         live = [st[kk, :, 0] > 0 for kk in range(4)]
         t0 = min(st[kk, live[kk], 0].min() for kk in range(4) if live[kk].any())
@@ -794,6 +794,11 @@ def run_timeline(name, args, torch, mb, synth):
             slots.setdefault(key, []).append((up[w, 4] - t0) / 100.0)
         # HW_ID: CU id bits 8-11, shader array bit 12, engine bits 13-15; XCC_ID above
         cu = (up[:, 7] >> 32) * 256 + ((up[:, 7] >> 8) & 0xff)
+        per_cu = {}
+        for w in g:
+            xcds.setdefault("xcd %d" % (up[w, 7] >> 32), []).append((up[w, 4] - t0) / 100.0)
+            per_cu[int(cu[w])] = max(per_cu.get(int(cu[w]), 0.0), (up[w, 4] - t0) / 100.0)
+        cu_ends += list(per_cu.values())
         pairs += [bool(cu[w] == cu[w + 256]) for w in g if w + 256 < 1024 and up[w + 256, 4] > 0]
         # matrix-shape gate/up: its first task's duration by token tiles, cut
         # or whole, and CU slot (stamp 6: tokens | cut << 16 | ...)
@@ -810,7 +815,9 @@ def run_timeline(name, args, torch, mb, synth):
             "unit": "µs from the block's first workgroup start (100 MHz clock)",
             "points": out, "expert_up_end_by_cu_slot": {k: q(v) for k, v in sorted(slots.items())},
             "expert_up_g_and_g256_same_cu": round(sum(pairs) / len(pairs), 4) if pairs else None,
-            "expert_up_first_task_us": {k: q(v) for k, v in sorted(tasks.items())}}
+            "expert_up_first_task_us": {k: q(v) for k, v in sorted(tasks.items())},
+            "expert_up_end_by_xcd": {k: q(v) for k, v in sorted(xcds.items())},
+            "expert_up_cu_end": q(cu_ends)}
 
 
 # ---------------------------------------------------------------- main
