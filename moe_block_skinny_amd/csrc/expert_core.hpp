@@ -599,7 +599,7 @@ __device__ __forceinline__ void up_mfma(const ExpertLaunch& a, const int32_t* sl
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_rows_db<NT, kUpMfmaChunks / 2>(wa, wok, wb, wok, xrow, xok, sl.s0, sl.s1, s_x, acc);
+  mfma_rows_db<NT, kUpMfmaChunks / 2, true>(wa, wok, wb, wok, xrow, xok, sl.s0, sl.s1, s_x, acc);
   if (sl.split > 1) {
     // one K slice: store its sums (device-coherent: the tile's last slice,
     // another workgroup of this launch, reads them) and arrive

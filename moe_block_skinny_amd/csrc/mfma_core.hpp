@@ -203,8 +203,9 @@ __device__ __forceinline__ void mfma_rows(const bf16_t* wa, bool oka, const bf16
 // flight there is the one the next iteration multiplies first).  One
 // barrier per stage: it publishes the stage's activations and retires the
 // reads of the buffer the next stores overwrite.
-// s_x: 2 * MfmaX<NT, U>::kLdsBytes.
-template <int NT, int U>
+// s_x: 2 * MfmaX<NT, U>::kLdsBytes.  TURNS: a grid of two workgroups per
+// CU, which take turns at the higher wave priority (below).
+template <int NT, int U, bool TURNS = false>
 __device__ __forceinline__ void mfma_rows_db(const bf16_t* wa, bool oka, const bf16_t* wb, bool okb,
                                              const bf16_t* const (&xrow)[MfmaX<NT>::kPerThread],
                                              const bool (&xok)[MfmaX<NT>::kPerThread], int s0, int s1,
@@ -224,14 +225,16 @@ __device__ __forceinline__ void mfma_rows_db(const bf16_t* wa, bool oka, const b
   mfma_store_x<NT, U>(xv, xok, s0, s1, buf0);
   __builtin_amdgcn_sched_barrier(0);
   for (int c = s0;; c += 2 * G) {
-    // the two workgroups of a CU (g and g + kSlotStride in a grid of two per
-    // CU) take turns at the higher wave priority, a double stage each: left
-    // to age order the CU serves the older one first and the younger then
-    // streams alone at a lower rate (clock stamps at batch 64: identical
-    // tiles took 54 us on the first and 67 us on the second; with the turns
-    // the block took 133 instead of 134.8 us)
-    if (((c - s0) / (2 * G) + (blockIdx.x >= kSlotStride ? 1 : 0)) & 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+    // the two workgroups of a CU (g and g + kSlotStride) take turns at the
+    // higher wave priority, a double stage each: left to age order the CU
+    // serves the older one first and the younger then streams alone at a
+    // lower rate (clock stamps at batch 64: identical tiles took 54 us on
+    // the first and 67 us on the second; with the turns the block took 133
+    // instead of 134.8 us)
+    if constexpr (TURNS) {
+      if (((c - s0) / (2 * G) + (blockIdx.x >= kSlotStride ? 1 : 0)) & 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     mfma_issue_x<NT, U>(xrow, c + G, s1, xv);
     __builtin_amdgcn_sched_barrier(0);
     mfma_issue_w<U>(wa, wb, xrow[0], c + G, s1, va1, vb1);
