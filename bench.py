@@ -736,6 +736,7 @@ def run_timeline(name, args, torch, mb, synth):
         f.argtypes = [ctypes.c_void_p, ctypes.c_int]
     prod, mb.lib = mb.lib, stamps_lib
     try:
+        mb.set_block_schedule(args.schedule)
         cfg = synth.CONFIGS[name]
         R = 2
         sets = moe_sets(cfg, R, args.seed, torch)
