@@ -90,7 +90,10 @@ typedef enum {
   MOE_VARIANT_AUTO = 0,
   MOE_VARIANT_GEMV = 1,
   MOE_VARIANT_SPLITK = 2,
-  MOE_VARIANT_MFMA = 3
+  MOE_VARIANT_MFMA = 3,
+  MOE_VARIANT_ROWS = 4  /* dense product only (bf16, B <= 8, K <= 8192): each
+                           workgroup owns 12 weight rows over all of K; other
+                           products choose as under MOE_VARIANT_AUTO */
 } moe_variant_t;
 
 typedef enum {

@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libmoe_skinny.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 DT_F32, DT_BF16 = 0, 1
-VARIANT_AUTO, VARIANT_GEMV, VARIANT_SPLITK, VARIANT_MFMA = range(4)
+VARIANT_AUTO, VARIANT_GEMV, VARIANT_SPLITK, VARIANT_MFMA, VARIANT_ROWS = range(5)
 OP_SKINNY_GEMM, OP_ROUTE, OP_EXPERT_FFN, OP_BLOCK, OP_ROUTE_LATENT = range(5)
 KERNEL_ROUTE, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_SKINNY, KERNEL_BLOCK, KERNEL_STREAM = range(7)
-VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "splitk": VARIANT_SPLITK, "mfma": VARIANT_MFMA}
+VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "splitk": VARIANT_SPLITK, "mfma": VARIANT_MFMA, "rows": VARIANT_ROWS}
 SCHEDULE_AUTO, SCHEDULE_LAUNCHES, SCHEDULE_FUSED, SCHEDULE_ROUTER_IN_UP = range(4)
 SCHEDULES = {"auto": SCHEDULE_AUTO, "launches": SCHEDULE_LAUNCHES, "fused": SCHEDULE_FUSED,
              "router_in_up": SCHEDULE_ROUTER_IN_UP}

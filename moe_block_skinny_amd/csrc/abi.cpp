@@ -64,6 +64,7 @@ int forced() {
       if (!strcmp(e, "gemv")) f = MOE_VARIANT_GEMV;
       else if (!strcmp(e, "splitk")) f = MOE_VARIANT_SPLITK;
       else if (!strcmp(e, "mfma")) f = MOE_VARIANT_MFMA;
+      else if (!strcmp(e, "rows")) f = MOE_VARIANT_ROWS;
     }
     int expect = -1;
     g_force.compare_exchange_strong(expect, f);
@@ -123,26 +124,35 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // ---- kernel shape of the skinny product --------------------------------------
 
-// Automatic shapes: the small-matrix (gemv) shape at B <= 2, split-K above.
-// The dense product takes the matrix shape from B = 5 (bf16, K % 32 == 0):
-// measured at N = 3072, K = 7168 the split-K shape takes 11.4 us at B = 4
-// and 14.2-15.0 us at B = 5..8 (from B = 5 it runs the 8-token instance),
-// while the matrix shape stays at ~13.2 us.  The router keeps split-K up to
-// B = 8, where the gate/up launch selects from its logits.
-constexpr int kDenseSplitkMaxB = 4;
+// Automatic shapes: the small-matrix (gemv) shape at B <= 2, split-K above
+// (fp32, and the router up to B = 8, where the gate/up launch selects from
+// its logits).  The dense bf16 product takes the rows shape at B = 2..8
+// (K <= 8192) and the matrix shape above; measured at N = 3072, K = 7168:
+// rows 9.1 / 9.6 / 11.1 us at B = 2 / 4 / 8 against gemv 9.6, split-K 11.4
+// and the matrix shape 13.8; at B = 1 gemv (8.7 us) stays ahead of rows
+// (8.9).
+constexpr int kDenseRowsMaxB = 8;
+constexpr int kDenseSplitkMaxB = 4;   // beyond the rows shape's K (bf16, K % 32 == 0)
+bool rows_ok(int bf16, int B, int K) { return bf16 && B <= kDenseRowsMaxB && K % 8 == 0 && K / 8 <= 1024; }
 
 moe_status_t resolve_skinny(int bf16, int B, int K, int* variant, bool router = true) {
   const int f = forced();
   int v = f;
-  if (f == MOE_VARIANT_AUTO) {
+  // the rows shape is the dense product's only: other products choose as
+  // under MOE_VARIANT_AUTO
+  const bool auto_choice = f == MOE_VARIANT_AUTO || (f == MOE_VARIANT_ROWS && router);
+  if (auto_choice) {
     const bool mfma_ok = bf16 && K % 32 == 0;
     const int splitk_max = (router || !mfma_ok) ? 8 : kDenseSplitkMaxB;
-    v = B <= 2 ? VAR_GEMV : (B <= splitk_max ? VAR_SPLITK : VAR_MFMA);
+    if (!router && B >= 2 && rows_ok(bf16, B, K)) v = VAR_ROWS;
+    else v = B <= 2 ? VAR_GEMV : (B <= splitk_max ? VAR_SPLITK : VAR_MFMA);
   }
   if (v == VAR_GEMV && B > 2) return fail(MOE_EUNSUPPORTED, "gemv shape supports B <= 2 (B=%d)", B);
   if (v == VAR_SPLITK && B > 8) return fail(MOE_EUNSUPPORTED, "splitk shape supports B <= 8 (B=%d)", B);
   if (v == VAR_MFMA && !bf16) return fail(MOE_EUNSUPPORTED, "mfma shape needs bf16 (fp32 supports B <= 8)");
   if (v == VAR_MFMA && K % 32) return fail(MOE_EUNSUPPORTED, "mfma shape needs K %% 32 == 0 (K=%d)", K);
+  if (v == VAR_ROWS && !rows_ok(bf16, B, K))
+    return fail(MOE_EUNSUPPORTED, "rows shape needs bf16, B <= 8 and K %% 8 == 0, K <= 8192 (B=%d, K=%d)", B, K);
   *variant = v;
   return MOE_OK;
 }
@@ -302,7 +312,7 @@ moe_status_t expert_force(int dt, int B, int* force) {
     return fail(MOE_EUNSUPPORTED, "mfma shape needs bf16");
   if ((f == MOE_VARIANT_GEMV || f == MOE_VARIANT_SPLITK) && B > 8)
     return fail(MOE_EUNSUPPORTED, "vector expert shape supports up to 8 tokens per expert (B=%d)", B);
-  *force = f == MOE_VARIANT_MFMA ? VAR_MFMA : (f == MOE_VARIANT_AUTO ? VAR_AUTO : VAR_GEMV);
+  *force = f == MOE_VARIANT_MFMA ? VAR_MFMA : ((f == MOE_VARIANT_AUTO || f == MOE_VARIANT_ROWS) ? VAR_AUTO : VAR_GEMV);
   return MOE_OK;
 }
 
@@ -447,7 +457,7 @@ const char* moe_last_variant(void) { return g_variant; }
 
 int moe_set_variant(int variant) {
   const int prev = forced();
-  if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_MFMA) return prev;
+  if (variant < MOE_VARIANT_AUTO || variant > MOE_VARIANT_ROWS) return prev;
   g_force.store(variant);
   return prev;
 }

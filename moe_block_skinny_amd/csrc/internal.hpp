@@ -9,7 +9,7 @@
 
 namespace moe {
 
-enum Variant { VAR_AUTO = 0, VAR_GEMV = 1, VAR_SPLITK = 2, VAR_MFMA = 3 };
+enum Variant { VAR_AUTO = 0, VAR_GEMV = 1, VAR_SPLITK = 2, VAR_MFMA = 3, VAR_ROWS = 4 };
 
 // Router rows per workgroup when the router product runs inside the gate/up
 // launch (ExpertLaunch::router_wgs), and the copies of the logit keys it

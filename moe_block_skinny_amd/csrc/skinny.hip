@@ -21,6 +21,10 @@
 //   mfma   : M <= 64 (bf16); v_mfma_f32_16x16x32_bf16 with 16 weight rows as
 //            the A operand and up to four 16-token tiles as B, used once
 //            batch x rows is a dense contraction; its waves split K.
+//   rows   : the dense product at M = 2..8 (bf16, K <= 8192); a workgroup
+//            owns 12 weight rows over all of K, one 16-byte chunk of K per
+//            thread, so every activation chunk serves 12 rows and no
+//            partial sum leaves the workgroup.
 // Split-K stays inside the workgroup: each wave reduces its lanes, the waves
 // meet in LDS and are summed in fixed wave order, so results are
 // deterministic and no partial sum ever goes through global memory (a
@@ -262,6 +266,153 @@ __global__ __launch_bounds__(1024) void skinny_valu_kernel(SkinnyLaunch a) {
   if constexpr (ROUTER) router_tail(a);
 }
 
+// ---- rows kernel (bf16, few tokens, K <= 8192) -----------------------------
+
+// A workgroup owns kRowsGroups x RPP weight rows over all of K; thread j
+// takes the 16-byte chunk j of K (K / 8 threads).  Its activation chunks
+// (MB tokens) are requested once and serve every row, so the activations
+// cost 8 x MB bytes per 16 x RPP x kRowsGroups bytes of weights, and no
+// partial sum leaves the workgroup: no K slices, no arrival counter, no
+// reduction tail.  The rows go RPP at a time; the next group's weights are
+// requested before the current group's products.  A group's RPP x MB sums
+// are reduced across the wave by halving exchanges (each step keeps half
+// the values and adds the partner lane's other half, so after log2(V)
+// steps lane l holds sum V-index l >> (6 - log2 V)), finished by
+// exchanges over the remaining lane bits; the waves meet in LDS and are
+// added in wave order (deterministic).
+constexpr int kRowsGroups = 3;
+
+// Lane exchanges of the halving steps.  Over 32 and 16 lanes: the swaps
+// of gfx950 (v_permlane32_swap: lanes 32-63 of the first operand trade
+// places with lanes 0-31 of the second; v_permlane16_swap: the odd 16-lane
+// rows of the first with the even rows of the second), so that lo + hi
+// afterwards holds, in a lower lane, its lo plus its partner's lo and, in
+// an upper lane, its hi plus its partner's hi.  Within a row: DPP
+// (mirror, half-mirror, quad permutes), pairing lane i with a lane that
+// differs in bit log2(M) and holds the same sums so far.
+template <int M>
+__device__ __forceinline__ float swap_halves_sum(float lo, float hi) {
+  const unsigned a = __builtin_bit_cast(unsigned, lo), b = __builtin_bit_cast(unsigned, hi);
+  unsigned x, y;
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    x = r[0];
+    y = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    x = r[0];
+    y = r[1];
+  }
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+template <int M>
+__device__ __forceinline__ float in_row_partner(float v) {
+  static_assert(M == 8 || M == 4 || M == 2 || M == 1, "in-row masks");
+  if constexpr (M == 8) return dpp_f32<0x140>(v);        // row_mirror: i <-> 15 - i
+  else if constexpr (M == 4) return dpp_f32<0x141>(v);   // row_half_mirror: i <-> 7 - i
+  else if constexpr (M == 2) return dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  else return dpp_f32<0xB1>(v);                          // quad_perm [1,0,3,2]
+}
+
+// One halving step over mask M on the first N of v's values (a lane with
+// bit M keeps the upper half), then the next steps; all indices are
+// compile-time constants.
+template <int N, int M, int V>
+__device__ __forceinline__ void halve(float (&v)[V], int lane) {
+  if constexpr (N > 1) {
+    if constexpr (M >= 16) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) v[i] = swap_halves_sum<M>(v[i], v[i + N / 2]);
+    } else {
+      const bool upper = (lane & M) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float give = upper ? v[i] : v[i + N / 2];
+        const float keep = upper ? v[i + N / 2] : v[i];
+        v[i] = keep + in_row_partner<M>(give);
+      }
+    }
+    halve<N / 2, M / 2>(v, lane);
+  }
+}
+
+// The halving steps over masks M0, M0 / 2, ... for V values (V <= 2 M0,
+// both powers of two), then sums of the one value left over the lower
+// masks.  (The first step over mask 32 is taken with the products.)
+template <int V, int M0>
+__device__ __forceinline__ float halving_sum(float (&v)[V]) {
+  static_assert(V >= 1 && V <= 2 * M0 && (V & (V - 1)) == 0, "V a power of two <= 2 M0");
+  static_assert(M0 <= 16, "the in-row sums below take masks up to 8");
+  halve<V, M0>(v, threadIdx.x & 63);
+  float r = v[0];
+  if constexpr (M0 / V >= 8) r += in_row_partner<8>(r);
+  if constexpr (M0 / V >= 4) r += in_row_partner<4>(r);
+  if constexpr (M0 / V >= 2) r += in_row_partner<2>(r);
+  if constexpr (M0 / V >= 1) r += in_row_partner<1>(r);
+  return r;
+}
+
+template <int MB, int RPP>
+__global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
+  static_assert(RPP >= 2 && (RPP & (RPP - 1)) == 0, "row pairs for the first halving step");
+  constexpr int V = RPP * MB;
+  constexpr int SH = V == 64 ? 0 : (V == 32 ? 1 : (V == 16 ? 2 : (V == 8 ? 3 : (V == 4 ? 4 : (V == 2 ? 5 : 6)))));
+  __shared__ float s_w[16][kRowsGroups * V];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int n0 = blockIdx.x * (RPP * kRowsGroups);
+  const int C = a.K / 8;
+  const bool live = (int)threadIdx.x < C;
+  const int c = live ? (int)threadIdx.x : C - 1;   // a lane past K: zero activations
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
+  u32x4 xv[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) xv[t] = ld128(X + (size_t)(t < a.M ? t : 0) * a.K + (size_t)c * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wv[2][RPP];
+#pragma unroll
+  for (int r = 0; r < RPP; ++r) wv[0][r] = ld128_stream(product_row<bf16_t>(a, n0 + r) + (size_t)c * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  bool xz = false;   // activations zeroed past K (once, at their first use)
+#pragma unroll
+  for (int g = 0; g < kRowsGroups; ++g) {
+    if (g + 1 < kRowsGroups) {
+#pragma unroll
+      for (int r = 0; r < RPP; ++r)
+        wv[(g + 1) & 1][r] = ld128_stream(product_row<bf16_t>(a, n0 + (g + 1) * RPP + r) + (size_t)c * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // products of rows r and r + RPP / 2 and the first halving step (mask
+    // 32) together, so that only half the sums are live at once
+    if (!xz) {
+#pragma unroll
+      for (int t = 0; t < MB; ++t) xv[t] = live ? xv[t] : zero;
+      xz = true;
+    }
+    float h[V / 2];
+#pragma unroll
+    for (int r = 0; r < RPP / 2; ++r) {
+      const u32x4 wl = wv[g & 1][r];
+      const u32x4 wh = wv[g & 1][r + RPP / 2];
+#pragma unroll
+      for (int t = 0; t < MB; ++t)
+        h[r * MB + t] = swap_halves_sum<32>(dot_chunk(wl, xv[t], 0.f, bf16_t()), dot_chunk(wh, xv[t], 0.f, bf16_t()));
+    }
+    const float v = halving_sum<V / 2, 16>(h);
+    if ((lane & ((1 << SH) - 1)) == 0) s_w[wave][g * V + (lane >> SH)] = v;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < kRowsGroups * V) {
+    const int g = threadIdx.x / V, j = threadIdx.x % V;
+    const int n = n0 + g * RPP + j / MB, t = j % MB;
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += s_w[w][threadIdx.x];
+    if (n < a.N && t < a.M) finish_value(a, t, n, sum);
+  }
+}
+
 // ---- MFMA kernel (bf16) --------------------------------------------------
 
 // Workgroup of 4 waves = 64 weight rows (wave w: rows n0 + 16 w .. + 15)
@@ -453,11 +604,13 @@ int skinny_rows_per_block(int variant, int router) {
   if (router == 2) return kRouterLatentRows;
   if (router) return kRouterRows;
   if (variant == VAR_SPLITK) return 4;
+  if (variant == VAR_ROWS) return 4 * kRowsGroups;
   return 2;
 }
 int skinny_default_splits(int variant, int bf16, int M, int N, int K, int router) {
   (void)M;
   if (variant == VAR_MFMA) return kMfmaWaves;
+  if (variant == VAR_ROWS) return (K / 8 + 63) / 64;   // one 16-byte chunk of K per thread
   // The router's workgroups have 16 waves (the finish is shared among them);
   // waves beyond the K range just idle through the product.
   if (router) return 16;
@@ -561,6 +714,13 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
       else if (a.M <= 4) launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 4, 2, true>, grid, block, 0, st, a);
       else launch(K_ROUTE, skinny_valu_kernel<float, kRouterRows, 8, 1, true>, grid, block, 0, st, a);
     }
+  } else if (a.variant == VAR_ROWS) {
+    if (!a.bf16 || a.router || a.K % 8 || a.K / 8 > 1024 || a.M > 8) return hipErrorInvalidValue;
+    if (a.M <= 1) launch(K_SKINNY, skinny_rows_kernel<1, 4>, grid, block, 0, st, a);
+    else if (a.M <= 2) launch(K_SKINNY, skinny_rows_kernel<2, 4>, grid, block, 0, st, a);
+    else if (a.M <= 4) launch(K_SKINNY, skinny_rows_kernel<4, 4>, grid, block, 0, st, a);
+    else launch(K_SKINNY, skinny_rows_kernel<8, 4>, grid, block, 0, st, a);
+    name = "rows";
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {
       if (a.M <= 4) launch(K_SKINNY, skinny_valu_kernel<bf16_t, 4, 4, 2, false>, grid, block, 0, st, a);

@@ -180,6 +180,11 @@ def test_forced_variant_scope():
         mb.set_variant("mfma")
         assert gemm(dt=mb.DT_F32, ydt=mb.DT_F32, B=2) == mb.EUNSUPPORTED
         assert gemm(B=2, K=264) == mb.EUNSUPPORTED
+        mb.set_variant("rows")
+        assert gemm(B=9) == mb.EUNSUPPORTED
+        assert gemm(dt=mb.DT_F32, ydt=mb.DT_F32, B=2) == mb.EUNSUPPORTED
+        assert gemm(B=2, K=8200) == mb.EUNSUPPORTED
+        assert b"rows" in lib.moe_last_error()
     finally:
         mb.set_variant(prev)
     assert mb.set_variant(prev) == prev

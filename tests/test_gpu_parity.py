@@ -44,13 +44,13 @@ def ws_for(op, dtype, **kw):
     return mb.workspace(mb.workspace_bytes(op, dtype, **kw))
 
 
-SHAPES = {"gemv": [1, 2], "splitk": [1, 2, 3, 4, 5, 8], "mfma": [1, 2, 5, 9, 16, 17, 33, 64],
+SHAPES = {"gemv": [1, 2], "splitk": [1, 2, 3, 4, 5, 8], "mfma": [1, 2, 5, 9, 16, 17, 33, 64], "rows": [1, 2, 3, 4, 5, 7, 8],
           "auto": [1, 2, 3, 4, 5, 6, 8, 16, 24, 48, 64]}
 
 
 # ---------------------------------------------------------------- skinny_gemm
 
-@pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma"])
+@pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma", "rows"])
 @pytest.mark.parametrize("K", [7168, 1056])
 def test_skinny_gemm_integer_exact(var, K):
     rng = np.random.default_rng(K)
@@ -81,7 +81,7 @@ def test_skinny_gemm_dense_workload(B):
     X, W = dev(Xh), dev(Wh)
     N, K = Wh.shape
     ws = ws_for(mb.OP_SKINNY_GEMM, mb.DT_BF16, B=B, N=N, K=K)
-    for var in ["auto"] + [v for v in ("gemv", "splitk", "mfma") if B in SHAPES[v] or v == "mfma"]:
+    for var in ["auto"] + [v for v in ("gemv", "splitk", "mfma", "rows") if B in SHAPES[v] or v == "mfma"]:
         say("skinny_gemm dense", var, "B", B)
         Y32 = torch.empty((B, N), device="cuda")
         Y16 = torch.empty((B, N), device="cuda", dtype=torch.bfloat16)
@@ -95,7 +95,7 @@ def test_skinny_gemm_dense_workload(B):
         assert np.all(err16 <= bound + 2.0 ** -8 * np.abs(ref)), (var, B)
 
 
-@pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma"])
+@pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma", "rows"])
 @pytest.mark.parametrize("K", [3072, 1056])
 def test_skinny_gemm_residual_integer_exact(var, K):
     """Output projection with residual on small integers: every sum is exact
