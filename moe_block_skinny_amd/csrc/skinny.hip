@@ -404,11 +404,12 @@ __global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  if ((int)threadIdx.x < kRowsGroups * V) {
-    const int g = threadIdx.x / V, j = threadIdx.x % V;
+  // (a loop: a workgroup of one wave has fewer threads than results)
+  for (int i = threadIdx.x; i < kRowsGroups * V; i += blockDim.x) {
+    const int g = i / V, j = i % V;
     const int n = n0 + g * RPP + j / MB, t = j % MB;
     float sum = 0.f;
-    for (int w = 0; w < nw; ++w) sum += s_w[w][threadIdx.x];
+    for (int w = 0; w < nw; ++w) sum += s_w[w][i];
     if (n < a.N && t < a.M) finish_value(a, t, n, sum);
   }
 }

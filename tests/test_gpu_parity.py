@@ -51,7 +51,7 @@ SHAPES = {"gemv": [1, 2], "splitk": [1, 2, 3, 4, 5, 8], "mfma": [1, 2, 5, 9, 16,
 # ---------------------------------------------------------------- skinny_gemm
 
 @pytest.mark.parametrize("var", ["auto", "gemv", "splitk", "mfma", "rows"])
-@pytest.mark.parametrize("K", [7168, 1056])
+@pytest.mark.parametrize("K", [7168, 1056, 256])
 def test_skinny_gemm_integer_exact(var, K):
     rng = np.random.default_rng(K)
     N = 200
