@@ -498,7 +498,7 @@ def run_gemm(kind, B, args, torch, mb, synth, with_roofline):
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=stored_traffic("%s_b%d" % (kind, B), "skinny_gemm"),
-                    kernel="skinny_valu_kernel / skinny_mfma_kernel", launch="skinny_gemm",
+                    kernel="skinny_valu_kernel / skinny_rows_kernel / skinny_mfma_kernel", launch="skinny_gemm",
                     bytes_per_launch=nbytes, avg_us=round(kus, 3), launches_timed=len(durs))
     del sets, ws
     torch.cuda.empty_cache()
