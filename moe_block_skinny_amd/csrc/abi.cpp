@@ -130,8 +130,11 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // (K <= 8192) and the matrix shape above; measured at N = 3072, K = 7168:
 // rows 9.1 / 9.6 / 11.1 us at B = 2 / 4 / 8 against gemv 9.6, split-K 11.4
 // and the matrix shape 13.8; at B = 1 gemv (8.7 us) stays ahead of rows
-// (8.9).
+// (8.9).  With a short K (the output projection, K = 3072: 6 waves per
+// workgroup) rows loses at B = 2 (9.9 against gemv 9.4 us), ties split-K
+// at B = 4 (10.7) and wins at B = 8 (14.2 against the matrix shape's 14.7).
 constexpr int kDenseRowsMaxB = 8;
+constexpr int kDenseRowsMinKAtB2 = 6144;
 constexpr int kDenseSplitkMaxB = 4;   // beyond the rows shape's K (bf16, K % 32 == 0)
 bool rows_ok(int bf16, int B, int K) { return bf16 && B <= kDenseRowsMaxB && K % 8 == 0 && K / 8 <= 1024; }
 
@@ -144,7 +147,7 @@ moe_status_t resolve_skinny(int bf16, int B, int K, int* variant, bool router = 
   if (auto_choice) {
     const bool mfma_ok = bf16 && K % 32 == 0;
     const int splitk_max = (router || !mfma_ok) ? 8 : kDenseSplitkMaxB;
-    if (!router && B >= 2 && rows_ok(bf16, B, K)) v = VAR_ROWS;
+    if (!router && (B >= 3 || (B == 2 && K >= kDenseRowsMinKAtB2)) && rows_ok(bf16, B, K)) v = VAR_ROWS;
     else v = B <= 2 ? VAR_GEMV : (B <= splitk_max ? VAR_SPLITK : VAR_MFMA);
   }
   if (v == VAR_GEMV && B > 2) return fail(MOE_EUNSUPPORTED, "gemv shape supports B <= 2 (B=%d)", B);
