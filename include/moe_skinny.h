@@ -57,8 +57,10 @@
  *     is enqueued unless MOE_OK is returned; no call ever silently switches
  *     to another path.  moe_last_error() gives the detail.
  *   - Kernel shape follows the batch (WRITEUP part 1 §1): "gemv" at B <= 2,
- *     "splitk" at B <= 8, "mfma" above.  moe_set_variant() (or the
- *     MOE_FORCE_VARIANT environment variable: gemv, splitk, mfma) forces one
+ *     "splitk" at B <= 8, "mfma" above; the dense bf16 products (skinny_gemm,
+ *     skinny_gemm_residual) take "rows" at B = 3..8 (and at B = 2 when
+ *     K >= 6144) where K <= 8192.  moe_set_variant() (or the
+ *     MOE_FORCE_VARIANT environment variable: gemv, splitk, mfma, rows) forces one
  *     shape wherever it supports the sizes, and fails the call with
  *     MOE_EUNSUPPORTED where it does not.  MOE_TRACE=1 prints the chosen
  *     shape of every call to stderr; moe_last_variant() returns it
@@ -235,7 +237,9 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Dense skinny product Y[b][n] = sum_c X[b][c] * W[n][c]   (WRITEUP part 1
  * §1, the attention input projection at decode batch: small-matrix kernel at
- * batch 1-2, split-K at larger batch).
+ * batch 1-2, split-K at larger batch; here the rows shape takes the split-K
+ * role for bf16: 12 weight rows per workgroup over all of K, no partial sums
+ * outside the workgroup).
  *   X [B][K] dtype, W [N][K] dtype, Y [B][N] of y_dtype (dtype or
  *   MOE_DT_F32).  1 <= B <= 64; K a multiple of 8 (bf16) or 4 (fp32), and of
  *   32 for the mfma shape (bf16 only).  Output rounded to nearest-even when
