@@ -352,15 +352,19 @@ __device__ __forceinline__ float halving_sum(float (&v)[V]) {
   return r;
 }
 
-template <int MB, int RPP>
+// NG groups of RPP rows; ALL: every group's weights requested before the
+// first products (NG register sets) instead of the next group's during the
+// current products (two sets in turns).
+template <int MB, int RPP, int NG = kRowsGroups, bool ALL = false>
 __global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
+  static_assert(RPP * NG == 4 * kRowsGroups, "12 rows per workgroup");
   static_assert(RPP >= 2 && (RPP & (RPP - 1)) == 0, "row pairs for the first halving step");
   constexpr int V = RPP * MB;
   constexpr int SH = V == 64 ? 0 : (V == 32 ? 1 : (V == 16 ? 2 : (V == 8 ? 3 : (V == 4 ? 4 : (V == 2 ? 5 : 6)))));
-  __shared__ float s_w[16][kRowsGroups * V];
+  __shared__ float s_w[16][NG * V];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  const int n0 = blockIdx.x * (RPP * kRowsGroups);
+  const int n0 = blockIdx.x * (RPP * NG);
   const int C = a.K / 8;
   const bool live = (int)threadIdx.x < C;
   const int c = live ? (int)threadIdx.x : C - 1;   // a lane past K: zero activations
@@ -369,18 +373,21 @@ __global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
 #pragma unroll
   for (int t = 0; t < MB; ++t) xv[t] = ld128(X + (size_t)(t < a.M ? t : 0) * a.K + (size_t)c * 8);
   __builtin_amdgcn_sched_barrier(0);
-  u32x4 wv[2][RPP];
+  constexpr int NB = ALL ? NG : 2;   // weight register sets: every group's, or two in turns
+  u32x4 wv[NB][RPP];
 #pragma unroll
-  for (int r = 0; r < RPP; ++r) wv[0][r] = ld128_stream(product_row<bf16_t>(a, n0 + r) + (size_t)c * 8);
+  for (int g = 0; g < (ALL ? NG : 1); ++g)
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) wv[g][r] = ld128_stream(product_row<bf16_t>(a, n0 + g * RPP + r) + (size_t)c * 8);
   __builtin_amdgcn_sched_barrier(0);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   bool xz = false;   // activations zeroed past K (once, at their first use)
 #pragma unroll
-  for (int g = 0; g < kRowsGroups; ++g) {
-    if (g + 1 < kRowsGroups) {
+  for (int g = 0; g < NG; ++g) {
+    if (!ALL && g + 1 < NG) {
 #pragma unroll
       for (int r = 0; r < RPP; ++r)
-        wv[(g + 1) & 1][r] = ld128_stream(product_row<bf16_t>(a, n0 + (g + 1) * RPP + r) + (size_t)c * 8);
+        wv[(g + 1) % NB][r] = ld128_stream(product_row<bf16_t>(a, n0 + (g + 1) * RPP + r) + (size_t)c * 8);
     }
     __builtin_amdgcn_sched_barrier(0);
     // products of rows r and r + RPP / 2 and the first halving step (mask
@@ -393,8 +400,8 @@ __global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
     float h[V / 2];
 #pragma unroll
     for (int r = 0; r < RPP / 2; ++r) {
-      const u32x4 wl = wv[g & 1][r];
-      const u32x4 wh = wv[g & 1][r + RPP / 2];
+      const u32x4 wl = wv[g % NB][r];
+      const u32x4 wh = wv[g % NB][r + RPP / 2];
 #pragma unroll
       for (int t = 0; t < MB; ++t)
         h[r * MB + t] = swap_halves_sum<32>(dot_chunk(wl, xv[t], 0.f, bf16_t()), dot_chunk(wh, xv[t], 0.f, bf16_t()));
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(1024) void skinny_rows_kernel(SkinnyLaunch a) {
   }
   __syncthreads();
   // (a loop: a workgroup of one wave has fewer threads than results)
-  for (int i = threadIdx.x; i < kRowsGroups * V; i += blockDim.x) {
+  for (int i = threadIdx.x; i < NG * V; i += blockDim.x) {
     const int g = i / V, j = i % V;
     const int n = n0 + g * RPP + j / MB, t = j % MB;
     float sum = 0.f;
@@ -720,7 +727,12 @@ hipError_t launch_skinny(const SkinnyLaunch& a0, hipStream_t st, char* desc, siz
     if (a.M <= 1) launch(K_SKINNY, skinny_rows_kernel<1, 4>, grid, block, 0, st, a);
     else if (a.M <= 2) launch(K_SKINNY, skinny_rows_kernel<2, 4>, grid, block, 0, st, a);
     else if (a.M <= 4) launch(K_SKINNY, skinny_rows_kernel<4, 4>, grid, block, 0, st, a);
-    else launch(K_SKINNY, skinny_rows_kernel<8, 4>, grid, block, 0, st, a);
+    // 5..8 tokens: every group's weights requested up front (ALL): the
+    // products of the last group, which follow the last weight bytes, are
+    // the part the stream cannot hide (dense B = 8 11.3 -> 11.1 us, output
+    // projection 14.2 -> 13.5 us, same box; 6 groups of 2 rows: 11.2 /
+    // 13.7 us)
+    else launch(K_SKINNY, skinny_rows_kernel<8, 4, kRowsGroups, true>, grid, block, 0, st, a);
     name = "rows";
   } else if (a.variant == VAR_SPLITK) {
     if (a.bf16) {
